@@ -1,0 +1,12 @@
+"""Plain fp64 CPU oracle for jagged flash attention (test infrastructure only).
+
+Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The HIP library never calls it.
+"""
+from .attention import (  # noqa: F401
+    sequence_forward,
+    sequence_backward,
+    forward,
+    backward,
+    row_count,
+)

@@ -1,0 +1,342 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Each test checks the oracle against something other than itself: a padded
+dense library reference (torch's scaled_dot_product_attention in fp64 with
+autograd), central finite differences, closed forms, a hand-derived worked
+example, and exact identities of softmax attention.  A plausible slip in the
+oracle (dropped scale, wrong sign, transposed operand, wrong causal direction,
+wrong LSE base, missing batch sum of the shared dQ, off-by-one offsets) fails
+at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_case(rng, lengths, h, d, broadcast_q, lq):
+    t = int(sum(lengths))
+    q = rng.standard_normal((lq if broadcast_q else t, h, d))
+    k = rng.standard_normal((t, h, d))
+    v = rng.standard_normal((t, h, d))
+    rows = len(lengths) * lq if broadcast_q else t
+    g = rng.standard_normal((rows, h, d))
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    return q, k, v, g, off
+
+
+def _padded_reference(q, k, v, g, off, broadcast_q, causal, scale):
+    """Padded dense masked attention via torch SDPA (fp64, CPU) + autograd."""
+    b = len(off) - 1
+    h, d = k.shape[1], k.shape[2]
+    lens = np.diff(off)
+    lmax = int(lens.max())
+    lq = q.shape[0] if broadcast_q else lmax
+    kp = torch.zeros(b, h, lmax, d, dtype=torch.float64)
+    vp = torch.zeros(b, h, lmax, d, dtype=torch.float64)
+    gp = torch.zeros(b, h, lq, d, dtype=torch.float64)
+    mask = torch.zeros(b, 1, lq, lmax, dtype=torch.bool)
+    if broadcast_q:
+        qsh = torch.tensor(q, dtype=torch.float64).permute(1, 0, 2).contiguous().requires_grad_(True)
+        qp = qsh.unsqueeze(0).expand(b, h, lq, d)
+    else:
+        qp0 = torch.zeros(b, h, lq, d, dtype=torch.float64)
+    for i in range(b):
+        a, e = int(off[i]), int(off[i + 1])
+        n = e - a
+        kp[i, :, :n] = torch.tensor(k[a:e]).permute(1, 0, 2)
+        vp[i, :, :n] = torch.tensor(v[a:e]).permute(1, 0, 2)
+        if broadcast_q:
+            gp[i] = torch.tensor(g[i * lq:(i + 1) * lq]).permute(1, 0, 2)
+            mask[i, 0, :, :n] = True
+        else:
+            qp0[i, :, :n] = torch.tensor(q[a:e]).permute(1, 0, 2)
+            gp[i, :, :n] = torch.tensor(g[a:e]).permute(1, 0, 2)
+            vis = torch.ones(lq, lmax, dtype=torch.bool)
+            vis[:, n:] = False
+            if causal:
+                vis &= torch.tril(torch.ones(lq, lmax, dtype=torch.bool))
+            mask[i, 0] = vis
+            mask[i, 0, n:, :] = False
+            mask[i, 0, n:, 0] = True  # padded query rows: keep finite, discarded below
+    if not broadcast_q:
+        qp = qp0.requires_grad_(True)
+    kp.requires_grad_(True)
+    vp.requires_grad_(True)
+    o = F.scaled_dot_product_attention(qp, kp, vp, attn_mask=mask, scale=scale)
+    scores = (qp @ kp.transpose(-1, -2)) * scale
+    lse = torch.logsumexp(scores.masked_fill(~mask, -math.inf), dim=-1)
+    (o * gp).sum().backward()
+    rows = b * lq if broadcast_q else int(off[-1])
+    o_ref = np.zeros((rows, h, d))
+    lse_ref = np.zeros((h, rows))
+    dk_ref = np.zeros_like(k)
+    dv_ref = np.zeros_like(v)
+    dq_ref = np.zeros_like(q)
+    for i in range(b):
+        a, e = int(off[i]), int(off[i + 1])
+        n = e - a
+        r0, r1 = (i * lq, (i + 1) * lq) if broadcast_q else (a, e)
+        nr = lq if broadcast_q else n
+        o_ref[r0:r1] = o[i, :, :nr].permute(1, 0, 2).detach().numpy()
+        lse_ref[:, r0:r1] = lse[i, :, :nr].detach().numpy()
+        dk_ref[a:e] = kp.grad[i, :, :n].permute(1, 0, 2).numpy()
+        dv_ref[a:e] = vp.grad[i, :, :n].permute(1, 0, 2).numpy()
+        if not broadcast_q:
+            dq_ref[a:e] = qp.grad[i, :, :n].permute(1, 0, 2).numpy()
+    if broadcast_q:
+        dq_ref = qsh.grad.permute(1, 0, 2).numpy()
+    return o_ref, lse_ref, dq_ref, dk_ref, dv_ref
+
+
+MODES = [(True, False), (False, False), (False, True)]  # (broadcast_q, causal)
+
+
+@pytest.mark.parametrize("broadcast_q,causal", MODES)
+@pytest.mark.parametrize("seed", [0, 1])
+def test_matches_padded_dense_sdpa(broadcast_q, causal, seed):
+    rng = np.random.default_rng(100 + seed)
+    lengths = [5, 1, 17, 9] if seed == 0 else [33, 2, 64, 7, 1]
+    h, d, lq = 3, 8, (6 if seed == 0 else 19)
+    scale = 0.37
+    q, k, v, g, off = _rand_case(rng, lengths, h, d, broadcast_q, lq)
+    o, lse = oracle.forward(q, k, v, off, broadcast_q=broadcast_q, causal=causal, scale=scale)
+    dq, dk, dv = oracle.backward(q, k, v, off, g, broadcast_q=broadcast_q, causal=causal, scale=scale)
+    ro, rlse, rdq, rdk, rdv = _padded_reference(q, k, v, g, off, broadcast_q, causal, scale)
+    for name, a, r in [("O", o, ro), ("LSE", lse, rlse), ("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)]:
+        np.testing.assert_allclose(a, r, rtol=0, atol=1e-12, err_msg=name)
+
+
+@pytest.mark.parametrize("broadcast_q,causal", MODES)
+def test_finite_differences(broadcast_q, causal):
+    """Central differences of L = sum(O * G) for every element of Q, K and V."""
+    rng = np.random.default_rng(7)
+    lengths, h, d, lq, scale = [1, 2, 5], 2, 4, 3, 0.8
+    q, k, v, g, off = _rand_case(rng, lengths, h, d, broadcast_q, lq)
+    kw = dict(broadcast_q=broadcast_q, causal=causal, scale=scale)
+    dq, dk, dv = oracle.backward(q, k, v, off, g, **kw)
+
+    def loss(q_, k_, v_):
+        return float((oracle.forward(q_, k_, v_, off, **kw)[0] * g).sum())
+
+    eps = 1e-6
+    for name, x, grad in [("q", q, dq), ("k", k, dk), ("v", v, dv)]:
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = {"q": q, "k": k, "v": v}
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (loss(**{n + "_": a for n, a in args_p.items()})
+                        - loss(**{n + "_": a for n, a in args_m.items()})) / (2 * eps)
+        err = np.abs(num - grad).max() / max(np.abs(grad).max(), 1e-30)
+        assert err <= 1e-6, (name, err)
+
+
+@pytest.mark.parametrize("broadcast_q,causal", MODES)
+def test_rows_sum_to_one(broadcast_q, causal):
+    """With V = 1 everywhere the output is exactly the softmax row sum, i.e. 1."""
+    rng = np.random.default_rng(3)
+    q, k, v, g, off = _rand_case(rng, [4, 1, 30], 2, 16, broadcast_q, 9)
+    o, _ = oracle.forward(q * 3, k * 3, np.ones_like(v), off, broadcast_q=broadcast_q,
+                          causal=causal, scale=1.0)
+    np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("broadcast_q", [True, False])
+def test_single_key_closed_form(broadcast_q):
+    """n_b = 1: O_i = V_0, LSE_i = c q_i.k_0, dK_0 = 0, dQ contribution 0, dV_0 = sum_i G_i."""
+    rng = np.random.default_rng(11)
+    lq, h, d, c = 5, 2, 8, 0.3
+    q, k, v, g, off = _rand_case(rng, [1], h, d, broadcast_q, lq)
+    o, lse = oracle.forward(q, k, v, off, broadcast_q=broadcast_q, scale=c)
+    dq, dk, dv = oracle.backward(q, k, v, off, g, broadcast_q=broadcast_q, scale=c)
+    rows = o.shape[0]
+    for hh in range(h):
+        np.testing.assert_array_equal(o[:, hh, :], np.broadcast_to(v[0, hh], (rows, d)))
+        np.testing.assert_allclose(lse[hh], c * (q[:, hh, :] @ k[0, hh]), atol=1e-14)
+        np.testing.assert_allclose(dv[0, hh], g[:, hh, :].sum(axis=0), atol=1e-13)
+    assert np.abs(dk).max() < 1e-14
+    assert np.abs(dq).max() < 1e-14
+
+
+def test_broadcast_dq_is_sum_over_sequences():
+    rng = np.random.default_rng(5)
+    lengths, h, d, lq, c = [7, 3, 12, 1], 2, 8, 6, 0.5
+    q, k, v, g, off = _rand_case(rng, lengths, h, d, True, lq)
+    dq, dk, dv = oracle.backward(q, k, v, off, g, broadcast_q=True, scale=c)
+    acc = np.zeros_like(q)
+    for b in range(len(lengths)):
+        a, e = off[b], off[b + 1]
+        dq_b, dk_b, dv_b = oracle.backward(q, k[a:e], v[a:e], np.array([0, e - a]),
+                                           g[b * lq:(b + 1) * lq], broadcast_q=True, scale=c)
+        acc += dq_b
+        np.testing.assert_allclose(dk[a:e], dk_b, atol=1e-13)
+        np.testing.assert_allclose(dv[a:e], dv_b, atol=1e-13)
+    np.testing.assert_allclose(dq, acc, atol=1e-12)
+
+
+@pytest.mark.parametrize("broadcast_q,causal", MODES)
+def test_exact_identities(broadcast_q, causal):
+    rng = np.random.default_rng(9)
+    lengths, h, d, lq, c = [6, 1, 20, 3], 2, 8, 5, 0.45
+    q, k, v, g, off = _rand_case(rng, lengths, h, d, broadcast_q, lq)
+    kw = dict(broadcast_q=broadcast_q, causal=causal, scale=c)
+    o, _ = oracle.forward(q, k, v, off, **kw)
+    dq, dk, dv = oracle.backward(q, k, v, off, g, **kw)
+    for b in range(len(lengths)):
+        a, e = off[b], off[b + 1]
+        r0, r1 = (b * lq, (b + 1) * lq) if broadcast_q else (a, e)
+        # softmax shift invariance: the key gradients of one sequence sum to zero
+        np.testing.assert_allclose(dk[a:e].sum(axis=0), 0.0, atol=1e-12)
+        # rows of P sum to one: the value gradients sum to the upstream gradient sum
+        np.testing.assert_allclose(dv[a:e].sum(axis=0), g[r0:r1].sum(axis=0), atol=1e-12)
+    for hh in range(h):
+        # scores depend on Q K^T only: scaling Q by t and K by 1/t changes nothing
+        np.testing.assert_allclose((q[:, hh] * dq[:, hh]).sum(), (k[:, hh] * dk[:, hh]).sum(), atol=1e-11)
+    # O is linear in V
+    np.testing.assert_allclose((v * dv).sum(), (o * g).sum(), atol=1e-11)
+    if causal:
+        for b in range(len(lengths)):
+            a = off[b]
+            np.testing.assert_array_equal(o[a], v[a])
+
+
+def test_permuting_sequences():
+    rng = np.random.default_rng(12)
+    lengths, h, d, lq, c = [4, 9, 1, 6], 2, 8, 5, 0.6
+    q, k, v, g, off = _rand_case(rng, lengths, h, d, True, lq)
+    perm = [2, 0, 3, 1]
+    ks = [k[off[b]:off[b + 1]] for b in range(4)]
+    vs = [v[off[b]:off[b + 1]] for b in range(4)]
+    gs = [g[b * lq:(b + 1) * lq] for b in range(4)]
+    k2 = np.concatenate([ks[p] for p in perm])
+    v2 = np.concatenate([vs[p] for p in perm])
+    g2 = np.concatenate([gs[p] for p in perm])
+    off2 = np.concatenate([[0], np.cumsum([lengths[p] for p in perm])])
+    o, lse = oracle.forward(q, k, v, off, broadcast_q=True, scale=c)
+    o2, lse2 = oracle.forward(q, k2, v2, off2, broadcast_q=True, scale=c)
+    dq, dk, dv = oracle.backward(q, k, v, off, g, broadcast_q=True, scale=c)
+    dq2, dk2, dv2 = oracle.backward(q, k2, v2, off2, g2, broadcast_q=True, scale=c)
+    for j, p in enumerate(perm):
+        np.testing.assert_array_equal(o2[j * lq:(j + 1) * lq], o[p * lq:(p + 1) * lq])
+        np.testing.assert_array_equal(lse2[:, j * lq:(j + 1) * lq], lse[:, p * lq:(p + 1) * lq])
+        np.testing.assert_array_equal(dk2[off2[j]:off2[j + 1]], dk[off[p]:off[p + 1]])
+        np.testing.assert_array_equal(dv2[off2[j]:off2[j + 1]], dv[off[p]:off[p + 1]])
+    np.testing.assert_allclose(dq2, dq, atol=1e-12)
+
+
+def test_duplicating_a_broadcast_sequence_doubles_its_dq():
+    rng = np.random.default_rng(13)
+    h, d, lq, c = 2, 8, 4, 0.7
+    q, k, v, g, off = _rand_case(rng, [5], h, d, True, lq)
+    dq1, _, _ = oracle.backward(q, k, v, off, g, broadcast_q=True, scale=c)
+    k2, v2, g2 = np.concatenate([k, k]), np.concatenate([v, v]), np.concatenate([g, g])
+    o2, _ = oracle.forward(q, k2, v2, [0, 5, 10], broadcast_q=True, scale=c)
+    o1, _ = oracle.forward(q, k, v, off, broadcast_q=True, scale=c)
+    dq2, _, _ = oracle.backward(q, k2, v2, [0, 5, 10], g2, broadcast_q=True, scale=c)
+    np.testing.assert_array_equal(o2[:lq], o1)
+    np.testing.assert_array_equal(o2[lq:], o1)
+    np.testing.assert_allclose(dq2, 2 * dq1, atol=1e-13)
+
+
+@pytest.mark.parametrize("block", [4, 64])
+def test_fixed_length_self_attention_is_block_diagonal(block):
+    """All n_b equal: jagged self-attention == dense attention with a block-diagonal mask."""
+    rng = np.random.default_rng(21)
+    nblk, h, d, c = 3, 2, 8, 0.35
+    t = nblk * block
+    q, k, v, g, off = _rand_case(rng, [block] * nblk, h, d, False, 0)
+    o, lse = oracle.forward(q, k, v, off, broadcast_q=False, scale=c)
+    blk = np.arange(t) // block
+    for hh in range(h):
+        s = c * q[:, hh] @ k[:, hh].T
+        s = np.where(blk[:, None] == blk[None, :], s, -np.inf)
+        ref_lse = np.log(np.exp(s).sum(axis=1))
+        ref_o = (np.exp(s - ref_lse[:, None])) @ v[:, hh]
+        np.testing.assert_allclose(o[:, hh], ref_o, atol=1e-12)
+        np.testing.assert_allclose(lse[hh], ref_lse, atol=1e-12)
+
+
+def test_golden_two_key_worked_example():
+    ex = json.load(open(os.path.join(GOLDEN, "two_key_worked_example.json")))
+    q = np.array(ex["q"])[:, None, :]
+    k = np.array(ex["k"])[:, None, :]
+    v = np.array(ex["v"])[:, None, :]
+    g = np.array(ex["g"])[:, None, :]
+    off = [0, 2]
+    o, lse = oracle.forward(q, k, v, off, broadcast_q=True, scale=ex["scale"])
+    dq, dk, dv = oracle.backward(q, k, v, off, g, broadcast_q=True, scale=ex["scale"])
+    np.testing.assert_allclose(o[:, 0], ex["o"], atol=1e-15)
+    np.testing.assert_allclose(lse[0], ex["lse"], atol=1e-15)
+    np.testing.assert_allclose(dq[:, 0], ex["dq"], atol=1e-15)
+    np.testing.assert_allclose(dk[:, 0], ex["dk"], atol=1e-15)
+    np.testing.assert_allclose(dv[:, 0], ex["dv"], atol=1e-15)
+
+
+def test_golden_causal_two_token_example():
+    ex = json.load(open(os.path.join(GOLDEN, "causal_two_token_example.json")))
+    q = np.array(ex["q"])[:, None, :]
+    k = np.array(ex["k"])[:, None, :]
+    v = np.array(ex["v"])[:, None, :]
+    o, lse = oracle.forward(q, k, v, [0, 2], broadcast_q=False, causal=True, scale=ex["scale"])
+    np.testing.assert_allclose(o[:, 0], ex["o"], atol=1e-15)
+    np.testing.assert_allclose(lse[0], ex["lse"], atol=1e-15)
+
+
+def test_empty_sequence_reading():
+    """n_b = 0: its O rows are 0, LSE is -inf, and it adds nothing to dQ."""
+    rng = np.random.default_rng(4)
+    lq, h, d = 3, 2, 4
+    q, k, v, g, off = _rand_case(rng, [2, 0, 3], h, d, True, lq)
+    o, lse = oracle.forward(q, k, v, off, broadcast_q=True, scale=0.5)
+    assert np.all(o[lq:2 * lq] == 0) and np.all(np.isneginf(lse[:, lq:2 * lq]))
+    dq, _, _ = oracle.backward(q, k, v, off, g, broadcast_q=True, scale=0.5)
+    keep = [0, 1, 2, 5, 6, 7, 8]
+    off2 = [0, 2, 5]
+    g2 = np.concatenate([g[:lq], g[2 * lq:]])
+    dq2, _, _ = oracle.backward(q, k, v, off2, g2, broadcast_q=True, scale=0.5)
+    np.testing.assert_allclose(dq, dq2, atol=1e-14)
+    assert keep  # rows of the empty sequence were checked above
+
+
+def test_rejects_broadcast_causal_and_bad_offsets():
+    rng = np.random.default_rng(1)
+    q, k, v, g, off = _rand_case(rng, [3], 1, 4, True, 2)
+    with pytest.raises(ValueError):
+        oracle.forward(q, k, v, off, broadcast_q=True, causal=True, scale=1.0)
+    with pytest.raises(ValueError):
+        oracle.forward(q, k, v, [0, 2], broadcast_q=True, scale=1.0)
+
+
+def test_workload_recipes_seed0():
+    """The length recipes reproduce the seed-0 statistics recorded for the workloads."""
+    c = workloads.make_workload("tiny_broadcast")
+    assert list(c["lengths"]) == [218, 164, 131, 70]
+    assert c["offsets"].dtype == torch.int64
+    rng = np.random.default_rng(0)
+    assert int(workloads.draw_lengths(workloads.WORKLOADS["gem_broadcast"], rng).sum()) == 1017228
+    rng = np.random.default_rng(0)
+    assert int(workloads.draw_lengths(workloads.WORKLOADS["dq_stress"], rng).sum()) == 1121466
+    rng = np.random.default_rng(0)
+    ln = workloads.draw_lengths(workloads.WORKLOADS["self_causal"], rng)
+    assert int(ln.sum()) == 528065 and ln.min() == 64 and ln.max() == 4096
+    rng = np.random.default_rng(0)
+    assert int(workloads.draw_lengths(workloads.WORKLOADS["block64"], rng).sum()) == 1152 * 2048
+
+
+def test_bf16_inputs_round_to_nearest_even():
+    x = workloads.normal_bf16(np.random.default_rng(0), (1000,))
+    ref = torch.from_numpy(np.random.default_rng(0).standard_normal(1000, dtype=np.float32))
+    assert torch.equal(x, ref.to(torch.bfloat16))
