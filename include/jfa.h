@@ -1,0 +1,130 @@
+/*
+ * jfa.h -- C ABI of the MI355X (gfx950) Jagged Flash Attention library (libjfa.so).
+ *
+ * Jagged Flash Attention is exact softmax attention applied directly to packed,
+ * unpadded sequences addressed through an offsets tensor ("Meta's TLX attention
+ * kernel outpaces FlashAttention-4 on B200", section "GEM's sequences do not fit
+ * a fixed grid"; "Optimizing Jagged Flash Attention with TLX" reading note,
+ * section "Why variable lengths change the problem").  Two modes:
+ *
+ *   broadcast-Q  one dense query sequence Q [Lq, H, D] attends to the K/V of every
+ *                sequence b; output rows b*Lq + i.  In the backward pass every
+ *                sequence adds into the same dQ (same sections of both pages).
+ *   self         Q, K and V are all packed with the same offsets; optional causal
+ *                mask inside each sequence (key j visible to query i iff j <= i,
+ *                both counted from the sequence start).  Block-diagonal attention
+ *                ("Meta's TLX Block Attention Beats Flash Attention v2 by 2.3x on
+ *                Blackwell GPUs", section "The Pattern That Changes Everything") is
+ *                the case where every sequence has 64 tokens.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major memory, 16-byte
+ *     aligned.  bf16 means IEEE bfloat16 stored as 2 bytes.
+ *   - q      bf16 [Lq, H, D] (broadcast) or [T, H, D] (self).
+ *   - k, v   bf16 [T, H, D], T = total_kv = offsets[batch].
+ *   - offsets int32 or int64 [batch + 1] (offsets_is_int64 selects), device memory.
+ *     Preconditions (not checked on the device): offsets[0] = 0, non-decreasing,
+ *     offsets[batch] = total_kv.
+ *   - o, d_o bf16 [rows, H, D] with rows = batch*Lq (broadcast) or T (self).
+ *   - lse    fp32 [H, rows]: natural-log log-sum-exp of the scaled scores
+ *            c * q_i . k_j over the visible keys; -inf for a row with no key.
+ *   - dq like q, dk and dv like k; all bf16.  Accumulation is fp32 throughout.
+ *   - head_dim must be 64 or 128 (the page on Block Attention, section "Who Should
+ *     Use This", names these two head sizes); heads >= 1.
+ *   - Work is enqueued on `stream` without any host synchronisation; the caller
+ *     keeps every buffer alive until that work completes.  Outputs are
+ *     overwritten, never accumulated into.
+ *   - The library allocates no device memory: scratch space comes from the
+ *     caller's `workspace` (size from the matching *_workspace_size call, 256-byte
+ *     aligned).  Its only state is a per-device cache of the compute-unit count
+ *     and the schedule selector below.
+ *   - Errors are returned as jfa_status_t; nothing aborts or throws across the
+ *     ABI.  jfa_last_error() gives a thread-local message for the last non-OK
+ *     status.  batch == 0 or rows == 0 is an OK no-op (outputs untouched except
+ *     that dk/dv rows, which then do not exist).
+ */
+#ifndef JFA_H_
+#define JFA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  JFA_OK = 0,
+  JFA_ERR_INVALID_ARGUMENT = 1,   /* null/misaligned pointer, negative size, bad scale, bad flag */
+  JFA_ERR_UNSUPPORTED = 2,        /* head_dim not in {64,128}, broadcast_q together with causal */
+  JFA_ERR_WORKSPACE_TOO_SMALL = 3,
+  JFA_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+} jfa_status_t;
+
+/* Tile schedule used by the forward and backward kernels (process-wide).
+ *   JFA_SCHED_SORTED_ZIGZAG  forward tiles sorted by KV work (descending) and dealt
+ *                            boustrophedon across persistent workgroups; backward
+ *                            valid (b, h, KV-block) tiles dealt round-robin (JFA news
+ *                            page, "Five changes unlocked the gains", item 1).  Default.
+ *   JFA_SCHED_IDENTITY       tiles in natural (b, block, h) order, dealt round-robin.
+ *   JFA_SCHED_DYNAMIC        sorted tiles claimed through a device atomic counter by
+ *                            whichever workgroup is free (the same section, item 2).
+ * Results are independent of the schedule: O, LSE, dK and dV bit for bit, dQ up to
+ * the order of its fp32 additions. */
+typedef enum {
+  JFA_SCHED_SORTED_ZIGZAG = 0,
+  JFA_SCHED_IDENTITY = 1,
+  JFA_SCHED_DYNAMIC = 2
+} jfa_schedule_t;
+
+/* Selects the schedule for subsequent calls from any thread.  Returns
+ * JFA_ERR_INVALID_ARGUMENT for an unknown value. */
+jfa_status_t jfa_set_schedule(int schedule);
+int jfa_get_schedule(void);
+
+/* Bytes of workspace jfa_fwd needs for these sizes (0 if the sizes are invalid). */
+size_t jfa_fwd_workspace_size(int64_t batch, int64_t num_heads, int64_t head_dim,
+                              int64_t q_len, int64_t total_kv, int broadcast_q, int causal);
+
+/* Bytes of workspace jfa_bwd needs for these sizes (0 if the sizes are invalid).
+ * It holds the fp32 dQ accumulator (8 stripes of [Lq, H, D] in broadcast mode,
+ * [T, H, D] in self mode), the row sums delta [H, rows] and the tile plan. */
+size_t jfa_bwd_workspace_size(int64_t batch, int64_t num_heads, int64_t head_dim,
+                              int64_t q_len, int64_t total_kv, int broadcast_q, int causal);
+
+/* Forward pass: O = softmax(c Q K^T) V per sequence and head, and its LSE.
+ * q_len is Lq (> 0) in broadcast mode and must be 0 in self mode.  softmax_scale
+ * c must be finite and > 0. */
+jfa_status_t jfa_fwd(const void* q, const void* k, const void* v,
+                     const void* offsets, int offsets_is_int64,
+                     int64_t batch, int64_t num_heads, int64_t head_dim,
+                     int64_t q_len, int64_t total_kv,
+                     int broadcast_q, int causal, float softmax_scale,
+                     void* o, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward pass: gradients of sum(O * dO) with respect to q, k and v, given the
+ * o and lse that jfa_fwd returned for the same inputs.  In broadcast mode dq is
+ * the sum over all sequences (JFA news page, "GEM's sequences do not fit a fixed
+ * grid").  Same size rules as jfa_fwd. */
+jfa_status_t jfa_bwd(const void* q, const void* k, const void* v,
+                     const void* offsets, int offsets_is_int64,
+                     int64_t batch, int64_t num_heads, int64_t head_dim,
+                     int64_t q_len, int64_t total_kv,
+                     int broadcast_q, int causal, float softmax_scale,
+                     const void* o, const float* lse, const void* d_o,
+                     void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Thread-local, NUL-terminated description of the last non-OK status returned
+ * on this thread ("" if none).  Owned by the library; valid until the next call. */
+const char* jfa_last_error(void);
+
+/* Library version string, e.g. "jfa 0.1 gfx950". */
+const char* jfa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JFA_H_ */

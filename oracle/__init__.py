@@ -6,6 +6,7 @@ Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 from .attention import (  # noqa: F401
     sequence_forward,
     sequence_backward,
+    sequence_dq_rows,
     forward,
     backward,
     row_count,

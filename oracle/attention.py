@@ -98,6 +98,32 @@ def sequence_backward(qb, kb, vb, gb, scale: float, causal: bool = False):
     return dq, dk, dv
 
 
+def sequence_dq_rows(qb, kb, vb, gb, rows, scale: float, causal: bool = False):
+    """dQ of selected query rows only, for one sequence and one head.
+
+    Each row of dQ depends only on that row's scores: dQ_i = c sum_j dS_ij k_j with
+    dS_ij = P_ij (dP_ij - delta_i).  Same definition as sequence_backward, restricted
+    to the listed rows so that a batch-summed dQ row can be checked at full size.
+    Returns [len(rows), D].
+    """
+    qb, kb, vb, gb = _f64(qb), _f64(kb), _f64(vb), _f64(gb)
+    rows = np.asarray(rows, dtype=np.int64)
+    n, d = kb.shape[0], kb.shape[1]
+    if n == 0:
+        return np.zeros((len(rows), d))
+    s = scale * (qb[rows] @ kb.T)
+    if causal:
+        j = np.arange(n)[None, :]
+        s = np.where(j <= rows[:, None], s, -np.inf)
+    m = s.max(axis=1)
+    lse = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+    p = np.exp(s - lse[:, None])
+    dp = gb[rows] @ vb.T
+    delta = (p * dp).sum(axis=1)
+    ds = p * (dp - delta[:, None])
+    return scale * (ds @ kb)
+
+
 def row_count(offsets, broadcast_q: bool, q_len: int) -> int:
     """Number of output rows: B * Lq for broadcast-Q, T = offsets[B] otherwise."""
     offsets = np.asarray(offsets, dtype=np.int64)

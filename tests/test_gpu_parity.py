@@ -1,0 +1,226 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Small cases are compared element by element; the full-size workloads run in the
+launch configuration the benchmark times and are checked on sampled sequences
+(all of their O / LSE / dK / dV rows, and dQ rows in self mode) and, for the
+batch-summed broadcast dQ, on sampled query rows summed over every sequence.
+
+Tolerances (from the method's accuracy target): max |O - O_ref| <= 1e-2,
+max |LSE - LSE_ref| <= 1e-3, and for dQ, dK, dV max abs error <= 2e-2 * max |ref|.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = 1e-2
+TOL_LSE = 1e-3
+TOL_GRAD = 2e-2
+
+
+def _jfa():
+    import variable_length_flash_jfa_amd as jfa
+    return jfa
+
+
+def _run(case, sched=None, offsets_dtype=None):
+    jfa = _jfa()
+    dev = "cuda"
+    q, k, v, g = (case[x].to(dev) for x in ("q", "k", "v", "g"))
+    off = case["offsets"].to(dev)
+    if offsets_dtype is not None:
+        off = off.to(offsets_dtype)
+    old = jfa.get_schedule()
+    if sched is not None:
+        jfa.set_schedule(sched)
+    try:
+        o, lse = jfa.fwd(q, k, v, off, broadcast_q=case["broadcast_q"], causal=case["causal"],
+                         scale=case["scale"])
+        dq, dk, dv = jfa.bwd(q, k, v, off, o, lse, g, broadcast_q=case["broadcast_q"],
+                             causal=case["causal"], scale=case["scale"])
+        torch.cuda.synchronize()
+    finally:
+        jfa.set_schedule(old)
+    return {"o": o.cpu(), "lse": lse.cpu(), "dq": dq.cpu(), "dk": dk.cpu(), "dv": dv.cpu()}
+
+
+def _f64(t):
+    return t.to(torch.float64).numpy()
+
+
+def _check_lse(got, ref, what="LSE"):
+    got = np.asarray(got, dtype=np.float64)
+    inf_ref = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), inf_ref), f"{what}: -inf pattern differs"
+    fin = ~inf_ref
+    if fin.any():
+        err = np.abs(got[fin] - ref[fin]).max()
+        assert err <= TOL_LSE, f"{what}: max abs err {err:.3e} > {TOL_LSE}"
+
+
+def _check_abs(got, ref, tol, what):
+    err = np.abs(np.asarray(got, dtype=np.float64) - ref).max() if ref.size else 0.0
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.3e}"
+
+
+def _check_grad(got, ref, what):
+    scale = np.abs(ref).max() if ref.size else 0.0
+    _check_abs(got, ref, TOL_GRAD * max(scale, 1e-30), what)
+
+
+def _compare_full(case, out, zero_grad_floor=0.0):
+    kw = dict(broadcast_q=case["broadcast_q"], causal=case["causal"], scale=case["scale"])
+    off = case["offsets"].numpy()
+    q, k, v, g = (_f64(case[x]) for x in ("q", "k", "v", "g"))
+    o_ref, lse_ref = oracle.forward(q, k, v, off, **kw)
+    dq_ref, dk_ref, dv_ref = oracle.backward(q, k, v, off, g, **kw)
+    _check_abs(_f64(out["o"]), o_ref, TOL_O, "O")
+    _check_lse(out["lse"].numpy(), lse_ref)
+    for name, ref in (("dq", dq_ref), ("dk", dk_ref)):
+        if zero_grad_floor:
+            _check_abs(_f64(out[name]), ref, max(zero_grad_floor, TOL_GRAD * np.abs(ref).max()), name)
+        else:
+            _check_grad(_f64(out[name]), ref, name)
+    _check_grad(_f64(out["dv"]), dv_ref, "dV")
+
+
+SMALL_CASES = {
+    # name: (lengths, heads, head_dim, broadcast_q, causal, q_len)
+    "bcast_d64_lq64": ([218, 164, 131, 70], 2, 64, True, False, 64),
+    "bcast_d128_lq256_ragged": ([1, 63, 64, 65, 130, 1000], 2, 128, True, False, 256),
+    "bcast_d128_lq512": ([5, 300, 700], 2, 128, True, False, 512),
+    "bcast_d128_lq100": ([17, 64, 129], 3, 128, True, False, 100),
+    "bcast_d128_lq33": ([17, 64, 129, 2], 2, 128, True, False, 33),
+    "bcast_d64_lq200": ([3, 77, 256, 513], 2, 64, True, False, 200),
+    "bcast_empty_seq": ([10, 0, 70], 2, 64, True, False, 64),
+    "self_d128": ([1, 17, 64, 65, 200, 513], 2, 128, False, False, 0),
+    "self_d128_causal": ([1, 5, 64, 127, 128, 129, 300, 700], 2, 128, False, True, 0),
+    "self_d64_causal": ([2, 33, 190, 257], 3, 64, False, True, 0),
+    "self_d64": ([2, 33, 190, 257], 3, 64, False, False, 0),
+    "self_empty_seq_causal": ([20, 0, 45], 2, 128, False, True, 0),
+    "block64": ([64] * 40, 4, 128, False, False, 0),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL_CASES))
+def test_small_cases_match_oracle(name):
+    lengths, h, d, bq, causal, lq = SMALL_CASES[name]
+    case = workloads.make_case(lengths, heads=h, head_dim=d, broadcast_q=bq, causal=causal,
+                               q_len=lq, seed=zlib.crc32(name.encode()) % 1000)
+    out = _run(case)
+    _compare_full(case, out)
+
+
+def test_tiny_broadcast_workload_int64_and_int32():
+    case = workloads.make_workload("tiny_broadcast")
+    assert case["offsets"].dtype == torch.int64
+    out64 = _run(case)
+    _compare_full(case, out64)
+    out32 = _run(case, offsets_dtype=torch.int32)
+    for name in ("o", "lse", "dk", "dv"):
+        assert torch.equal(out64[name], out32[name]), name
+    _check_grad(_f64(out32["dq"]), _f64(out64["dq"]).astype(np.float64), "dQ int32 vs int64")
+
+
+def test_single_key_sequences_return_v_exactly():
+    case = workloads.make_case([1, 1, 1], heads=2, head_dim=128, broadcast_q=True, q_len=40, seed=5)
+    out = _run(case)
+    v = case["v"]
+    for b in range(3):
+        rows = out["o"][b * 40:(b + 1) * 40]
+        assert torch.equal(rows, v[b:b + 1].expand(40, -1, -1)), b
+    # With one key the exact dQ and dK are identically 0, so the relative bound
+    # degenerates.  Here O = V exactly, so delta = dO.O and dP = dO.V differ only by
+    # the order of two fp32 dot products of 128 N(0,1) products (a few 1e-6), which
+    # dS = P (dP - delta) carries into dQ and dK; 1e-4 bounds that.
+    _compare_full(case, out, zero_grad_floor=1e-4)
+
+
+@pytest.mark.parametrize("bq,causal", [(True, False), (False, True)])
+def test_schedules_agree(bq, causal):
+    jfa = _jfa()
+    lengths = [700, 3, 64, 129, 1000, 65, 256, 31] if causal else [700, 3, 64, 129, 1000, 65, 2000, 31]
+    case = workloads.make_case(lengths, heads=3, head_dim=128, broadcast_q=bq, causal=causal,
+                               q_len=256 if bq else 0, seed=17)
+    outs = [_run(case, sched=s) for s in (jfa.SCHED_SORTED_ZIGZAG, jfa.SCHED_IDENTITY, jfa.SCHED_DYNAMIC)]
+    for other in outs[1:]:
+        for name in ("o", "lse", "dk", "dv"):
+            assert torch.equal(outs[0][name], other[name]), name
+        _check_grad(_f64(other["dq"]), _f64(outs[0]["dq"]), "dQ across schedules")
+    _compare_full(case, outs[0])
+
+
+def test_autograd_wrapper():
+    jfa = _jfa()
+    case = workloads.make_case([40, 90], heads=2, head_dim=64, broadcast_q=True, q_len=48, seed=3)
+    q = case["q"].cuda().requires_grad_(True)
+    k = case["k"].cuda().requires_grad_(True)
+    v = case["v"].cuda().requires_grad_(True)
+    o = jfa.jagged_attention(q, k, v, case["offsets"].cuda(), broadcast_q=True)
+    o.backward(case["g"].cuda())
+    out = {"o": o.detach().cpu(), "lse": None, "dq": q.grad.cpu(), "dk": k.grad.cpu(), "dv": v.grad.cpu()}
+    ref = _run(case)
+    for name in ("o", "dk", "dv"):
+        assert torch.equal(out[name], ref[name]), name
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled checks
+# ---------------------------------------------------------------------------
+
+def _sample_sequences(lengths, rng, count=5):
+    order = np.argsort(lengths, kind="stable")
+    picks = {int(order[0]), int(order[-1]), int(order[len(order) // 2])}
+    while len(picks) < min(count, len(lengths)):
+        picks.add(int(rng.integers(len(lengths))))
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("name", ["gem_broadcast", "dq_stress", "self_causal", "block64"])
+def test_full_size_workload_sampled(name):
+    case = workloads.make_workload(name, seed=0, device="cuda")
+    w = case["workload"]
+    out = _run(case)
+    off = case["offsets"].cpu().numpy().astype(np.int64)
+    lengths = np.diff(off)
+    rng = np.random.default_rng(123)
+    seqs = _sample_sequences(lengths, rng)
+    heads = sorted({0, w.heads - 1})
+    lq = w.q_len
+    qd, kd, vd, gd = case["q"], case["k"], case["v"], case["g"]
+    q_host = _f64(qd.cpu()) if w.broadcast_q else None
+    o_err = lse_err = 0.0
+    for b in seqs:
+        a, e = int(off[b]), int(off[b + 1])
+        r0, r1 = (b * lq, (b + 1) * lq) if w.broadcast_q else (a, e)
+        for h in heads:
+            qb = q_host[:, h] if w.broadcast_q else _f64(qd[a:e, h].cpu())
+            kb, vb = _f64(kd[a:e, h].cpu()), _f64(vd[a:e, h].cpu())
+            gb = _f64(gd[r0:r1, h].cpu())
+            o_ref, lse_ref = oracle.sequence_forward(qb, kb, vb, case["scale"], w.causal)
+            dq_ref, dk_ref, dv_ref = oracle.sequence_backward(qb, kb, vb, gb, case["scale"], w.causal)
+            _check_abs(_f64(out["o"][r0:r1, h]), o_ref, TOL_O, f"O seq {b} head {h}")
+            _check_lse(out["lse"][h, r0:r1].numpy(), lse_ref, f"LSE seq {b} head {h}")
+            _check_grad(_f64(out["dk"][a:e, h]), dk_ref, f"dK seq {b} head {h}")
+            _check_grad(_f64(out["dv"][a:e, h]), dv_ref, f"dV seq {b} head {h}")
+            if not w.broadcast_q:
+                _check_grad(_f64(out["dq"][a:e, h]), dq_ref, f"dQ seq {b} head {h}")
+    if w.broadcast_q:
+        # batch-summed dQ on sampled query rows: every sequence contributes
+        rows = sorted({0, lq - 1, *rng.integers(lq, size=4).tolist()})
+        k_host, v_host, g_host = _f64(kd.cpu()), _f64(vd.cpu()), _f64(gd.cpu())
+        for h in heads:
+            ref = np.zeros((len(rows), w.head_dim))
+            for b in range(w.batch):
+                a, e = int(off[b]), int(off[b + 1])
+                ref += oracle.sequence_dq_rows(q_host[:, h], k_host[a:e, h], v_host[a:e, h],
+                                               g_host[b * lq:(b + 1) * lq, h], rows, case["scale"])
+            _check_grad(_f64(out["dq"][rows, h]), ref, f"dQ rows {rows} head {h}")
+    assert np.isfinite(out["o"].float().numpy()).all()
+    assert np.isfinite(out["dq"].float().numpy()).all()

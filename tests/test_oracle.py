@@ -340,3 +340,15 @@ def test_bf16_inputs_round_to_nearest_even():
     x = workloads.normal_bf16(np.random.default_rng(0), (1000,))
     ref = torch.from_numpy(np.random.default_rng(0).standard_normal(1000, dtype=np.float32))
     assert torch.equal(x, ref.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dq_rows_match_full_backward(causal):
+    """The row-restricted dQ equals the matching rows of the full backward."""
+    rng = np.random.default_rng(31)
+    n, d, c = 23, 8, 0.4
+    qb, kb, vb, gb = (rng.standard_normal((n, d)) for _ in range(4))
+    dq, _, _ = oracle.sequence_backward(qb, kb, vb, gb, c, causal)
+    rows = [0, 3, 22, 11]
+    np.testing.assert_allclose(oracle.sequence_dq_rows(qb, kb, vb, gb, rows, c, causal), dq[rows],
+                               atol=1e-13)

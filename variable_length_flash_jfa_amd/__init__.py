@@ -1,0 +1,22 @@
+"""MI355X (gfx950) Jagged Flash Attention.
+
+Thin Python binding over the C ABI of ``_lib/libjfa.so`` (declared in
+``include/jfa.h``).  Every step of the computation runs in the library's HIP
+kernels; this package only marshals torch tensors, streams and workspaces.
+"""
+from ._binding import (  # noqa: F401
+    JfaError,
+    SCHED_SORTED_ZIGZAG,
+    SCHED_IDENTITY,
+    SCHED_DYNAMIC,
+    fwd,
+    bwd,
+    fwd_workspace_size,
+    bwd_workspace_size,
+    set_schedule,
+    get_schedule,
+    library,
+    library_path,
+    version,
+)
+from .autograd import jagged_attention  # noqa: F401

@@ -1,0 +1,187 @@
+"""ctypes binding of libjfa.so: argument marshalling only.
+
+Names follow the C ABI (``jfa_fwd`` -> ``fwd``, ``jfa_bwd`` -> ``bwd``).  Tensors
+must live on the current HIP device; work is enqueued on torch's current stream.
+The library must have been built (``__graft_entry__.build()``); there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "_lib", "libjfa.so")
+
+SCHED_SORTED_ZIGZAG = 0
+SCHED_IDENTITY = 1
+SCHED_DYNAMIC = 2
+
+_STATUS = {
+    0: "JFA_OK",
+    1: "JFA_ERR_INVALID_ARGUMENT",
+    2: "JFA_ERR_UNSUPPORTED",
+    3: "JFA_ERR_WORKSPACE_TOO_SMALL",
+    4: "JFA_ERR_HIP",
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class JfaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def library() -> ctypes.CDLL:
+    """Loads libjfa.so (once).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise RuntimeError(
+                    f"{_LIB_PATH} is missing: build the HIP library first "
+                    "(python -c 'import __graft_entry__ as g; g.build()')")
+            lib = ctypes.CDLL(_LIB_PATH)
+            i64, i32, vp, f32, sz = (ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_float, ctypes.c_size_t)
+            lib.jfa_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32]
+            lib.jfa_fwd_workspace_size.restype = sz
+            lib.jfa_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32]
+            lib.jfa_bwd_workspace_size.restype = sz
+            lib.jfa_fwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, i64, i32, i32, f32,
+                                    vp, vp, vp, sz, vp]
+            lib.jfa_fwd.restype = i32
+            lib.jfa_bwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, i64, i32, i32, f32,
+                                    vp, vp, vp, vp, vp, vp, vp, sz, vp]
+            lib.jfa_bwd.restype = i32
+            lib.jfa_last_error.argtypes = []
+            lib.jfa_last_error.restype = ctypes.c_char_p
+            lib.jfa_version.argtypes = []
+            lib.jfa_version.restype = ctypes.c_char_p
+            lib.jfa_set_schedule.argtypes = [i32]
+            lib.jfa_set_schedule.restype = i32
+            lib.jfa_get_schedule.argtypes = []
+            lib.jfa_get_schedule.restype = i32
+            _lib = lib
+        return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = library().jfa_last_error().decode(errors="replace")
+        raise JfaError(status, msg)
+
+
+def version() -> str:
+    return library().jfa_version().decode()
+
+
+def set_schedule(schedule: int) -> None:
+    _check(library().jfa_set_schedule(int(schedule)))
+
+
+def get_schedule() -> int:
+    return int(library().jfa_get_schedule())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _sizes(q, k, offsets, broadcast_q):
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q, k, v must be [rows, heads, head_dim]")
+    batch = offsets.numel() - 1
+    heads, head_dim = k.shape[1], k.shape[2]
+    q_len = q.shape[0] if broadcast_q else 0
+    total_kv = k.shape[0]
+    rows = batch * q_len if broadcast_q else total_kv
+    return batch, heads, head_dim, q_len, total_kv, rows
+
+
+def _validate(q, k, v, offsets):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+    if offsets.dtype not in (torch.int32, torch.int64) or not offsets.is_cuda:
+        raise TypeError("offsets must be an int32/int64 GPU tensor")
+    if not offsets.is_contiguous():
+        raise ValueError("offsets must be contiguous")
+
+
+def fwd_workspace_size(batch, heads, head_dim, q_len, total_kv, broadcast_q, causal) -> int:
+    return int(library().jfa_fwd_workspace_size(batch, heads, head_dim, q_len, total_kv,
+                                                 int(broadcast_q), int(causal)))
+
+
+def bwd_workspace_size(batch, heads, head_dim, q_len, total_kv, broadcast_q, causal) -> int:
+    return int(library().jfa_bwd_workspace_size(batch, heads, head_dim, q_len, total_kv,
+                                                int(broadcast_q), int(causal)))
+
+
+def fwd(q, k, v, offsets, *, broadcast_q: bool, causal: bool = False, scale=None,
+        out=None, lse=None, workspace=None):
+    """O, LSE = jfa_fwd(...).  O: [rows, H, D] bf16; LSE: [H, rows] fp32."""
+    _validate(q, k, v, offsets)
+    batch, heads, head_dim, q_len, total_kv, rows = _sizes(q, k, offsets, broadcast_q)
+    scale = 1.0 / math.sqrt(head_dim) if scale is None else float(scale)
+    dev = q.device
+    if out is None:
+        out = torch.empty((rows, heads, head_dim), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((heads, rows), dtype=torch.float32, device=dev)
+    need = fwd_workspace_size(batch, heads, head_dim, q_len, total_kv, broadcast_q, causal)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = library().jfa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(offsets),
+                           int(offsets.dtype == torch.int64), batch, heads, head_dim, q_len,
+                           total_kv, int(broadcast_q), int(causal), scale, _ptr(out), _ptr(lse),
+                           _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st)
+    return out, lse
+
+
+def bwd(q, k, v, offsets, o, lse, d_o, *, broadcast_q: bool, causal: bool = False, scale=None,
+        dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV = jfa_bwd(...) (bf16, shapes of q, k, v)."""
+    _validate(q, k, v, offsets)
+    batch, heads, head_dim, q_len, total_kv, rows = _sizes(q, k, offsets, broadcast_q)
+    for name, t, dt in (("o", o, torch.bfloat16), ("d_o", d_o, torch.bfloat16), ("lse", lse, torch.float32)):
+        if t.dtype != dt or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous {dt} GPU tensor")
+    if o.shape != (rows, heads, head_dim) or d_o.shape != o.shape or lse.shape != (heads, rows):
+        raise ValueError("o / d_o / lse shapes do not match the problem")
+    scale = 1.0 / math.sqrt(head_dim) if scale is None else float(scale)
+    dev = q.device
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = bwd_workspace_size(batch, heads, head_dim, q_len, total_kv, broadcast_q, causal)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = library().jfa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(offsets),
+                           int(offsets.dtype == torch.int64), batch, heads, head_dim, q_len,
+                           total_kv, int(broadcast_q), int(causal), scale, _ptr(o), _ptr(lse),
+                           _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                           workspace.numel(), _stream(dev))
+    _check(st)
+    return dq, dk, dv

@@ -1,0 +1,272 @@
+// C ABI of libjfa.so: argument checks, workspace sizing and carving, launches.
+// The declarations and their documentation are in include/jfa.h.
+#include "jfa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "jfa_internal.h"
+
+namespace {
+
+thread_local char g_error[512] = "";
+std::atomic<int> g_schedule{JFA_SCHED_SORTED_ZIGZAG};
+
+jfa_status_t fail(jfa_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_error, sizeof(g_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+jfa_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(JFA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Sizes {
+  bool ok;
+  const char* why;
+  jfa_status_t st;
+};
+
+Sizes check_sizes(int64_t batch, int64_t heads, int64_t head_dim, int64_t q_len, int64_t total_kv,
+                  int broadcast_q, int causal) {
+  if (head_dim != 64 && head_dim != 128)
+    return {false, "head_dim must be 64 or 128", JFA_ERR_UNSUPPORTED};
+  if (broadcast_q && causal)
+    return {false, "causal masking is defined for self-attention only (broadcast_q=1, causal=1)",
+            JFA_ERR_UNSUPPORTED};
+  if (batch < 0 || heads < 1 || q_len < 0 || total_kv < 0)
+    return {false, "sizes must be non-negative and num_heads >= 1", JFA_ERR_INVALID_ARGUMENT};
+  if (broadcast_q && q_len < 1)
+    return {false, "broadcast mode needs q_len >= 1", JFA_ERR_INVALID_ARGUMENT};
+  if (!broadcast_q && q_len != 0)
+    return {false, "self mode needs q_len == 0 (queries come from the packed sequences)",
+            JFA_ERR_INVALID_ARGUMENT};
+  // 32-bit limits of the tile indices used on the device
+  const int64_t lim = (int64_t)1 << 30;
+  const int64_t rows = broadcast_q ? batch * q_len : total_kv;
+  if (batch >= lim || total_kv >= lim || q_len >= lim || heads >= 4096 || rows >= ((int64_t)1 << 36))
+    return {false, "problem too large for this library build", JFA_ERR_UNSUPPORTED};
+  if ((total_kv / jfa::kBwdBN + batch) * heads >= lim)
+    return {false, "too many tiles for this library build", JFA_ERR_UNSUPPORTED};
+  return {true, "", JFA_OK};
+}
+
+jfa::Problem make_problem(const void* q, const void* k, const void* v, const void* offsets,
+                          int off64, int64_t batch, int64_t heads, int64_t head_dim, int64_t q_len,
+                          int64_t total_kv, int broadcast_q, int causal, float scale) {
+  jfa::Problem p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.offsets = offsets;
+  p.off64 = off64 ? 1 : 0;
+  p.batch = (int)batch;
+  p.heads = (int)heads;
+  p.head_dim = (int)head_dim;
+  p.q_len = (int)q_len;
+  p.total_kv = total_kv;
+  p.rows = broadcast_q ? batch * q_len : total_kv;
+  p.broadcast = broadcast_q ? 1 : 0;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  return p;
+}
+
+size_t fwd_ws_bytes(const jfa::Problem& p) {
+  return kAlign + align_up(64) + align_up((size_t)jfa::fwd_max_items(p) * sizeof(int2));
+}
+
+size_t bwd_ws_bytes(const jfa::Problem& p) {
+  const int64_t q_rows = p.broadcast ? (int64_t)p.q_len * jfa::kDqStripes : p.total_kv;
+  return kAlign + align_up(64) + align_up((size_t)jfa::bwd_max_items(p) * sizeof(int2)) +
+         align_up((size_t)p.heads * p.rows * sizeof(float)) +
+         align_up((size_t)q_rows * p.heads * p.head_dim * sizeof(float));
+}
+
+bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) != 0; }
+
+char* carve(char*& cur, size_t bytes) {
+  char* r = cur;
+  cur += align_up(bytes);
+  return r;
+}
+
+}  // namespace
+
+namespace jfa {
+
+int device_cu_count() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  cache[dev] = cus;
+  return cus;
+}
+
+int persistent_grid(const void* kernel, int block_threads, int64_t max_tiles) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  int per_cu = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto key = std::make_pair(kernel, dev);
+    auto it = cache.find(key);
+    if (it != cache.end()) {
+      per_cu = it->second;
+    } else {
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block_threads, 0) != hipSuccess ||
+          per_cu < 1)
+        per_cu = 1;
+      cache[key] = per_cu;
+    }
+  }
+  int64_t grid = (int64_t)device_cu_count() * per_cu;
+  const int64_t cap = (max_tiles + 7) / 8 * 8;
+  if (grid > cap) grid = cap;
+  grid = grid / 8 * 8;
+  if (grid < 8) grid = 8;
+  return (int)grid;
+}
+
+}  // namespace jfa
+
+extern "C" {
+
+jfa_status_t jfa_set_schedule(int schedule) {
+  if (schedule < JFA_SCHED_SORTED_ZIGZAG || schedule > JFA_SCHED_DYNAMIC)
+    return fail(JFA_ERR_INVALID_ARGUMENT, "unknown schedule %d", schedule);
+  g_schedule.store(schedule);
+  return JFA_OK;
+}
+
+int jfa_get_schedule(void) { return g_schedule.load(); }
+
+size_t jfa_fwd_workspace_size(int64_t batch, int64_t num_heads, int64_t head_dim, int64_t q_len,
+                              int64_t total_kv, int broadcast_q, int causal) {
+  if (!check_sizes(batch, num_heads, head_dim, q_len, total_kv, broadcast_q, causal).ok) return 0;
+  const jfa::Problem p = make_problem(nullptr, nullptr, nullptr, nullptr, 0, batch, num_heads, head_dim,
+                                      q_len, total_kv, broadcast_q, causal, 1.f);
+  return fwd_ws_bytes(p);
+}
+
+size_t jfa_bwd_workspace_size(int64_t batch, int64_t num_heads, int64_t head_dim, int64_t q_len,
+                              int64_t total_kv, int broadcast_q, int causal) {
+  if (!check_sizes(batch, num_heads, head_dim, q_len, total_kv, broadcast_q, causal).ok) return 0;
+  const jfa::Problem p = make_problem(nullptr, nullptr, nullptr, nullptr, 0, batch, num_heads, head_dim,
+                                      q_len, total_kv, broadcast_q, causal, 1.f);
+  return bwd_ws_bytes(p);
+}
+
+jfa_status_t jfa_fwd(const void* q, const void* k, const void* v, const void* offsets,
+                     int offsets_is_int64, int64_t batch, int64_t num_heads, int64_t head_dim,
+                     int64_t q_len, int64_t total_kv, int broadcast_q, int causal, float softmax_scale,
+                     void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  g_error[0] = '\0';
+  const Sizes sz = check_sizes(batch, num_heads, head_dim, q_len, total_kv, broadcast_q, causal);
+  if (!sz.ok) return fail(sz.st, "jfa_fwd: %s", sz.why);
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
+    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_fwd: softmax_scale must be finite and > 0");
+  const jfa::Problem p = make_problem(q, k, v, offsets, offsets_is_int64, batch, num_heads, head_dim,
+                                      q_len, total_kv, broadcast_q, causal, softmax_scale);
+  if (p.batch == 0 || p.rows == 0) return JFA_OK;
+  if (!q || !offsets || !o || !lse || !workspace || (p.total_kv > 0 && (!k || !v)))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_fwd: null pointer argument");
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(workspace) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3) ||
+      (reinterpret_cast<uintptr_t>(offsets) & (offsets_is_int64 ? 7 : 3)))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_fwd: tensors must be 16-byte aligned");
+  const size_t need = fwd_ws_bytes(p);
+  if (workspace_bytes < need)
+    return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "jfa_fwd: workspace of %zu bytes, need %zu",
+                workspace_bytes, need);
+  char* cur = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(workspace)));
+  jfa::Plan plan;
+  plan.meta = reinterpret_cast<int*>(carve(cur, 64));
+  plan.max_items = jfa::fwd_max_items(p);
+  plan.items = reinterpret_cast<int2*>(carve(cur, plan.max_items * sizeof(int2)));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int sched = g_schedule.load();
+  hipError_t e = jfa::launch_plan_fwd(p, plan, sched, s);
+  if (e != hipSuccess) return hip_fail(e, "jfa_fwd: plan launch");
+  e = jfa::launch_fwd(p, plan, sched, o, lse, s);
+  if (e != hipSuccess) return hip_fail(e, "jfa_fwd: kernel launch");
+  return JFA_OK;
+}
+
+jfa_status_t jfa_bwd(const void* q, const void* k, const void* v, const void* offsets,
+                     int offsets_is_int64, int64_t batch, int64_t num_heads, int64_t head_dim,
+                     int64_t q_len, int64_t total_kv, int broadcast_q, int causal, float softmax_scale,
+                     const void* o, const float* lse, const void* d_o, void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  g_error[0] = '\0';
+  const Sizes sz = check_sizes(batch, num_heads, head_dim, q_len, total_kv, broadcast_q, causal);
+  if (!sz.ok) return fail(sz.st, "jfa_bwd: %s", sz.why);
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
+    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_bwd: softmax_scale must be finite and > 0");
+  const jfa::Problem p = make_problem(q, k, v, offsets, offsets_is_int64, batch, num_heads, head_dim,
+                                      q_len, total_kv, broadcast_q, causal, softmax_scale);
+  if (p.batch == 0 || p.rows == 0) return JFA_OK;
+  if (!q || !offsets || !o || !lse || !d_o || !dq || !workspace ||
+      (p.total_kv > 0 && (!k || !v || !dk || !dv)))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_bwd: null pointer argument");
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(d_o) ||
+      misaligned(dq) || misaligned(dk) || misaligned(dv) || misaligned(workspace) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3) ||
+      (reinterpret_cast<uintptr_t>(offsets) & (offsets_is_int64 ? 7 : 3)))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_bwd: tensors must be 16-byte aligned");
+  const size_t need = bwd_ws_bytes(p);
+  if (workspace_bytes < need)
+    return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "jfa_bwd: workspace of %zu bytes, need %zu",
+                workspace_bytes, need);
+  char* cur = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(workspace)));
+  jfa::Plan plan;
+  plan.meta = reinterpret_cast<int*>(carve(cur, 64));
+  plan.max_items = jfa::bwd_max_items(p);
+  plan.items = reinterpret_cast<int2*>(carve(cur, plan.max_items * sizeof(int2)));
+  float* delta = reinterpret_cast<float*>(carve(cur, (size_t)p.heads * p.rows * sizeof(float)));
+  const int64_t q_rows = p.broadcast ? (int64_t)p.q_len * jfa::kDqStripes : p.total_kv;
+  const int64_t acc_elems = q_rows * p.heads * p.head_dim;
+  float* dq_acc = reinterpret_cast<float*>(carve(cur, (size_t)acc_elems * sizeof(float)));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int sched = g_schedule.load();
+  hipError_t e = jfa::launch_bwd_pre(p, o, d_o, delta, dq_acc, acc_elems, s);
+  if (e != hipSuccess) return hip_fail(e, "jfa_bwd: delta launch");
+  if (p.total_kv > 0) {
+    e = jfa::launch_plan_bwd(p, plan, sched, s);
+    if (e != hipSuccess) return hip_fail(e, "jfa_bwd: plan launch");
+    e = jfa::launch_bwd(p, plan, sched, lse, d_o, delta, dq_acc, dk, dv, s);
+    if (e != hipSuccess) return hip_fail(e, "jfa_bwd: kernel launch");
+  }
+  e = jfa::launch_dq_finalize(p, dq_acc, dq, s);
+  if (e != hipSuccess) return hip_fail(e, "jfa_bwd: dq finalize launch");
+  return JFA_OK;
+}
+
+const char* jfa_last_error(void) { return g_error; }
+
+const char* jfa_version(void) { return "jfa 0.1 gfx950"; }
+
+}  // extern "C"

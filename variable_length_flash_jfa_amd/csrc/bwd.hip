@@ -1,0 +1,493 @@
+// Jagged Flash Attention backward for gfx950.
+//
+// Launch sequence of one backward call:
+//   1. bwd_pre_kernel: delta_i = sum_d dO_i . O_i per (row, head) -- the row-wise
+//      sum the backward needs ("Meta's TLX Block Attention Beats Flash Attention
+//      v2 by 2.3x on Blackwell GPUs", section "One Constraint, Five
+//      Eliminations", the Di preprocessing) -- and zeroing of the fp32 dQ
+//      accumulator;
+//   2. the backward tile planner (plan.hip);
+//   3. bwd_kernel: persistent workgroups over valid (sequence, 128-key block, head)
+//      tiles.  Four waves own 32 keys each, hold dK^T / dV^T accumulators and
+//      their V fragment in registers, and stream the tile's query rows in blocks
+//      of 32 straight from HBM into double-buffered LDS (gfx950 direct LDS loads).  Per query block every wave recomputes
+//      P from the saved LSE and forms dV^T += dO^T P, dP = dO V^T,
+//      dS = P (dP - delta), dK^T += Q^T dS on v_mfma_f32_32x32x16_bf16;
+//   4. the dQ contribution of the whole 128-key tile is reduced in LDS first: the
+//      waves publish dS^T to LDS and each computes a 32-column slice of
+//      dQ_block = dS K over all 128 keys, so a tile adds one fp32 partial per query
+//      row into HBM instead of one per wave.  In broadcast-Q mode every sequence
+//      adds into the same dQ ("Meta's TLX attention kernel outpaces
+//      FlashAttention-4 on B200", section "GEM's sequences do not fit a fixed
+//      grid"), so the accumulator is striped per XCD (8 fp32 copies) to keep the
+//      reduce-adds inside each XCD's L2 (the pages stage this reduction through a
+//      double-buffered on-chip pipeline: section "Five changes unlocked the
+//      gains", item 3);
+//   5. dq_finalize_kernel: sum of the stripes, times the softmax scale -> bf16.
+#include "jfa_device.h"
+#include "jfa_internal.h"
+
+namespace jfa {
+namespace {
+
+// ---------------------------------------------------------------------------
+// 1. delta = rowsum(dO * O) and dQ accumulator zeroing
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o,
+                                                       const bf16* __restrict__ d_o,
+                                                       float* __restrict__ delta, int64_t rows,
+                                                       int heads, float* __restrict__ dq_acc,
+                                                       int64_t acc_vec4) {
+  constexpr int TPR = D / 8;                 // threads per (row, head)
+  const int64_t pair = ((int64_t)blockIdx.x * 256 + threadIdx.x) / TPR;
+  const int part = threadIdx.x % TPR;
+  const int64_t npairs = rows * heads;
+  float s = 0.f;
+  if (pair < npairs) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + pair * D + part * 8);
+    const bf16x8 b = *reinterpret_cast<const bf16x8*>(d_o + pair * D + part * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += (float)a[e] * (float)b[e];
+  }
+#pragma unroll
+  for (int m = TPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+  if (pair < npairs && part == 0) {
+    const int64_t row = pair / heads;
+    const int h = (int)(pair % heads);
+    delta[(int64_t)h * rows + row] = s;
+  }
+  // grid-stride zero fill of the dQ accumulator
+  const int64_t nthreads = (int64_t)gridDim.x * 256;
+  float4* acc = reinterpret_cast<float4*>(dq_acc);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < acc_vec4; i += nthreads)
+    acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// ---------------------------------------------------------------------------
+// 3./4. tile kernel
+// ---------------------------------------------------------------------------
+struct BwdArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const bf16* d_o;
+  const float* lse;
+  const float* delta;
+  const void* offsets;
+  int off64;
+  int heads;
+  int q_len;
+  int64_t rows;
+  float scale_log2;
+  float scale;
+  float* dq_acc;
+  bf16* dk;
+  bf16* dv;
+  const int2* items;
+  int* meta;
+  int sched;
+};
+
+template <int D, bool BCAST, bool CAUSAL>
+struct BwdKernel {
+  static constexpr int BN = kBwdBN;     // keys per tile (4 waves x 32)
+  static constexpr int BQ = kBwdBQ;     // query rows per block
+  static constexpr int NT = 64 * kBwdWaves;
+  static constexpr int CH = D / 8;
+  static constexpr int DT = D / 32;
+  static constexpr int KS = D / 16;
+  static constexpr int KT_BYTES = BN * D * 2;
+  static constexpr int QT_BYTES = BQ * D * 2;
+  static constexpr int DS_BYTES = BN * BQ * 2;
+  // LDS map
+  static constexpr int OFF_K = 0;
+  static constexpr int OFF_Q = OFF_K + KT_BYTES;              // 2 buffers
+  static constexpr int OFF_DO = OFF_Q + 2 * QT_BYTES;         // 2 buffers
+  static constexpr int OFF_DS = OFF_DO + 2 * QT_BYTES;
+  static constexpr int OFF_ROW = OFF_DS + DS_BYTES;           // [2][lse, delta][64] fp32
+  static constexpr int SMEM = OFF_ROW + 2 * 2 * 64 * 4;
+  static_assert((BQ * D * 2 / 1024) % kBwdWaves == 0, "a query block must split evenly over the waves");
+
+  BwdArgs a;
+  char* smem;
+  int lane, wave, c32, hf;
+  int64_t rs;
+
+  // per tile
+  int64_t kv0, n, j0;
+  int h, q_rows;
+  int64_t grow0;        // first dO / LSE row of the sequence
+  bf16x8 vf[KS];
+  f32x16 dvt[DT], dkt[DT];
+
+  __device__ BwdKernel(const BwdArgs& args, char* sm) : a(args), smem(sm) {
+    lane = threadIdx.x & 63;
+    wave = threadIdx.x >> 6;
+    c32 = lane & 31;
+    hf = lane >> 5;
+    rs = (int64_t)a.heads * D;
+  }
+
+  __device__ __forceinline__ char* qbuf(int b) { return smem + OFF_Q + b * QT_BYTES; }
+  __device__ __forceinline__ char* gbuf(int b) { return smem + OFF_DO + b * QT_BYTES; }
+  __device__ __forceinline__ float* rowbuf(int b) {
+    return reinterpret_cast<float*>(smem + OFF_ROW) + b * 2 * 64;
+  }
+
+  // Issues the direct LDS loads of query block [qi0, qi0 + BQ): Q and dO rows, and
+  // the LSE / delta values of those rows.  Rows past the end read as zeros; the
+  // masked path gives them zero weight.
+  __device__ __forceinline__ void load_qblock(int64_t qi0, int buf) {
+    const int64_t rows = min((int64_t)q_rows - qi0, (int64_t)BQ);
+    const uint32_t row_bytes = (uint32_t)(rs * 2);
+    const uint32_t bytes = (uint32_t)(rows * rs * 2);
+    const bf16* qsrc = a.q + ((BCAST ? 0 : kv0) + qi0) * rs + (int64_t)h * D;
+    const bf16* gsrc = a.d_o + (grow0 + qi0) * rs + (int64_t)h * D;
+    lds_load_tile<D, kBwdWaves>(qbuf(buf), BQ, wave, lane, make_rsrc(qsrc, bytes), row_bytes);
+    lds_load_tile<D, kBwdWaves>(gbuf(buf), BQ, wave, lane, make_rsrc(gsrc, bytes), row_bytes);
+    if (wave == kBwdWaves - 1) {
+      const int64_t r0 = (int64_t)h * a.rows + grow0 + qi0;
+      const uint32_t rb = (uint32_t)(rows * 4);
+      lds_load4(make_rsrc(a.lse + r0, rb), (uint32_t)lane * 4u, reinterpret_cast<char*>(rowbuf(buf)));
+      lds_load4(make_rsrc(a.delta + r0, rb), (uint32_t)lane * 4u, reinterpret_cast<char*>(rowbuf(buf) + 64));
+    }
+  }
+
+  template <bool MASKED>
+  __device__ __forceinline__ void qblock(int buf, int64_t qi0) {
+    const char* kt = smem + OFF_K;
+    const char* qt = qbuf(buf);
+    const char* gt = gbuf(buf);
+    const float* lse2 = rowbuf(buf);   // natural-log LSE
+    const float* dl = rowbuf(buf) + 64;
+    char* dst = smem + OFF_DS;
+
+    // S = Q K^T and dP = dO V^T for this wave's 32 keys (C: m = query i, n = key j)
+    // Operands are read one step ahead of their MFMAs; the scheduling fences keep
+    // the compiler from hoisting every read of the unrolled loop (which would push
+    // the live registers past the 256 that two waves per SIMD allow).
+    f32x16 s = zero16(), dp = zero16();
+    bf16x8 qa = lds_read8(qt, tile_off<D>(c32, 8 * hf));
+    bf16x8 kb = lds_read8(kt, tile_off<D>(32 * wave + c32, 8 * hf));
+    bf16x8 ga = lds_read8(gt, tile_off<D>(c32, 8 * hf));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 qa_n = qa, kb_n = kb, ga_n = ga;
+      if (ks + 1 < KS) {
+        qa_n = lds_read8(qt, tile_off<D>(c32, 16 * (ks + 1) + 8 * hf));
+        kb_n = lds_read8(kt, tile_off<D>(32 * wave + c32, 16 * (ks + 1) + 8 * hf));
+        ga_n = lds_read8(gt, tile_off<D>(c32, 16 * (ks + 1) + 8 * hf));
+      }
+      s = mfma32(qa, kb, s);
+      dp = mfma32(ga, vf[ks], dp);
+      qa = qa_n;
+      kb = kb_n;
+      ga = ga_n;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // P = exp2(S c log2e - LSE log2e); dS = P (dP - delta)
+    bf16x8 pb[2], sb[2];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + 8 * q4 + 4 * hf);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + 8 * q4 + 4 * hf);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * q4 + e;
+        float p = fast_exp2(fmaf(s[r], a.scale_log2, -l4[e] * kLog2e));
+        if constexpr (MASKED) {
+          // rows past the query end, keys past the sequence end, and (causal) keys
+          // after the query get zero probability
+          const int64_t ipos = qi0 + 8 * q4 + 4 * hf + e;
+          const int64_t jpos = j0 + 32 * wave + c32;
+          bool vis = jpos < n && ipos < q_rows;
+          if constexpr (CAUSAL) vis = vis && jpos <= ipos;
+          if (!vis) p = 0.f;
+        }
+        const float ds = p * (dp[r] - d4[e]);
+        pb[r >> 3][r & 7] = (bf16)p;
+        sb[r >> 3][r & 7] = (bf16)ds;
+      }
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS (C: m = d, n = key j)
+    {
+      bf16x8 g_op = lds_operand_tr<D>(gt, 4 * hf, 4 * hf + 8, 0, lane);
+      bf16x8 q_op = lds_operand_tr<D>(qt, 4 * hf, 4 * hf + 8, 0, lane);
+#pragma unroll
+      for (int step = 0; step < 2 * DT; ++step) {
+        const int kc = step / DT, dt = step % DT;
+        bf16x8 g_n = g_op, q_n = q_op;
+        if (step + 1 < 2 * DT) {
+          const int kc1 = (step + 1) / DT, dt1 = (step + 1) % DT;
+          const int ib1 = 16 * kc1 + 4 * hf;
+          g_n = lds_operand_tr<D>(gt, ib1, ib1 + 8, 32 * dt1, lane);
+          q_n = lds_operand_tr<D>(qt, ib1, ib1 + 8, 32 * dt1, lane);
+        }
+        dvt[dt] = mfma32(g_op, pb[kc], dvt[dt]);
+        dkt[dt] = mfma32(q_op, sb[kc], dkt[dt]);
+        g_op = g_n;
+        q_op = q_n;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // publish dS^T [key][query] (bf16) once the previous block's dQ reads are done
+    __syncthreads();
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = sb[q4 >> 1][4 * (q4 & 1) + e];
+      *reinterpret_cast<bf16x4*>(dst + (32 * wave + c32) * (BQ * 2) + (8 * q4 + 4 * hf) * 2) = w;
+    }
+  }
+
+  // dQ_block[:, 32w .. 32w+31] = dS K over the tile's 128 keys, added to HBM.
+  __device__ __forceinline__ void dq_block(int64_t qi0) {
+    if (wave >= DT) return;
+    const char* kt = smem + OFF_K;
+    const char* dst = smem + OFF_DS;
+    f32x16 dq = zero16();
+    const int t = lane & 15;
+    const int col = ((lane >> 4) & 1) * 16 + 4 * (t & 3);
+    auto ds_op = [&](int k0) {
+      return cat(lds_read_tr(dst + (k0 + (t >> 2)) * (BQ * 2) + col * 2),
+                 lds_read_tr(dst + (k0 + 4 + (t >> 2)) * (BQ * 2) + col * 2));
+    };
+    bf16x8 sa = ds_op(8 * hf);
+    bf16x8 kb = lds_operand_tr<D>(kt, 8 * hf, 8 * hf + 4, 32 * wave, lane);
+#pragma unroll
+    for (int jb = 0; jb < BN; jb += 16) {
+      bf16x8 sa_n = sa, kb_n = kb;
+      if (jb + 16 < BN) {
+        const int k1 = jb + 16 + 8 * hf;
+        sa_n = ds_op(k1);
+        kb_n = lds_operand_tr<D>(kt, k1, k1 + 4, 32 * wave, lane);
+      }
+      dq = mfma32(sa, kb, dq);
+      sa = sa_n;
+      kb = kb_n;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int d = 32 * wave + c32;
+    const int64_t stripe_rows = BCAST ? (int64_t)(blockIdx.x & (kDqStripes - 1)) * a.q_len : 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t i = qi0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+      if (i < q_rows) {
+        const int64_t qrow = BCAST ? stripe_rows + i : kv0 + i;
+        unsafeAtomicAdd(a.dq_acc + (qrow * a.heads + h) * D + d, dq[r]);
+      }
+    }
+  }
+
+  template <bool MASKED>
+  __device__ __forceinline__ void run(int64_t qs, int64_t qe, int64_t q_last) {
+    for (int64_t qi0 = qs; qi0 < qe; qi0 += BQ) {
+      const int buf = (int)((qi0 / BQ) & 1);
+      if (qi0 + BQ < q_last) load_qblock(qi0 + BQ, buf ^ 1);   // one block ahead
+      qblock<MASKED>(buf, qi0);
+      wait_lds_loads();
+      __syncthreads();
+      dq_block(qi0);
+    }
+  }
+
+  __device__ __forceinline__ void tile(int b, int jblk, int head) {
+    h = head;
+    kv0 = load_offset(a.offsets, a.off64, b);
+    n = load_offset(a.offsets, a.off64, b + 1) - kv0;
+    j0 = (int64_t)jblk * BN;
+    q_rows = BCAST ? a.q_len : (int)n;
+    grow0 = BCAST ? (int64_t)b * a.q_len : kv0;
+
+    __syncthreads();   // previous tile's LDS readers are done
+    // K tile -> LDS (rows past the end read as zeros and are masked); this wave's
+    // V fragment -> registers
+    {
+      const int64_t rows = min(n - j0, (int64_t)BN);
+      lds_load_tile<D, kBwdWaves>(smem + OFF_K, BN, wave, lane,
+                                  make_rsrc(a.k + (kv0 + j0) * rs + (int64_t)h * D, (uint32_t)(rows * rs * 2)),
+                                  (uint32_t)(rs * 2));
+      const int64_t j = j0 + 32 * wave + c32;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        vf[ks] = j < n ? *reinterpret_cast<const bf16x8*>(a.v + (kv0 + j) * rs + (int64_t)h * D + 16 * ks + 8 * hf)
+                       : zero_bf16x8();
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      dvt[dt] = zero16();
+      dkt[dt] = zero16();
+    }
+    // query rows that can see this tile's keys
+    int64_t qs = 0;
+    if constexpr (CAUSAL) qs = (j0 / BQ) * BQ;
+    const int64_t q_last = q_rows;
+    if (qs < q_last) load_qblock(qs, (int)((qs / BQ) & 1));
+    wait_lds_loads();
+    __syncthreads();
+    // Peeled loops: query blocks that need a mask (causal diagonal, a partial K/V
+    // block at the sequence end, or a partial last query block) run apart from the
+    // branch-free bulk.
+    const bool kv_tail = j0 + BN > n;
+    int64_t qm = qs;
+    if constexpr (CAUSAL) qm = min(q_last, ((j0 + BN - 1 + BQ - 1) / BQ) * BQ);
+    if (kv_tail) qm = q_last;
+    const int64_t qfull = max(qm, (q_last / BQ) * BQ);
+    run<true>(qs, qm, q_last);
+    run<false>(qm, qfull, q_last);
+    run<true>(qfull, q_last, q_last);
+
+    // dK = c dS^T Q and dV -> bf16
+    const int64_t j = j0 + 32 * wave + c32;
+    if (j < n) {
+      bf16* dkp = a.dk + (kv0 + j) * rs + (int64_t)h * D;
+      bf16* dvp = a.dv + (kv0 + j) * rs + (int64_t)h * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          bf16x4 kk, vv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kk[e] = (bf16)(dkt[dt][4 * q4 + e] * a.scale);
+            vv[e] = (bf16)(dvt[dt][4 * q4 + e]);
+          }
+          *reinterpret_cast<bf16x4*>(dkp + 32 * dt + 8 * q4 + 4 * hf) = kk;
+          *reinterpret_cast<bf16x4*>(dvp + 32 * dt + 8 * q4 + 4 * hf) = vv;
+        }
+      }
+    }
+  }
+};
+
+template <int D, bool BCAST, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_kernel(BwdArgs a) {
+  using K = BwdKernel<D, BCAST, CAUSAL>;
+  __shared__ __attribute__((aligned(16))) char smem[K::SMEM];
+  __shared__ int claimed;
+  K kern(a, smem);
+  const int num_wg = gridDim.x;
+  const int lwg = xcd_logical_wg(blockIdx.x, num_wg);
+  const int ntiles = a.meta[2];
+  for (int r = 0;; ++r) {
+    int idx;
+    if (a.sched == kDynamic) {
+      if (threadIdx.x == 0) claimed = atomicAdd(a.meta + 1, 1);
+      __syncthreads();
+      idx = claimed;
+      __syncthreads();
+    } else {
+      idx = r * num_wg + lwg;
+    }
+    if (idx >= ntiles) break;
+    const int item = idx / a.heads;
+    const int2 it = a.items[item];
+    kern.tile(it.x, it.y, idx - item * a.heads);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 5. dQ finalize
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restrict__ acc,
+                                                          bf16* __restrict__ dq, int64_t n_vec4,
+                                                          int64_t stripe_vec4, int stripes,
+                                                          float scale) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_vec4) return;
+  const float4* a4 = reinterpret_cast<const float4*>(acc);
+  float4 s = a4[i];
+  for (int k = 1; k < stripes; ++k) {
+    const float4 t = a4[i + k * stripe_vec4];
+    s.x += t.x;
+    s.y += t.y;
+    s.z += t.z;
+    s.w += t.w;
+  }
+  bf16x4 o;
+  o[0] = (bf16)(s.x * scale);
+  o[1] = (bf16)(s.y * scale);
+  o[2] = (bf16)(s.z * scale);
+  o[3] = (bf16)(s.w * scale);
+  reinterpret_cast<bf16x4*>(dq)[i] = o;
+}
+
+template <int D, bool BCAST, bool CAUSAL>
+hipError_t launch_bwd_inst(const BwdArgs& a, hipStream_t s, int64_t max_tiles) {
+  const void* fn = reinterpret_cast<const void*>(&bwd_kernel<D, BCAST, CAUSAL>);
+  const int grid = persistent_grid(fn, 256, max_tiles);
+  hipLaunchKernelGGL((bwd_kernel<D, BCAST, CAUSAL>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_d(const Problem& p, const BwdArgs& a, hipStream_t s) {
+  const int64_t max_tiles = bwd_max_items(p) * p.heads;
+  if (p.broadcast) return launch_bwd_inst<D, true, false>(a, s, max_tiles);
+  if (p.causal) return launch_bwd_inst<D, false, true>(a, s, max_tiles);
+  return launch_bwd_inst<D, false, false>(a, s, max_tiles);
+}
+
+}  // namespace
+
+int64_t bwd_max_items(const Problem& p) { return (p.total_kv + kBwdBN - 1) / kBwdBN + p.batch; }
+
+hipError_t launch_bwd_pre(const Problem& p, const void* o, const void* d_o, float* delta,
+                          float* dq_acc, int64_t dq_acc_elems, hipStream_t s) {
+  const int64_t pairs = p.rows * p.heads;
+  const int tpr = p.head_dim / 8;
+  int64_t blocks = (pairs * tpr + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  const int64_t vec4 = dq_acc_elems / 4;
+  if (p.head_dim == 128)
+    hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<const bf16*>(o), static_cast<const bf16*>(d_o), delta, p.rows,
+                       p.heads, dq_acc, vec4);
+  else
+    hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<const bf16*>(o), static_cast<const bf16*>(d_o), delta, p.rows,
+                       p.heads, dq_acc, vec4);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const Problem& p, const Plan& plan, int sched, const float* lse,
+                      const void* d_o, const float* delta, float* dq_acc, void* dk, void* dv,
+                      hipStream_t s) {
+  BwdArgs a;
+  a.q = static_cast<const bf16*>(p.q);
+  a.k = static_cast<const bf16*>(p.k);
+  a.v = static_cast<const bf16*>(p.v);
+  a.d_o = static_cast<const bf16*>(d_o);
+  a.lse = lse;
+  a.delta = delta;
+  a.offsets = p.offsets;
+  a.off64 = p.off64;
+  a.heads = p.heads;
+  a.q_len = p.q_len;
+  a.rows = p.rows;
+  a.scale_log2 = p.scale * kLog2e;
+  a.scale = p.scale;
+  a.dq_acc = dq_acc;
+  a.dk = static_cast<bf16*>(dk);
+  a.dv = static_cast<bf16*>(dv);
+  a.items = plan.items;
+  a.meta = plan.meta;
+  a.sched = sched;
+  return p.head_dim == 128 ? launch_bwd_d<128>(p, a, s) : launch_bwd_d<64>(p, a, s);
+}
+
+hipError_t launch_dq_finalize(const Problem& p, const float* dq_acc, void* dq, hipStream_t s) {
+  const int64_t q_rows = p.broadcast ? p.q_len : p.total_kv;
+  const int64_t n = q_rows * p.heads * p.head_dim;
+  const int64_t vec4 = n / 4;
+  const int64_t blocks = (vec4 + 255) / 256;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(dq_finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, s, dq_acc,
+                     static_cast<bf16*>(dq), vec4, vec4, p.broadcast ? kDqStripes : 1, p.scale);
+  return hipGetLastError();
+}
+
+}  // namespace jfa

@@ -1,0 +1,176 @@
+// Device-side building blocks shared by the gfx950 JFA kernels.
+//
+// Matrix products use the CDNA4 bf16 MFMA v_mfma_f32_32x32x16_bf16 (one 64-lane
+// wave computes a 32x32 fp32 tile from a 32x16 and a 16x32 bf16 operand).
+// Operand/accumulator lane layouts (checked on the device):
+//   A (M x K):  lane l holds A[m = l % 32][k = 8 * (l / 32) + e], e = 0..7
+//   B (K x N):  lane l holds B[k = 8 * (l / 32) + e][n = l % 32]
+//   C (M x N):  lane l, register r holds C[m = 8 * (r / 4) + 4 * (l / 32) + r % 4][n = l % 32]
+// Only the pairing of k between A and B matters for the product, so an operand
+// may carry any fixed permutation of k as long as the other carries the same.
+//
+// LDS tiles of bf16 rows (D elements) are stored row-major with 16-byte chunks
+// XOR-swizzled by row, so that both 16-byte row reads of 32 consecutive rows and
+// the gfx950 transposing read ds_read_b64_tr_b16 over groups of 4 rows are spread
+// over the LDS banks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jfa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegBig = -1.0e30f;   // finite "minus infinity" for running maxima
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  bf16x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = (bf16)0.f;
+  return z;
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Value of x held by lane (l ^ 32), combined with x by max / sum, via the gfx950
+// cross-half swap (lanes < 32 see the upper half in element 1, lanes >= 32 see
+// the lower half in element 0; the other element keeps the lane's own value).
+__device__ __forceinline__ float max_across_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_across_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- swizzled LDS tiles -----------------------------------------------------
+
+template <int D>
+__device__ __forceinline__ int swz_chunk(int row, int chunk) {
+  if constexpr (D == 128) {
+    return chunk ^ (((row & 3) << 2) | ((row >> 2) & 3));
+  } else {
+    return chunk ^ (((row & 3) << 1) | ((row >> 2) & 1));
+  }
+}
+
+// Byte offset of element (row, col) of a [rows][D] bf16 tile; col % 4 == 0 or the
+// 16-byte chunk start.
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int col) {
+  return row * (D * 2) + (swz_chunk<D>(row, col >> 3) << 4) + ((col & 7) << 1);
+}
+
+__device__ __forceinline__ bf16x8 lds_read8(const char* base, int off) {
+  return *reinterpret_cast<const bf16x8*>(base + off);
+}
+__device__ __forceinline__ void lds_write8(char* base, int off, bf16x8 v) {
+  *reinterpret_cast<bf16x8*>(base + off) = v;
+}
+
+// gfx950 transposing LDS read.  Within each group of 16 lanes, lane t supplies the
+// address of 4 consecutive bf16 and receives element (t % 4) of the chunk read by
+// lanes 4e + t / 4, e = 0..3.  With lane t pointing at row (k0 + t / 4), column
+// (n0 + 4 * (t % 4)) of a row-major matrix M, lane t receives M[k0 + e][n0 + t].
+__device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (__attribute__((address_space(3))) bf16x4*)(p));
+}
+
+// MFMA A/B operand (32 columns x 8 k) taken from a row-major [k][n] bf16 tile in
+// LDS through two transposing reads: lane l gets M[kb + e][nb + l % 32] for e = 0..3
+// from rows kb.., and M[kb2 + e][...] for e = 4..7 from rows kb2...
+template <int D>
+__device__ __forceinline__ bf16x8 lds_operand_tr(const char* tile, int kb, int kb2, int nb, int lane) {
+  const int t = lane & 15;
+  const int col = nb + ((lane >> 4) & 1) * 16 + 4 * (t & 3);
+  const bf16x4 lo = lds_read_tr(tile + tile_off<D>(kb + (t >> 2), col));
+  const bf16x4 hi = lds_read_tr(tile + tile_off<D>(kb2 + (t >> 2), col));
+  return cat(lo, hi);
+}
+
+// ---- direct HBM -> LDS loads ------------------------------------------------------
+
+// Raw buffer resource over `bytes` bytes from `base` (gfx9-family descriptor word 3).
+// Buffer loads past `bytes` return zeros, which zero-fills rows past a sequence end.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// One 16-byte (or 4-byte) chunk per lane from the buffer straight into LDS (gfx950
+// buffer_load_dwordx4 ... lds): the 64 lanes of a wave fill 64 consecutive chunks
+// starting at the wave-uniform LDS address `lds`.  Completion is tracked by the
+// vector-memory counter: call wait_lds_loads() before the barrier that publishes
+// the data.
+__device__ __forceinline__ void lds_load16(rsrc_t r, uint32_t voff, char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(rsrc_t r, uint32_t voff, char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
+}
+// s_waitcnt vmcnt(0): all of this wave's vector memory operations are complete.
+__device__ __forceinline__ void wait_lds_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Copies rows [0, nrows) of a [rows][D] bf16 tile (row r at byte r * row_bytes of
+// the buffer) into a swizzled LDS tile.  Each wave instruction covers 1024 bytes =
+// 1024 / (2 D) rows; instruction u goes to wave u % NW.  Lane i of an instruction
+// fills LDS chunk slot (i % CH) of its row, so it fetches logical chunk
+// swz_chunk(row, slot) (the swizzle is an XOR involution).
+template <int D, int NW>
+__device__ __forceinline__ void lds_load_tile(char* tile, int nrows, int wave, int lane, rsrc_t r,
+                                              uint32_t row_bytes) {
+  constexpr int CH = D / 8;
+  constexpr int RPI = 64 / CH;
+  const int per_wave = nrows / RPI / NW;
+#pragma unroll
+  for (int k = 0; k < per_wave; ++k) {
+    const int u = wave + k * NW;
+    const int row = u * RPI + lane / CH;
+    const int chunk = swz_chunk<D>(row, lane % CH);
+    lds_load16(r, (uint32_t)row * row_bytes + (uint32_t)chunk * 16u, tile + u * 1024);
+  }
+}
+
+// ---- offsets -------------------------------------------------------------------
+
+__device__ __forceinline__ int64_t load_offset(const void* offsets, int is64, int64_t i) {
+  return is64 ? reinterpret_cast<const int64_t*>(offsets)[i]
+              : (int64_t)reinterpret_cast<const int32_t*>(offsets)[i];
+}
+
+// ---- tile schedules ------------------------------------------------------------
+
+enum Schedule : int { kSortedZigzag = 0, kIdentity = 1, kDynamic = 2 };
+
+// Logical index of this persistent workgroup such that logical neighbours sit on
+// the same XCD (workgroups are dispatched to the 8 XCDs round-robin by blockIdx).
+__device__ __forceinline__ int xcd_logical_wg(int wg, int num_wg) {
+  const int per = num_wg >> 3;            // num_wg is a multiple of 8
+  return (wg & 7) * per + (wg >> 3);
+}
+
+}  // namespace jfa

@@ -1,0 +1,67 @@
+// Host-side interface between the C ABI layer and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace jfa {
+
+// Forward tile geometry.  A forward tile is (sequence, block of BM query rows, head);
+// every wave owns 32 query rows and K/V stream through LDS in blocks of kFwdBN keys.
+constexpr int kFwdBN = 64;
+// Backward tile geometry: a tile is (sequence, block of kBwdBN keys, head); four
+// waves own 32 keys each and stream the query rows in blocks of kBwdBQ.
+constexpr int kBwdBN = 128;
+constexpr int kBwdBQ = 32;
+constexpr int kBwdWaves = 4;
+// Broadcast-mode dQ accumulates into one fp32 stripe per XCD.
+constexpr int kDqStripes = 8;
+
+struct Problem {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* offsets;
+  int off64;
+  int batch;
+  int heads;
+  int head_dim;
+  int q_len;          // Lq in broadcast mode, 0 in self mode
+  int64_t total_kv;   // T
+  int64_t rows;       // output rows: batch * Lq or T
+  int broadcast;
+  int causal;
+  float scale;
+};
+
+// Plan written on the device: meta[0] = number of items, meta[1] = dynamic-schedule
+// counter, meta[2] = number of tiles.  items[i] = (sequence, block) pairs.
+struct Plan {
+  int* meta;
+  int2* items;
+  int64_t max_items;
+};
+
+int fwd_waves(const Problem& p);                 // waves per forward workgroup
+int64_t fwd_max_items(const Problem& p);         // capacity of the forward item list
+int64_t bwd_max_items(const Problem& p);         // capacity of the backward item list
+
+hipError_t launch_plan_fwd(const Problem& p, const Plan& plan, int sched, hipStream_t s);
+hipError_t launch_fwd(const Problem& p, const Plan& plan, int sched, void* o, float* lse,
+                      hipStream_t s);
+
+hipError_t launch_bwd_pre(const Problem& p, const void* o, const void* d_o, float* delta,
+                          float* dq_acc, int64_t dq_acc_elems, hipStream_t s);
+hipError_t launch_plan_bwd(const Problem& p, const Plan& plan, int sched, hipStream_t s);
+hipError_t launch_bwd(const Problem& p, const Plan& plan, int sched, const float* lse,
+                      const void* d_o, const float* delta, float* dq_acc, void* dk, void* dv,
+                      hipStream_t s);
+hipError_t launch_dq_finalize(const Problem& p, const float* dq_acc, void* dq, hipStream_t s);
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+// Persistent grid size for a kernel: CUs x resident workgroups, a multiple of 8.
+int persistent_grid(const void* kernel, int block_threads, int64_t max_tiles);
+
+}  // namespace jfa

@@ -1,0 +1,258 @@
+// Device-side tile planners.
+//
+// Forward: tiles are sorted by the number of K/V blocks they visit (descending)
+// so that the persistent forward kernel can deal them boustrophedon across its
+// workgroups ("Meta's TLX attention kernel outpaces FlashAttention-4 on B200",
+// section "Five changes unlocked the gains", item 1; "Optimizing Jagged Flash
+// Attention with TLX" reading note, section "Why both static and dynamic
+// balancing help").  The pages sort on the host; here one workgroup does a
+// counting sort on the device so that a call needs no device-to-host copy of the
+// offsets and no synchronisation.
+//
+// Backward: the list of valid (sequence, K/V block) pairs is precomputed from a
+// prefix sum of per-sequence block counts (reading note, same section; "TLX JFA"
+// note, section "Structural changes and layered opts", item 1), and the kernel
+// deals them round-robin.
+#include "jfa_device.h"
+#include "jfa_internal.h"
+
+namespace jfa {
+namespace {
+
+constexpr int kPlanThreads = 1024;
+constexpr int kKeys = 1024;   // sort buckets; larger costs share the last bucket
+
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) x = max(x, __shfl_xor(x, s));
+  return x;
+}
+
+// Exclusive scan over the 1024 threads of the block; *total receives the sum.
+__device__ int block_exclusive_scan(int x, int* wave_sums, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    const int y = __shfl_up(incl, s);
+    if (lane >= s) incl += y;
+  }
+  if (lane == 63) wave_sums[w] = incl;
+  __syncthreads();
+  if (w == 0) {
+    int v = lane < kPlanThreads / 64 ? wave_sums[lane] : 0;
+    int vi = v;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+      const int y = __shfl_up(vi, s);
+      if (lane >= s) vi += y;
+    }
+    if (lane < kPlanThreads / 64) wave_sums[lane] = vi - v;
+    if (lane == kPlanThreads / 64 - 1) wave_sums[kPlanThreads / 64] = vi;
+  }
+  __syncthreads();
+  const int r = wave_sums[w] + incl - x;
+  *total = wave_sums[kPlanThreads / 64];
+  __syncthreads();
+  return r;
+}
+
+// Wave-aggregated LDS atomic add of 1 to counters[key]: one atomic per distinct
+// key among the active lanes.  Returns the old value plus the lane's rank.
+__device__ __forceinline__ int aggregated_increment(int* counters, int key) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long pending = __ballot(1);
+  int result = 0;
+  while (pending) {
+    const int leader = __ffsll((long long)pending) - 1;
+    const int lk = __shfl(key, leader);
+    const unsigned long long same = __ballot(key == lk) & pending;
+    if (key == lk) {
+      const int rank = __popcll(same & ((1ull << lane) - 1ull));
+      int base = 0;
+      if (lane == leader) base = atomicAdd(&counters[lk], __popcll(same));
+      base = __shfl(base, leader);
+      result = base + rank;
+    }
+    pending &= ~same;
+  }
+  return result;
+}
+
+struct PlanFwdArgs {
+  const void* offsets;
+  int off64;
+  int batch;
+  int q_len;
+  int bm;          // query rows per tile
+  int broadcast;
+  int causal;
+  int heads;
+  int sched;
+  int2* items;
+  int* meta;
+};
+
+// Items: broadcast mode -> one item per sequence (its ceil(Lq / BM) x H tiles share
+// the cost); self mode -> one item per (sequence, query block).  Cost = number of
+// kFwdBN-key blocks the tile visits.
+__device__ __forceinline__ int fwd_items_of(const PlanFwdArgs& a, int64_t n) {
+  return a.broadcast ? 1 : (int)((n + a.bm - 1) / a.bm);
+}
+__device__ __forceinline__ int fwd_cost(const PlanFwdArgs& a, int64_t n, int m) {
+  int64_t kv = n;
+  if (a.causal) kv = min(n, (int64_t)(m + 1) * a.bm);
+  const int64_t c = (kv + kFwdBN - 1) / kFwdBN;
+  return (int)min(c, (int64_t)(kKeys - 1));
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_fwd_kernel(PlanFwdArgs a) {
+  __shared__ int wave_sums[kPlanThreads / 64 + 1];
+  __shared__ int hist[kKeys];
+  const int tid = threadIdx.x;
+  const int per = (a.batch + kPlanThreads - 1) / kPlanThreads;
+  const int b_begin = min(a.batch, tid * per);
+  const int b_end = min(a.batch, b_begin + per);
+
+  int count = 0;
+  for (int b = b_begin; b < b_end; ++b) {
+    const int64_t n = load_offset(a.offsets, a.off64, b + 1) - load_offset(a.offsets, a.off64, b);
+    count += fwd_items_of(a, n);
+  }
+  int total = 0;
+  const int base = block_exclusive_scan(count, wave_sums, &total);
+
+  if (a.sched == kIdentity) {
+    int pos = base;
+    for (int b = b_begin; b < b_end; ++b) {
+      const int64_t n = load_offset(a.offsets, a.off64, b + 1) - load_offset(a.offsets, a.off64, b);
+      const int mi = fwd_items_of(a, n);
+      for (int m = 0; m < mi; ++m) a.items[pos++] = make_int2(b, m);
+    }
+  } else {
+    for (int i = tid; i < kKeys; i += kPlanThreads) hist[i] = 0;
+    __syncthreads();
+    const int rounds = wave_max(count);
+    // pass 1: histogram of costs
+    {
+      int b = b_begin, m = 0;
+      int64_t n = 0;
+      int mi = 0;
+      for (int r = 0; r < rounds; ++r) {
+        if (r < count) {
+          while (m >= mi) {  // advance to the next sequence that has items
+            n = load_offset(a.offsets, a.off64, b + 1) - load_offset(a.offsets, a.off64, b);
+            mi = fwd_items_of(a, n);
+            m = 0;
+            if (mi == 0) ++b;
+          }
+          aggregated_increment(hist, fwd_cost(a, n, m));
+          if (++m >= mi) ++b;
+        }
+      }
+    }
+    __syncthreads();
+    // descending exclusive scan of the histogram: cursor[k] = #items with cost > k
+    {
+      const int k = kKeys - 1 - tid;
+      int tot = 0;
+      const int start = block_exclusive_scan(hist[k], wave_sums, &tot);
+      __syncthreads();
+      hist[k] = start;
+    }
+    __syncthreads();
+    // pass 2: scatter in cost order
+    {
+      int b = b_begin, m = 0;
+      int64_t n = 0;
+      int mi = 0;
+      for (int r = 0; r < rounds; ++r) {
+        if (r < count) {
+          while (m >= mi) {
+            n = load_offset(a.offsets, a.off64, b + 1) - load_offset(a.offsets, a.off64, b);
+            mi = fwd_items_of(a, n);
+            m = 0;
+            if (mi == 0) ++b;
+          }
+          const int pos = aggregated_increment(hist, fwd_cost(a, n, m));
+          a.items[pos] = make_int2(b, m);
+          if (++m >= mi) ++b;
+        }
+      }
+    }
+  }
+  if (tid == 0) {
+    const int per_item = a.broadcast ? ((a.q_len + a.bm - 1) / a.bm) * a.heads : a.heads;
+    a.meta[0] = total;
+    a.meta[1] = 0;
+    a.meta[2] = total * per_item;
+  }
+}
+
+struct PlanBwdArgs {
+  const void* offsets;
+  int off64;
+  int batch;
+  int heads;
+  int2* items;
+  int* meta;
+};
+
+// Valid (sequence, K/V block) pairs in natural order; tile t = (items[t / H], t % H).
+__global__ __launch_bounds__(kPlanThreads) void plan_bwd_kernel(PlanBwdArgs a) {
+  __shared__ int wave_sums[kPlanThreads / 64 + 1];
+  const int tid = threadIdx.x;
+  const int per = (a.batch + kPlanThreads - 1) / kPlanThreads;
+  const int b_begin = min(a.batch, tid * per);
+  const int b_end = min(a.batch, b_begin + per);
+  int count = 0;
+  for (int b = b_begin; b < b_end; ++b) {
+    const int64_t n = load_offset(a.offsets, a.off64, b + 1) - load_offset(a.offsets, a.off64, b);
+    count += (int)((n + kBwdBN - 1) / kBwdBN);
+  }
+  int total = 0;
+  int pos = block_exclusive_scan(count, wave_sums, &total);
+  for (int b = b_begin; b < b_end; ++b) {
+    const int64_t n = load_offset(a.offsets, a.off64, b + 1) - load_offset(a.offsets, a.off64, b);
+    const int nb = (int)((n + kBwdBN - 1) / kBwdBN);
+    for (int j = 0; j < nb; ++j) a.items[pos++] = make_int2(b, j);
+  }
+  if (tid == 0) {
+    a.meta[0] = total;
+    a.meta[1] = 0;
+    a.meta[2] = total * a.heads;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_plan_fwd(const Problem& p, const Plan& plan, int sched, hipStream_t s) {
+  PlanFwdArgs a;
+  a.offsets = p.offsets;
+  a.off64 = p.off64;
+  a.batch = p.batch;
+  a.q_len = p.q_len;
+  a.bm = 32 * fwd_waves(p);
+  a.broadcast = p.broadcast;
+  a.causal = p.causal;
+  a.heads = p.heads;
+  a.sched = sched;
+  a.items = plan.items;
+  a.meta = plan.meta;
+  hipLaunchKernelGGL(plan_fwd_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_bwd(const Problem& p, const Plan& plan, int /*sched*/, hipStream_t s) {
+  PlanBwdArgs a;
+  a.offsets = p.offsets;
+  a.off64 = p.off64;
+  a.batch = p.batch;
+  a.heads = p.heads;
+  a.items = plan.items;
+  a.meta = plan.meta;
+  hipLaunchKernelGGL(plan_bwd_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace jfa

@@ -95,30 +95,56 @@ def normal_bf16(rng: np.random.Generator, shape) -> torch.Tensor:
     return out.view(*shape)
 
 
+def normal_bf16_device(gen: torch.Generator, shape, device) -> torch.Tensor:
+    """float32 N(0,1) draws from a seeded device generator, rounded to bf16 (RNE)."""
+    return torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+
 def make_case(lengths, *, heads, head_dim, broadcast_q, causal=False, q_len=0, seed=0,
-              offsets_dtype="int64", with_grad=True, rng=None):
-    """Inputs for explicit sequence lengths.  Returns a dict of CPU tensors."""
-    rng = rng if rng is not None else np.random.default_rng(seed)
+              offsets_dtype="int64", with_grad=True, rng=None, device=None):
+    """Inputs for explicit sequence lengths.
+
+    With device=None the values come from numpy (``rng`` or default_rng(seed)) and
+    the tensors are on the CPU.  With a device, the values come from a torch
+    generator on that device seeded with ``seed`` (fast at full size) and the
+    tensors live there; offsets are always built from the lengths on the host.
+    """
     lengths = np.asarray(lengths, dtype=np.int64)
     total = int(lengths.sum())
     rows = len(lengths) * q_len if broadcast_q else total
-    q = normal_bf16(rng, (q_len if broadcast_q else total, heads, head_dim))
-    k = normal_bf16(rng, (total, heads, head_dim))
-    v = normal_bf16(rng, (total, heads, head_dim))
-    g = normal_bf16(rng, (rows, heads, head_dim)) if with_grad else None
-    return dict(q=q, k=k, v=v, g=g, offsets=offsets_from_lengths(lengths, offsets_dtype),
+    shapes = [(q_len if broadcast_q else total, heads, head_dim), (total, heads, head_dim),
+              (total, heads, head_dim), (rows, heads, head_dim)]
+    if device is None:
+        rng = rng if rng is not None else np.random.default_rng(seed)
+        draw = lambda shp: normal_bf16(rng, shp)  # noqa: E731
+        offsets = offsets_from_lengths(lengths, offsets_dtype)
+    else:
+        gen = torch.Generator(device=device)
+        gen.manual_seed(seed)
+        draw = lambda shp: normal_bf16_device(gen, shp, device)  # noqa: E731
+        offsets = offsets_from_lengths(lengths, offsets_dtype).to(device)
+    q = draw(shapes[0])
+    k = draw(shapes[1])
+    v = draw(shapes[2])
+    g = draw(shapes[3]) if with_grad else None
+    return dict(q=q, k=k, v=v, g=g, offsets=offsets,
                 lengths=lengths, broadcast_q=broadcast_q, causal=causal,
                 scale=1.0 / math.sqrt(head_dim), q_len=q_len if broadcast_q else 0)
 
 
-def make_workload(name: str, seed: int = 0, with_grad: bool = True, offsets_dtype=None):
-    """The named workload at its full size (lengths first, then Q, K, V, G)."""
+def make_workload(name: str, seed: int = 0, with_grad: bool = True, offsets_dtype=None,
+                  device=None):
+    """The named workload at its full size (lengths first, then Q, K, V, G).
+
+    Lengths always come from numpy default_rng(seed); values from the same numpy
+    stream (device=None) or from a device generator seeded with ``seed``.
+    """
     w = WORKLOADS[name]
     rng = np.random.default_rng(seed)
     lengths = draw_lengths(w, rng)
     case = make_case(lengths, heads=w.heads, head_dim=w.head_dim, broadcast_q=w.broadcast_q,
                      causal=w.causal, q_len=w.q_len, offsets_dtype=offsets_dtype or w.offsets_dtype,
-                     with_grad=with_grad, rng=rng)
+                     with_grad=with_grad, rng=rng, seed=seed, device=device)
     case["workload"] = w
     return case
 
