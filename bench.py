@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Throughput of the jagged flash attention hot path on one MI355X.
+
+One step = one forward (plan + attention kernel) and one backward (delta pre-pass,
+plan, backward kernel, dQ finalize) over the whole synthetic batch, with inputs,
+outputs and workspaces resident in HBM before the timed region starts.  The
+value is useful TFLOP/s over forward + backward: per head and sequence
+4 Lq n D (forward) and 10 Lq n D (backward); n^2 instead of Lq n in self mode,
+halved under causal masking.
+
+The printed JSON line also carries the roofline of the dominant kernel (its
+algorithmic bytes or FLOPs per launch over its HIP-event-measured average launch
+duration) and the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import workloads  # noqa: E402
+
+METRIC = "useful TFLOP/s fwd & bwd, jagged broadcast-Q attn bf16; % of MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def useful_flops(w, lengths):
+    n = np.asarray(lengths, dtype=np.float64)
+    if w.broadcast_q:
+        fwd = 4.0 * w.q_len * n.sum() * w.head_dim * w.heads
+    else:
+        fwd = 4.0 * (n * n).sum() * w.head_dim * w.heads
+        if w.causal:
+            fwd *= 0.5
+    return fwd, 2.5 * fwd
+
+
+def algorithmic_bytes(w, lengths):
+    """Bytes each kernel must move at least once (bf16 tensors, fp32 LSE / delta)."""
+    t = float(np.sum(lengths))
+    hd = w.heads * w.head_dim
+    rows = len(lengths) * w.q_len if w.broadcast_q else t
+    q_rows = w.q_len if w.broadcast_q else t
+    q = q_rows * hd * 2
+    kv = t * hd * 2
+    o = rows * hd * 2
+    lse = rows * w.heads * 4
+    return {
+        "fwd": q + 2 * kv + o + lse,                          # Q, K, V in; O, LSE out
+        "bwd": q + 2 * kv + o + 2 * lse + 2 * kv + q,         # Q, K, V, dO, LSE, delta in; dK, dV, dQ out
+        "bwd_pre": 2 * o + lse,                               # O, dO in; delta out
+        "dq_finalize": q,                                     # dQ out (bf16)
+    }
+
+
+def cpu_baseline(case, w, budget_s: float):
+    """The fp64 oracle on a bounded sample of sequences of the same workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    off = case["offsets"].cpu().numpy().astype(np.int64)
+    lengths = np.diff(off)
+    rng = np.random.default_rng(1)
+    order = rng.permutation(len(lengths))
+    f64 = lambda t: t.to(torch.float64).numpy()  # noqa: E731
+    q_host = f64(case["q"].cpu()) if w.broadcast_q else None
+    flops = 0.0
+    used = 0
+    t0 = time.perf_counter()
+    for b in order:
+        a, e = int(off[b]), int(off[b + 1])
+        r0, r1 = (b * w.q_len, (b + 1) * w.q_len) if w.broadcast_q else (a, e)
+        for h in range(w.heads):
+            qb = q_host[:, h] if w.broadcast_q else f64(case["q"][a:e, h].cpu())
+            kb, vb = f64(case["k"][a:e, h].cpu()), f64(case["v"][a:e, h].cpu())
+            gb = f64(case["g"][r0:r1, h].cpu())
+            oracle.sequence_forward(qb, kb, vb, case["scale"], w.causal)
+            oracle.sequence_backward(qb, kb, vb, gb, case["scale"], w.causal)
+        f, bwd = useful_flops(w, [e - a])
+        flops += f + bwd
+        used += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{used} of {len(lengths)} sequences (random, seed 1) x {w.heads} heads of "
+                  f"{w.name}, fp64 numpy forward+backward, {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gem_broadcast", choices=workloads.ORDER)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--schedule", type=int, default=0, help="0 sorted+zigzag, 1 identity, 2 dynamic")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
+              "multi-GPU path in this build", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    import variable_length_flash_jfa_amd as jfa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.WORKLOADS[args.workload]
+    case = workloads.make_workload(args.workload, seed=args.seed, device=dev)
+    lengths = case["lengths"]
+    q, k, v, g, off = case["q"], case["k"], case["v"], case["g"], case["offsets"]
+    rows = len(lengths) * w.q_len if w.broadcast_q else int(lengths.sum())
+    o = torch.empty((rows, w.heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.heads, rows), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    bq, causal, scale = w.broadcast_q, w.causal, case["scale"]
+    sizes = (len(lengths), w.heads, w.head_dim, w.q_len if bq else 0, int(lengths.sum()), bq, causal)
+    ws_f = torch.empty(jfa.fwd_workspace_size(*sizes), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(jfa.bwd_workspace_size(*sizes), dtype=torch.uint8, device=dev)
+    jfa.set_schedule(args.schedule)
+
+    def step():
+        jfa.fwd(q, k, v, off, broadcast_q=bq, causal=causal, scale=scale, out=o, lse=lse, workspace=ws_f)
+        jfa.bwd(q, k, v, off, o, lse, g, broadcast_q=bq, causal=causal, scale=scale,
+                dq=dq, dk=dk, dv=dv, workspace=ws_b)
+
+    log(f"workload {w.name}: B={len(lengths)} H={w.heads} D={w.head_dim} Lq={w.q_len} "
+        f"T={int(lengths.sum())} lengths min/median/mean/max = {lengths.min()}/{np.median(lengths):.0f}/"
+        f"{lengths.mean():.1f}/{lengths.max()}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    jfa.profile_enable(True)
+    jfa.profile_read()            # clear
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    kernels = jfa.profile_read()
+    jfa.profile_enable(False)
+    ms_per_step = start.elapsed_time(stop) / args.steps
+
+    fwd_flops, bwd_flops = useful_flops(w, lengths)
+    value = (fwd_flops + bwd_flops) / (ms_per_step * 1e-3) / 1e12
+    per_launch = {name: ms / max(cnt, 1) for name, (ms, cnt) in kernels.items()}
+    fwd_ms = per_launch.get("plan_fwd", 0.0) + per_launch.get("fwd", 0.0)
+    bwd_ms = sum(per_launch.get(x, 0.0) for x in ("bwd_pre", "plan_bwd", "bwd", "dq_finalize"))
+    log("per-launch ms (HIP events): " + ", ".join(f"{k_}={v_:.4f}" for k_, v_ in per_launch.items()))
+
+    # roofline of the dominant kernel
+    abytes = algorithmic_bytes(w, lengths)
+    aflops = {"fwd": fwd_flops, "bwd": bwd_flops}
+    dom = max(("fwd", "bwd"), key=lambda x: per_launch.get(x, 0.0))
+    dom_s = per_launch[dom] * 1e-3
+    t_hbm = abytes[dom] / (PEAK_HBM_GBS * 1e9)
+    t_mfma = aflops[dom] / (PEAK_BF16_TFLOPS * 1e12)
+    if t_mfma >= t_hbm:
+        achieved, peak, unit, bound = aflops[dom] / dom_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        achieved, peak, unit, bound = abytes[dom] / dom_s / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+    roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom,
+                "algorithmic_bytes": abytes[dom], "algorithmic_flops": aflops[dom],
+                "avg_launch_ms": round(per_launch[dom], 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"timing the fp64 oracle on a sample (~{args.cpu_seconds:.0f} s) ...")
+        cpu = cpu_baseline(case, w, args.cpu_seconds)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "description": w.description,
+            "batch": len(lengths), "heads": w.heads, "head_dim": w.head_dim, "q_len": w.q_len,
+            "total_kv": int(lengths.sum()), "causal": causal, "broadcast_q": bq, "seed": args.seed,
+            "schedule": ["sorted_zigzag", "identity", "dynamic"][args.schedule],
+        },
+        "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 3) if fwd_ms else None,
+        "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 3) if bwd_ms else None,
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "kernel_ms": {k_: round(v_, 4) for k_, v_ in per_launch.items()},
+        "wall_s_timed": round(t_wall, 3),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if result["fwd_tflops"]:
+        result["fwd_pct_mfma_peak"] = round(100.0 * result["fwd_tflops"] / PEAK_BF16_TFLOPS, 2)
+    if result["bwd_tflops"]:
+        result["bwd_pct_mfma_peak"] = round(100.0 * result["bwd_tflops"] / PEAK_BF16_TFLOPS, 2)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

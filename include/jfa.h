@@ -116,6 +116,20 @@ jfa_status_t jfa_bwd(const void* q, const void* k, const void* v,
                      void* dq, void* dk, void* dv,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Measurement support.  While enabled on a thread, every kernel this library
+ * launches from that thread is bracketed by two HIP events recorded on the
+ * launch stream (events are created on first use and reused).  Kernel names:
+ * "plan_fwd", "fwd", "bwd_pre", "plan_bwd", "bwd", "dq_finalize". */
+jfa_status_t jfa_profile_enable(int enable);
+
+/* Waits for the recorded launches of this thread, then writes per-kernel totals:
+ * for entry i < max_entries, names[i * name_len ...] (NUL-terminated, truncated),
+ * total_ms[i] (sum of event-measured durations) and launches[i].  *count receives
+ * the number of distinct kernels seen.  The record is cleared.  Returns
+ * JFA_ERR_HIP if an event query fails. */
+jfa_status_t jfa_profile_read(char* names, int name_len, double* total_ms, int64_t* launches,
+                              int max_entries, int* count);
+
 /* Thread-local, NUL-terminated description of the last non-OK status returned
  * on this thread ("" if none).  Owned by the library; valid until the next call. */
 const char* jfa_last_error(void);

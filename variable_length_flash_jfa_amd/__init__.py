@@ -14,6 +14,8 @@ from ._binding import (  # noqa: F401
     fwd_workspace_size,
     bwd_workspace_size,
     set_schedule,
+    profile_enable,
+    profile_read,
     get_schedule,
     library,
     library_path,

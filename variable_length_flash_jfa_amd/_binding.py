@@ -73,6 +73,12 @@ def library() -> ctypes.CDLL:
             lib.jfa_set_schedule.restype = i32
             lib.jfa_get_schedule.argtypes = []
             lib.jfa_get_schedule.restype = i32
+            lib.jfa_profile_enable.argtypes = [i32]
+            lib.jfa_profile_enable.restype = i32
+            lib.jfa_profile_read.argtypes = [ctypes.c_char_p, i32, ctypes.POINTER(ctypes.c_double),
+                                             ctypes.POINTER(ctypes.c_int64), i32,
+                                             ctypes.POINTER(ctypes.c_int)]
+            lib.jfa_profile_read.restype = i32
             _lib = lib
         return _lib
 
@@ -93,6 +99,26 @@ def set_schedule(schedule: int) -> None:
 
 def get_schedule() -> int:
     return int(library().jfa_get_schedule())
+
+
+def profile_enable(enable: bool = True) -> None:
+    """Brackets every kernel launch of this thread with HIP events on its stream."""
+    _check(library().jfa_profile_enable(int(bool(enable))))
+
+
+def profile_read(max_entries: int = 16) -> dict:
+    """Waits for the recorded launches; returns {kernel: (total_ms, launches)} and clears."""
+    name_len = 32
+    names = ctypes.create_string_buffer(name_len * max_entries)
+    ms = (ctypes.c_double * max_entries)()
+    cnt = (ctypes.c_int64 * max_entries)()
+    count = ctypes.c_int(0)
+    _check(library().jfa_profile_read(names, name_len, ms, cnt, max_entries, ctypes.byref(count)))
+    out = {}
+    for i in range(min(count.value, max_entries)):
+        raw = names.raw[i * name_len:(i + 1) * name_len]
+        out[raw.split(b"\0", 1)[0].decode()] = (ms[i], int(cnt[i]))
+    return out
 
 
 def _ptr(t):

@@ -11,7 +11,9 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <string>
 #include <utility>
+#include <vector>
 
 #include "jfa_internal.h"
 
@@ -95,6 +97,38 @@ size_t bwd_ws_bytes(const jfa::Problem& p) {
   return kAlign + align_up(64) + align_up((size_t)jfa::bwd_max_items(p) * sizeof(int2)) +
          align_up((size_t)p.heads * p.rows * sizeof(float)) +
          align_up((size_t)q_rows * p.heads * p.head_dim * sizeof(float));
+}
+
+// ---- optional per-launch event timing (jfa_profile_*) ----------------------------
+struct ProfRecord {
+  const char* name;
+  hipEvent_t start, stop;
+};
+thread_local bool g_prof = false;
+thread_local std::vector<ProfRecord> g_prof_records;
+thread_local std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs one launch; when profiling is on, brackets it with events on `s`.
+template <typename F>
+hipError_t timed_launch(const char* name, hipStream_t s, F&& launch) {
+  if (!g_prof) return launch();
+  hipEvent_t a = prof_event(), b = prof_event();
+  if (a) (void)hipEventRecord(a, s);
+  const hipError_t e = launch();
+  if (b) (void)hipEventRecord(b, s);
+  if (a && b) g_prof_records.push_back({name, a, b});
+  return e;
 }
 
 bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) != 0; }
@@ -209,9 +243,9 @@ jfa_status_t jfa_fwd(const void* q, const void* k, const void* v, const void* of
   plan.items = reinterpret_cast<int2*>(carve(cur, plan.max_items * sizeof(int2)));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int sched = g_schedule.load();
-  hipError_t e = jfa::launch_plan_fwd(p, plan, sched, s);
+  hipError_t e = timed_launch("plan_fwd", s, [&] { return jfa::launch_plan_fwd(p, plan, sched, s); });
   if (e != hipSuccess) return hip_fail(e, "jfa_fwd: plan launch");
-  e = jfa::launch_fwd(p, plan, sched, o, lse, s);
+  e = timed_launch("fwd", s, [&] { return jfa::launch_fwd(p, plan, sched, o, lse, s); });
   if (e != hipSuccess) return hip_fail(e, "jfa_fwd: kernel launch");
   return JFA_OK;
 }
@@ -252,17 +286,61 @@ jfa_status_t jfa_bwd(const void* q, const void* k, const void* v, const void* of
   float* dq_acc = reinterpret_cast<float*>(carve(cur, (size_t)acc_elems * sizeof(float)));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int sched = g_schedule.load();
-  hipError_t e = jfa::launch_bwd_pre(p, o, d_o, delta, dq_acc, acc_elems, s);
+  hipError_t e = timed_launch("bwd_pre", s, [&] {
+    return jfa::launch_bwd_pre(p, o, d_o, delta, dq_acc, acc_elems, s);
+  });
   if (e != hipSuccess) return hip_fail(e, "jfa_bwd: delta launch");
   if (p.total_kv > 0) {
-    e = jfa::launch_plan_bwd(p, plan, sched, s);
+    e = timed_launch("plan_bwd", s, [&] { return jfa::launch_plan_bwd(p, plan, sched, s); });
     if (e != hipSuccess) return hip_fail(e, "jfa_bwd: plan launch");
-    e = jfa::launch_bwd(p, plan, sched, lse, d_o, delta, dq_acc, dk, dv, s);
+    e = timed_launch("bwd", s, [&] {
+      return jfa::launch_bwd(p, plan, sched, lse, d_o, delta, dq_acc, dk, dv, s);
+    });
     if (e != hipSuccess) return hip_fail(e, "jfa_bwd: kernel launch");
   }
-  e = jfa::launch_dq_finalize(p, dq_acc, dq, s);
+  e = timed_launch("dq_finalize", s, [&] { return jfa::launch_dq_finalize(p, dq_acc, dq, s); });
   if (e != hipSuccess) return hip_fail(e, "jfa_bwd: dq finalize launch");
   return JFA_OK;
+}
+
+jfa_status_t jfa_profile_enable(int enable) {
+  g_prof = enable != 0;
+  return JFA_OK;
+}
+
+jfa_status_t jfa_profile_read(char* names, int name_len, double* total_ms, int64_t* launches,
+                              int max_entries, int* count) {
+  std::vector<std::string> keys;
+  std::vector<double> ms;
+  std::vector<int64_t> cnt;
+  jfa_status_t st = JFA_OK;
+  for (const ProfRecord& r : g_prof_records) {
+    float t = 0.f;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, r.start, r.stop);
+    if (e != hipSuccess && st == JFA_OK) st = hip_fail(e, "jfa_profile_read");
+    size_t i = 0;
+    while (i < keys.size() && keys[i] != r.name) ++i;
+    if (i == keys.size()) {
+      keys.emplace_back(r.name);
+      ms.push_back(0.0);
+      cnt.push_back(0);
+    }
+    ms[i] += t;
+    cnt[i] += 1;
+    g_prof_pool.push_back(r.start);
+    g_prof_pool.push_back(r.stop);
+  }
+  g_prof_records.clear();
+  if (count) *count = (int)keys.size();
+  for (int i = 0; i < (int)keys.size() && i < max_entries; ++i) {
+    if (names && name_len > 0) {
+      snprintf(names + (size_t)i * name_len, (size_t)name_len, "%s", keys[i].c_str());
+    }
+    if (total_ms) total_ms[i] = ms[i];
+    if (launches) launches[i] = cnt[i];
+  }
+  return st;
 }
 
 const char* jfa_last_error(void) { return g_error; }
