@@ -120,6 +120,12 @@ struct BwdKernel {
   int64_t grow0;        // first dO / LSE row of the sequence
   bf16x8 vf[KS];
   f32x16 dvt[DT], dkt[DT];
+  // lane parts of the LDS addresses (see row_read_base / tr_read_base)
+  uint32_t row_base;     // Q, dO, K row reads
+  uint32_t tr4_base;     // Q^T, dO^T transposing reads (k offset 4 (lane / 32))
+  uint32_t tr8_base;     // K transposing reads for dQ (k offset 8 (lane / 32))
+  uint32_t ds_tr_base;   // dS^T transposing reads for dQ
+  uint32_t dq_lane_off;  // byte offset of this lane's dQ element within a query block
 
   __device__ BwdKernel(const BwdArgs& args, char* sm) : a(args), smem(sm) {
     lane = threadIdx.x & 63;
@@ -127,6 +133,12 @@ struct BwdKernel {
     c32 = lane & 31;
     hf = lane >> 5;
     rs = (int64_t)a.heads * D;
+    row_base = row_read_base<D>(lane);
+    tr4_base = tr_read_base<D>(lane, 4 * hf);
+    tr8_base = tr_read_base<D>(lane, 8 * hf);
+    const int t = lane & 15;
+    ds_tr_base = (uint32_t)((8 * hf + (t >> 2)) * (BQ * 2) + (((lane >> 4) & 1) * 16 + 4 * (t & 3)) * 2);
+    dq_lane_off = (uint32_t)(((4 * hf) * a.heads * D + 32 * wave + c32) * 4);
   }
 
   __device__ __forceinline__ char* qbuf(int b) { return smem + OFF_Q + b * QT_BYTES; }
@@ -167,17 +179,19 @@ struct BwdKernel {
     // Operands are read one step ahead of their MFMAs; the scheduling fences keep
     // the compiler from hoisting every read of the unrolled loop (which would push
     // the live registers past the 256 that two waves per SIMD allow).
+    const uint32_t rb = launder(row_base);
+    const char* kw = kt + 32 * wave * 2 * D;   // this wave's 32 keys
     f32x16 s = zero16(), dp = zero16();
-    bf16x8 qa = lds_read8(qt, tile_off<D>(c32, 8 * hf));
-    bf16x8 kb = lds_read8(kt, tile_off<D>(32 * wave + c32, 8 * hf));
-    bf16x8 ga = lds_read8(gt, tile_off<D>(c32, 8 * hf));
+    bf16x8 qa = lds_read8(qt, row_read_addr(rb, 0));
+    bf16x8 kb = lds_read8(kw, row_read_addr(rb, 0));
+    bf16x8 ga = lds_read8(gt, row_read_addr(rb, 0));
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       bf16x8 qa_n = qa, kb_n = kb, ga_n = ga;
       if (ks + 1 < KS) {
-        qa_n = lds_read8(qt, tile_off<D>(c32, 16 * (ks + 1) + 8 * hf));
-        kb_n = lds_read8(kt, tile_off<D>(32 * wave + c32, 16 * (ks + 1) + 8 * hf));
-        ga_n = lds_read8(gt, tile_off<D>(c32, 16 * (ks + 1) + 8 * hf));
+        qa_n = lds_read8(qt, row_read_addr(rb, ks + 1));
+        kb_n = lds_read8(kw, row_read_addr(rb, ks + 1));
+        ga_n = lds_read8(gt, row_read_addr(rb, ks + 1));
       }
       s = mfma32(qa, kb, s);
       dp = mfma32(ga, vf[ks], dp);
@@ -210,19 +224,20 @@ struct BwdKernel {
         sb[r >> 3][r & 7] = (bf16)ds;
       }
     }
-    // dV^T += dO^T P and dK^T += Q^T dS (C: m = d, n = key j)
+    // dV^T += dO^T P and dK^T += Q^T dS (C: m = d, n = key j); query rows
+    // 16 kc + 4 (lane / 32) + e and + 8 pair with the P / dS registers
     {
-      bf16x8 g_op = lds_operand_tr<D>(gt, 4 * hf, 4 * hf + 8, 0, lane);
-      bf16x8 q_op = lds_operand_tr<D>(qt, 4 * hf, 4 * hf + 8, 0, lane);
+      const uint32_t tb = launder(tr4_base);
+      bf16x8 g_op = lds_operand_tr<D>(gt, tb, 0, 8, 0);
+      bf16x8 q_op = lds_operand_tr<D>(qt, tb, 0, 8, 0);
 #pragma unroll
       for (int step = 0; step < 2 * DT; ++step) {
         const int kc = step / DT, dt = step % DT;
         bf16x8 g_n = g_op, q_n = q_op;
         if (step + 1 < 2 * DT) {
           const int kc1 = (step + 1) / DT, dt1 = (step + 1) % DT;
-          const int ib1 = 16 * kc1 + 4 * hf;
-          g_n = lds_operand_tr<D>(gt, ib1, ib1 + 8, 32 * dt1, lane);
-          q_n = lds_operand_tr<D>(qt, ib1, ib1 + 8, 32 * dt1, lane);
+          g_n = lds_operand_tr<D>(gt, tb, 16 * kc1, 16 * kc1 + 8, dt1);
+          q_n = lds_operand_tr<D>(qt, tb, 16 * kc1, 16 * kc1 + 8, dt1);
         }
         dvt[dt] = mfma32(g_op, pb[kc], dvt[dt]);
         dkt[dt] = mfma32(q_op, sb[kc], dkt[dt]);
@@ -242,42 +257,42 @@ struct BwdKernel {
     }
   }
 
-  // dQ_block[:, 32w .. 32w+31] = dS K over the tile's 128 keys, added to HBM.
+  // dQ_block[:, 32w .. 32w+31] = dS K over the tile's 128 keys, reduce-added into
+  // the fp32 accumulator with buffer atomics (rows past the query end fall outside
+  // the buffer range and are dropped by the hardware).
   __device__ __forceinline__ void dq_block(int64_t qi0) {
     if (wave >= DT) return;
     const char* kt = smem + OFF_K;
     const char* dst = smem + OFF_DS;
+    const uint32_t dsb = launder(ds_tr_base);
+    const uint32_t kb8 = launder(tr8_base);
     f32x16 dq = zero16();
-    const int t = lane & 15;
-    const int col = ((lane >> 4) & 1) * 16 + 4 * (t & 3);
-    auto ds_op = [&](int k0) {
-      return cat(lds_read_tr(dst + (k0 + (t >> 2)) * (BQ * 2) + col * 2),
-                 lds_read_tr(dst + (k0 + 4 + (t >> 2)) * (BQ * 2) + col * 2));
+    auto ds_op = [&](int jb) {   // dS[query l % 32][keys jb + 8 (l / 32) + e]
+      return cat(lds_read_tr(dst + dsb + jb * (BQ * 2)), lds_read_tr(dst + dsb + (jb + 4) * (BQ * 2)));
     };
-    bf16x8 sa = ds_op(8 * hf);
-    bf16x8 kb = lds_operand_tr<D>(kt, 8 * hf, 8 * hf + 4, 32 * wave, lane);
+    bf16x8 sa = ds_op(0);
+    bf16x8 kb = lds_operand_tr<D>(kt, kb8, 0, 4, wave);
 #pragma unroll
     for (int jb = 0; jb < BN; jb += 16) {
       bf16x8 sa_n = sa, kb_n = kb;
       if (jb + 16 < BN) {
-        const int k1 = jb + 16 + 8 * hf;
-        sa_n = ds_op(k1);
-        kb_n = lds_operand_tr<D>(kt, k1, k1 + 4, 32 * wave, lane);
+        sa_n = ds_op(jb + 16);
+        kb_n = lds_operand_tr<D>(kt, kb8, jb + 16, jb + 20, wave);
       }
       dq = mfma32(sa, kb, dq);
       sa = sa_n;
       kb = kb_n;
       __builtin_amdgcn_sched_barrier(0);
     }
-    const int d = 32 * wave + c32;
-    const int64_t stripe_rows = BCAST ? (int64_t)(blockIdx.x & (kDqStripes - 1)) * a.q_len : 0;
+    const int64_t rows = min((int64_t)q_rows - qi0, (int64_t)BQ);
+    const int64_t qrow0 = BCAST ? (int64_t)(blockIdx.x & (kDqStripes - 1)) * a.q_len + qi0 : kv0 + qi0;
+    const rsrc_t acc = make_rsrc(a.dq_acc + (qrow0 * a.heads + h) * D, (uint32_t)(rows * a.heads * D * 4));
+    const uint32_t row_bytes = (uint32_t)(a.heads * D * 4);
+    const uint32_t lo = launder(dq_lane_off);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t i = qi0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-      if (i < q_rows) {
-        const int64_t qrow = BCAST ? stripe_rows + i : kv0 + i;
-        unsafeAtomicAdd(a.dq_acc + (qrow * a.heads + h) * D + d, dq[r]);
-      }
+      const uint32_t off = lo + (uint32_t)(8 * (r >> 2) + (r & 3)) * row_bytes;
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dq[r], acc, off, 0, 0);
     }
   }
 

@@ -72,6 +72,8 @@ struct FwdKernel {
   bf16x8 qf[KS];
   f32x16 acc[DT];
   float mrun, lsum;
+  uint32_t k_row_base;   // lane part of K row reads (rows 32 c + lane % 32)
+  uint32_t v_tr_base;    // lane part of V^T transposing reads (k offset 4 (lane / 32))
 
   __device__ FwdKernel(const FwdArgs& args, char* sm) : a(args), smem(sm) {
     lane = threadIdx.x & 63;
@@ -79,6 +81,8 @@ struct FwdKernel {
     c32 = lane & 31;
     hf = lane >> 5;
     rs = (int64_t)a.heads * D;
+    k_row_base = row_read_base<D>(lane);
+    v_tr_base = tr_read_base<D>(lane, 4 * hf);
   }
 
   __device__ __forceinline__ char* kbuf(int buf) { return smem + (buf * 2 + 0) * TILE_BYTES; }
@@ -101,13 +105,15 @@ struct FwdKernel {
   __device__ __forceinline__ void compute_block(int buf, int blk) {
     const char* kb = kbuf(buf);
     const char* vb = vbuf(buf);
+    const uint32_t krb = launder(k_row_base);
+    const uint32_t vtb = launder(v_tr_base);
     f32x16 s[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       s[c] = zero16();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kf = lds_read8(kb, tile_off<D>(32 * c + c32, 16 * ks + 8 * hf));
+        const bf16x8 kf = lds_read8(kb, row_read_addr(krb, ks) + 32 * c * 2 * D);
         s[c] = mfma32(kf, qf[ks], s[c]);
       }
     }
@@ -156,10 +162,10 @@ struct FwdKernel {
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
-        const int jb = 32 * c + 16 * kc + 4 * hf;
+        const int jb = 32 * c + 16 * kc;   // keys jb + 4 (lane / 32) + e, and + 8
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const bf16x8 vt = lds_operand_tr<D>(vb, jb, jb + 8, 32 * dt, lane);
+          const bf16x8 vt = lds_operand_tr<D>(vb, vtb, jb, jb + 8, dt);
           acc[dt] = mfma32(vt, p[c][kc], acc[dt]);
         }
       }

@@ -68,26 +68,79 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // ---- swizzled LDS tiles -----------------------------------------------------
 
+// XOR mask applied to the 16-byte chunk index of a row.  For D = 128 (16 chunks)
+// rows 0..15 get 16 distinct masks; for D = 64 (8 chunks) rows 0..7 get 8.
 template <int D>
-__device__ __forceinline__ int swz_chunk(int row, int chunk) {
+__host__ __device__ __forceinline__ int swz_mask(int row) {
   if constexpr (D == 128) {
-    return chunk ^ (((row & 3) << 2) | ((row >> 2) & 3));
+    return ((row & 3) << 2) | ((row >> 2) & 3);
   } else {
-    return chunk ^ (((row & 3) << 1) | ((row >> 2) & 1));
+    return ((row & 3) << 1) | ((row >> 2) & 1);
   }
 }
 
-// Byte offset of element (row, col) of a [rows][D] bf16 tile; col % 4 == 0 or the
-// 16-byte chunk start.
 template <int D>
-__device__ __forceinline__ int tile_off(int row, int col) {
+__host__ __device__ __forceinline__ int swz_chunk(int row, int chunk) {
+  return chunk ^ swz_mask<D>(row);
+}
+
+// Byte offset of element (row, col) of a [rows][D] bf16 tile; col % 4 == 0.
+template <int D>
+__host__ __device__ __forceinline__ int tile_off(int row, int col) {
   return row * (D * 2) + (swz_chunk<D>(row, col >> 3) << 4) + ((col & 7) << 1);
 }
 
-__device__ __forceinline__ bf16x8 lds_read8(const char* base, int off) {
+// Fast per-lane addressing.  Every LDS operand read of the kernels is written as
+// (lane_base ^ x) + y with compile-time (or wave-uniform) x and y, so that one
+// VGPR per access pattern holds the lane's part and each read costs at most one
+// XOR (y becomes the instruction's immediate offset).
+//
+// Row read (MFMA A operand, or B operand of a K^T product): lane l reads the 16
+// bytes of logical chunk 2 * ks + l / 32 of row r0 + l % 32, r0 a multiple of 16:
+//   tile_off(r0 + l % 32, 16 ks + 8 (l / 32)) == (row_base ^ (ks << 5)) + r0 * 2D.
+template <int D>
+__host__ __device__ __forceinline__ uint32_t row_read_base(int lane) {
+  const int r = lane & 31, hf = lane >> 5;
+  return (uint32_t)(r * (2 * D) + ((hf ^ swz_mask<D>(r)) << 4));
+}
+__host__ __device__ __forceinline__ uint32_t row_read_addr(uint32_t base, int ks) {
+  return base ^ (uint32_t)(ks << 5);
+}
+
+// Transposing read (ds_read_b64_tr_b16): lane l supplies row kl + K + (t >> 2) and
+// column 32 dt + 16 ((l >> 4) & 1) + 4 (t & 3), t = l % 16, where kl is the lane's
+// k offset (4 (l / 32) or 8 (l / 32)) and K a compile-time multiple of 4 (0, 4, 8,
+// 16 m, 32 m and their sums as used by the kernels: adding K then flips the row
+// mask by a constant, see tr_mask_delta):
+//   tile_off(kl + K + (t >> 2), col) == (tr_base ^ (((4 dt) ^ delta(K)) << 4)) + K * 2D.
+template <int D>
+__host__ __device__ __forceinline__ uint32_t tr_read_base(int lane, int kl) {
+  const int t = lane & 15, g1 = (lane >> 4) & 1;
+  const int r = kl + (t >> 2);
+  const int cl = 16 * g1 + 4 * (t & 3);
+  return (uint32_t)(r * (2 * D) + (((cl >> 3) ^ swz_mask<D>(r)) << 4) + ((cl & 7) << 1));
+}
+template <int D>
+__host__ __device__ __forceinline__ int tr_mask_delta(int K) {
+  return D == 128 ? ((K >> 2) & 3) : ((K >> 2) & 1);
+}
+template <int D>
+__host__ __device__ __forceinline__ uint32_t tr_read_addr(uint32_t base, int K, int dt) {
+  return (base ^ (uint32_t)(((4 * dt) ^ tr_mask_delta<D>(K)) << 4)) + (uint32_t)(K * 2 * D);
+}
+
+// Hides a value from the optimiser so that addresses derived from it are
+// recomputed where they are used instead of being hoisted out of loops (which
+// would keep dozens of loop-invariant addresses alive in VGPRs).
+__device__ __forceinline__ uint32_t launder(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+__device__ __forceinline__ bf16x8 lds_read8(const char* base, uint32_t off) {
   return *reinterpret_cast<const bf16x8*>(base + off);
 }
-__device__ __forceinline__ void lds_write8(char* base, int off, bf16x8 v) {
+__device__ __forceinline__ void lds_write8(char* base, uint32_t off, bf16x8 v) {
   *reinterpret_cast<bf16x8*>(base + off) = v;
 }
 
@@ -100,15 +153,14 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
       (__attribute__((address_space(3))) bf16x4*)(p));
 }
 
-// MFMA A/B operand (32 columns x 8 k) taken from a row-major [k][n] bf16 tile in
-// LDS through two transposing reads: lane l gets M[kb + e][nb + l % 32] for e = 0..3
-// from rows kb.., and M[kb2 + e][...] for e = 4..7 from rows kb2...
+// MFMA operand (32 columns x 8 k) from a swizzled row-major [k][n] tile through two
+// transposing reads: lane l gets M[kl + Klo + e][32 dt + l % 32] for e = 0..3 and
+// M[kl + Khi + e][...] for e = 4..7 (kl is folded into tr_base).
 template <int D>
-__device__ __forceinline__ bf16x8 lds_operand_tr(const char* tile, int kb, int kb2, int nb, int lane) {
-  const int t = lane & 15;
-  const int col = nb + ((lane >> 4) & 1) * 16 + 4 * (t & 3);
-  const bf16x4 lo = lds_read_tr(tile + tile_off<D>(kb + (t >> 2), col));
-  const bf16x4 hi = lds_read_tr(tile + tile_off<D>(kb2 + (t >> 2), col));
+__device__ __forceinline__ bf16x8 lds_operand_tr(const char* tile, uint32_t tr_base, int Klo, int Khi,
+                                                 int dt) {
+  const bf16x4 lo = lds_read_tr(tile + tr_read_addr<D>(tr_base, Klo, dt));
+  const bf16x4 hi = lds_read_tr(tile + tr_read_addr<D>(tr_base, Khi, dt));
   return cat(lo, hi);
 }
 
