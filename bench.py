@@ -120,6 +120,9 @@ def main():
     ap.add_argument("--schedule", type=int, default=0, help="0 sorted+zigzag, 1 identity, 2 dynamic")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (3 times); used to scale the "
+                         "FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -129,6 +132,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+
+    if args.copy_probe:
+        src = torch.ones(args.copy_probe // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": src.numel() * 4, "launches": 3}), flush=True)
+        return
 
     import variable_length_flash_jfa_amd as jfa
 

@@ -23,3 +23,24 @@ def test_fast_lds_addressing_matches_swizzle(tmp_path):
     run = subprocess.run([str(exe)], capture_output=True, text=True)
     assert run.returncode == 0, run.stdout + run.stderr
     assert "mismatches=0" in run.stdout
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+@pytest.mark.parametrize("src", ["fwd.hip", "bwd.hip"])
+def test_m0_only_written_by_lds_load_asm(tmp_path, src):
+    """The direct-to-LDS loads set M0 in inline assembly; that is only sound while
+    no compiler-generated instruction of the kernels reads or writes M0."""
+    csrc = os.path.join(ROOT, "variable_length_flash_jfa_amd", "csrc")
+    out = tmp_path / (src + ".s")
+    cmd = [HIPCC, "-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", os.path.join(ROOT, "include"), "-I", csrc, "-S", "--cuda-device-only",
+           os.path.join(csrc, src), "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    code = [ln.strip() for ln in out.read_text().splitlines()
+            if ln.strip() and not ln.strip().startswith((";", "."))]
+    uses = [ln for ln in code if "m0" in ln.replace(",", " ").split()]
+    asm_sets = [ln for ln in uses if ln.startswith("s_mov_b32 m0, s")]
+    assert asm_sets, "expected the LDS-load assembly to set M0"
+    assert uses == asm_sets, f"unexpected M0 uses: {sorted(set(uses) - set(asm_sets))[:5]}"

@@ -136,8 +136,12 @@ struct BwdKernel {
     row_base = row_read_base<D>(lane);
     tr4_base = tr_read_base<D>(lane, 4 * hf);
     tr8_base = tr_read_base<D>(lane, 8 * hf);
+    // dS^T tile [BN keys][BQ queries] bf16, 64-byte rows of eight 8-byte units; unit u
+    // of row j is stored at u ^ ((j >> 2) & 7), which keeps both the 32-row writes
+    // and the 4-row transposing reads free of bank conflicts.
     const int t = lane & 15;
-    ds_tr_base = (uint32_t)((8 * hf + (t >> 2)) * (BQ * 2) + (((lane >> 4) & 1) * 16 + 4 * (t & 3)) * 2);
+    const int unit = 4 * ((lane >> 4) & 1) + (t & 3);
+    ds_tr_base = (uint32_t)((8 * hf + (t >> 2)) * (BQ * 2) + ((unit ^ (2 * hf)) << 3));
     dq_lane_off = (uint32_t)(((4 * hf) * a.heads * D + 32 * wave + c32) * 4);
   }
 
@@ -156,13 +160,13 @@ struct BwdKernel {
     const uint32_t bytes = (uint32_t)(rows * rs * 2);
     const bf16* qsrc = a.q + ((BCAST ? 0 : kv0) + qi0) * rs + (int64_t)h * D;
     const bf16* gsrc = a.d_o + (grow0 + qi0) * rs + (int64_t)h * D;
-    lds_load_tile<D, kBwdWaves>(qbuf(buf), BQ, wave, lane, make_rsrc(qsrc, bytes), row_bytes);
-    lds_load_tile<D, kBwdWaves>(gbuf(buf), BQ, wave, lane, make_rsrc(gsrc, bytes), row_bytes);
+    lds_load_tile<D, kBwdWaves>(qbuf(buf), BQ, wave, lane, make_rsrc_sgpr(qsrc, bytes), row_bytes);
+    lds_load_tile<D, kBwdWaves>(gbuf(buf), BQ, wave, lane, make_rsrc_sgpr(gsrc, bytes), row_bytes);
     if (wave == kBwdWaves - 1) {
       const int64_t r0 = (int64_t)h * a.rows + grow0 + qi0;
       const uint32_t rb = (uint32_t)(rows * 4);
-      lds_load4(make_rsrc(a.lse + r0, rb), (uint32_t)lane * 4u, reinterpret_cast<char*>(rowbuf(buf)));
-      lds_load4(make_rsrc(a.delta + r0, rb), (uint32_t)lane * 4u, reinterpret_cast<char*>(rowbuf(buf) + 64));
+      lds_load4(make_rsrc_sgpr(a.lse + r0, rb), (uint32_t)lane * 4u, reinterpret_cast<char*>(rowbuf(buf)));
+      lds_load4(make_rsrc_sgpr(a.delta + r0, rb), (uint32_t)lane * 4u, reinterpret_cast<char*>(rowbuf(buf) + 64));
     }
   }
 
@@ -248,12 +252,16 @@ struct BwdKernel {
     }
     // publish dS^T [key][query] (bf16) once the previous block's dQ reads are done
     __syncthreads();
+    {
+      const int j = 32 * wave + c32;
+      const int sw = (j >> 2) & 7;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      bf16x4 w;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = sb[q4 >> 1][4 * (q4 & 1) + e];
-      *reinterpret_cast<bf16x4*>(dst + (32 * wave + c32) * (BQ * 2) + (8 * q4 + 4 * hf) * 2) = w;
+        for (int e = 0; e < 4; ++e) w[e] = sb[q4 >> 1][4 * (q4 & 1) + e];
+        *reinterpret_cast<bf16x4*>(dst + j * (BQ * 2) + (((2 * q4 + hf) ^ sw) << 3)) = w;
+      }
     }
   }
 
@@ -266,9 +274,12 @@ struct BwdKernel {
     const char* dst = smem + OFF_DS;
     const uint32_t dsb = launder(ds_tr_base);
     const uint32_t kb8 = launder(tr8_base);
-    f32x16 dq = zero16();
+    // two independent accumulators halve the dependent-MFMA chain
+    f32x16 dq = zero16(), dq2 = zero16();
     auto ds_op = [&](int jb) {   // dS[query l % 32][keys jb + 8 (l / 32) + e]
-      return cat(lds_read_tr(dst + dsb + jb * (BQ * 2)), lds_read_tr(dst + dsb + (jb + 4) * (BQ * 2)));
+      const uint32_t x = (uint32_t)(((jb >> 2) & 4) << 3);
+      return cat(lds_read_tr(dst + ((dsb ^ x) + jb * (BQ * 2))),
+                 lds_read_tr(dst + ((dsb ^ x ^ 8u) + (jb + 4) * (BQ * 2))));
     };
     bf16x8 sa = ds_op(0);
     bf16x8 kb = lds_operand_tr<D>(kt, kb8, 0, 4, wave);
@@ -279,11 +290,17 @@ struct BwdKernel {
         sa_n = ds_op(jb + 16);
         kb_n = lds_operand_tr<D>(kt, kb8, jb + 16, jb + 20, wave);
       }
-      dq = mfma32(sa, kb, dq);
+      if ((jb / 16) & 1) {
+        dq2 = mfma32(sa, kb, dq2);
+      } else {
+        dq = mfma32(sa, kb, dq);
+      }
       sa = sa_n;
       kb = kb_n;
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[r] += dq2[r];
     const int64_t rows = min((int64_t)q_rows - qi0, (int64_t)BQ);
     const int64_t qrow0 = BCAST ? (int64_t)(blockIdx.x & (kDqStripes - 1)) * a.q_len + qi0 : kv0 + qi0;
     const rsrc_t acc = make_rsrc(a.dq_acc + (qrow0 * a.heads + h) * D, (uint32_t)(rows * a.heads * D * 4));
@@ -296,15 +313,24 @@ struct BwdKernel {
     }
   }
 
+  // Query-block loop.  Iteration t issues the LDS loads of block t + 1, then the
+  // dQ reduce-adds of block t - 1, then block t.  Vector memory operations retire in
+  // issue order, so the wait before the barrier (for the loads) leaves the 16
+  // reduce-adds issued after them in flight.
   template <bool MASKED>
-  __device__ __forceinline__ void run(int64_t qs, int64_t qe, int64_t q_last) {
+  __device__ __forceinline__ void run(int64_t qs, int64_t qe, int64_t q_last, int64_t& pending) {
     for (int64_t qi0 = qs; qi0 < qe; qi0 += BQ) {
       const int buf = (int)((qi0 / BQ) & 1);
       if (qi0 + BQ < q_last) load_qblock(qi0 + BQ, buf ^ 1);   // one block ahead
+      if (pending >= 0) dq_block(pending);
       qblock<MASKED>(buf, qi0);
-      wait_lds_loads();
+      if (pending >= 0 && wave < DT) {
+        wait_lds_loads_but_16();
+      } else {
+        wait_lds_loads();
+      }
       __syncthreads();
-      dq_block(qi0);
+      pending = qi0;
     }
   }
 
@@ -322,7 +348,7 @@ struct BwdKernel {
     {
       const int64_t rows = min(n - j0, (int64_t)BN);
       lds_load_tile<D, kBwdWaves>(smem + OFF_K, BN, wave, lane,
-                                  make_rsrc(a.k + (kv0 + j0) * rs + (int64_t)h * D, (uint32_t)(rows * rs * 2)),
+                                  make_rsrc_sgpr(a.k + (kv0 + j0) * rs + (int64_t)h * D, (uint32_t)(rows * rs * 2)),
                                   (uint32_t)(rs * 2));
       const int64_t j = j0 + 32 * wave + c32;
 #pragma unroll
@@ -350,9 +376,11 @@ struct BwdKernel {
     if constexpr (CAUSAL) qm = min(q_last, ((j0 + BN - 1 + BQ - 1) / BQ) * BQ);
     if (kv_tail) qm = q_last;
     const int64_t qfull = max(qm, (q_last / BQ) * BQ);
-    run<true>(qs, qm, q_last);
-    run<false>(qm, qfull, q_last);
-    run<true>(qfull, q_last, q_last);
+    int64_t pending = -1;   // query block whose dQ reduce-add is still to be issued
+    run<true>(qs, qm, q_last, pending);
+    run<false>(qm, qfull, q_last, pending);
+    run<true>(qfull, q_last, q_last, pending);
+    if (pending >= 0) dq_block(pending);
 
     // dK = c dS^T Q and dV -> bf16
     const int64_t j = j0 + 32 * wave + c32;

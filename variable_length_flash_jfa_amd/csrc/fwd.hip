@@ -96,8 +96,8 @@ struct FwdKernel {
     const uint32_t bytes = (uint32_t)(rows * rs * 2);
     const int64_t base = (kv0 + jb) * rs + (int64_t)h * D;
     const uint32_t row_bytes = (uint32_t)(rs * 2);
-    lds_load_tile<D, NW>(kbuf(buf), BN, wave, lane, make_rsrc(a.k + base, bytes), row_bytes);
-    lds_load_tile<D, NW>(vbuf(buf), BN, wave, lane, make_rsrc(a.v + base, bytes), row_bytes);
+    lds_load_tile<D, NW>(kbuf(buf), BN, wave, lane, make_rsrc_sgpr(a.k + base, bytes), row_bytes);
+    lds_load_tile<D, NW>(vbuf(buf), BN, wave, lane, make_rsrc_sgpr(a.v + base, bytes), row_bytes);
   }
 
   // One K/V block for this wave's 32 query rows.

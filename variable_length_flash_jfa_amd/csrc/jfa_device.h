@@ -178,14 +178,46 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 // starting at the wave-uniform LDS address `lds`.  Completion is tracked by the
 // vector-memory counter: call wait_lds_loads() before the barrier that publishes
 // the data.
-__device__ __forceinline__ void lds_load16(rsrc_t r, uint32_t voff, char* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+//
+// The loads are issued through inline assembly on purpose: the compiler cannot
+// tell which LDS bytes a DMA load writes, so for the builtin it inserts a full
+// vmcnt(0) wait before the next LDS read, which would expose every prefetch (and
+// every outstanding dQ reduce-add).  The kernels instead wait explicitly before the
+// barrier that publishes a buffer.  The compiler does not count these loads, which
+// can only make its own vmcnt waits more conservative (vector memory operations
+// retire in issue order).
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p);
 }
-__device__ __forceinline__ void lds_load4(rsrc_t r, uint32_t voff, char* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
+// Buffer descriptor words forced into SGPRs (the same fields as make_rsrc).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 make_rsrc_sgpr(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+__device__ __forceinline__ void lds_load16(u32x4 r, uint32_t voff, char* lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(lds_addr(lds))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_load4(u32x4 r, uint32_t voff, char* lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(lds_addr(lds))
+               : "memory", "m0");
 }
 // s_waitcnt vmcnt(0): all of this wave's vector memory operations are complete.
 __device__ __forceinline__ void wait_lds_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(16): all but the 16 most recently issued vector memory operations
+// are complete (they retire in issue order).
+__device__ __forceinline__ void wait_lds_loads_but_16() { __builtin_amdgcn_s_waitcnt(0x4F70); }
 
 // Copies rows [0, nrows) of a [rows][D] bf16 tile (row r at byte r * row_bytes of
 // the buffer) into a swizzled LDS tile.  Each wave instruction covers 1024 bytes =
@@ -193,7 +225,7 @@ __device__ __forceinline__ void wait_lds_loads() { __builtin_amdgcn_s_waitcnt(0x
 // fills LDS chunk slot (i % CH) of its row, so it fetches logical chunk
 // swz_chunk(row, slot) (the swizzle is an XOR involution).
 template <int D, int NW>
-__device__ __forceinline__ void lds_load_tile(char* tile, int nrows, int wave, int lane, rsrc_t r,
+__device__ __forceinline__ void lds_load_tile(char* tile, int nrows, int wave, int lane, u32x4 r,
                                               uint32_t row_bytes) {
   constexpr int CH = D / 8;
   constexpr int RPI = 64 / CH;
