@@ -31,6 +31,8 @@ import torch  # noqa: E402
 import workloads  # noqa: E402
 
 METRIC = "useful TFLOP/s fwd & bwd, jagged broadcast-Q attn bf16; % of MFMA peak"
+KERNEL_SOURCES = ["fwd.hip", "bwd.hip", "plan.hip", "jfa_device.h", "jfa_internal.h"]
+PROFILES = os.path.join(ROOT, "profiles")
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 
@@ -66,6 +68,34 @@ def algorithmic_bytes(w, lengths):
         "bwd_pre": 2 * o + lse,                               # O, dO in; delta out
         "dq_finalize": q,                                     # dQ out (bf16)
     }
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the kernel sources; ties stored counter readings to this build."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "variable_length_flash_jfa_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    summary is missing or was taken on different kernel sources.
+
+    profiles/traffic_<kernel>_<workload>.json holds FETCH_SIZE and WRITE_SIZE (KiB
+    per dispatch) and the factors that map them to bytes, measured with a plain
+    copy of known size (bench.py --copy-probe)."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return (rec["fetch_kib"] * 1024 * rec["fetch_factor"] + rec["write_kib"] * 1024 * rec["write_factor"])
 
 
 def cpu_baseline(case, w, budget_s: float):
@@ -206,8 +236,9 @@ def main():
         achieved, peak, unit, bound = aflops[dom] / dom_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
     else:
         achieved, peak, unit, bound = abytes[dom] / dom_s / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+    traffic = measured_traffic(dom, w.name)
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom,
+                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
                 "algorithmic_bytes": abytes[dom], "algorithmic_flops": aflops[dom],
                 "avg_launch_ms": round(per_launch[dom], 4)}
 
@@ -236,6 +267,7 @@ def main():
             "total_kv": int(lengths.sum()), "causal": causal, "broadcast_q": bq, "seed": args.seed,
             "schedule": ["sorted_zigzag", "identity", "dynamic"][args.schedule],
         },
+        "kernel_source_hash": kernel_source_hash(),
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 3) if fwd_ms else None,
         "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 3) if bwd_ms else None,
