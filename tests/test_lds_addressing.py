@@ -40,7 +40,11 @@ def test_m0_only_written_by_lds_load_asm(tmp_path, src):
     assert res.returncode == 0, res.stderr[-2000:]
     code = [ln.strip() for ln in out.read_text().splitlines()
             if ln.strip() and not ln.strip().startswith((";", "."))]
-    uses = [ln for ln in code if "m0" in ln.replace(",", " ").split()]
-    asm_sets = [ln for ln in uses if ln.startswith("s_mov_b32 m0, s")]
-    assert asm_sets, "expected the LDS-load assembly to set M0"
-    assert uses == asm_sets, f"unexpected M0 uses: {sorted(set(uses) - set(asm_sets))[:5]}"
+    uses = [i for i, ln in enumerate(code) if "m0" in ln.replace(",", " ").split()]
+    assert uses, "expected the LDS-load assembly to set M0"
+    for i in uses:
+        # the only M0 writer is the inline pair "s_mov_b32 m0, <sgpr>" followed at
+        # once by the LDS-direct buffer load that consumes it
+        assert code[i].startswith("s_mov_b32 m0, "), f"unexpected M0 use: {code[i]}"
+        assert i + 1 < len(code) and code[i + 1].startswith("buffer_load_dword") \
+            and code[i + 1].endswith(" lds"), f"M0 write not followed by an LDS load: {code[i:i + 2]}"

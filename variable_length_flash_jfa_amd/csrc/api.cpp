@@ -62,7 +62,7 @@ Sizes check_sizes(int64_t batch, int64_t heads, int64_t head_dim, int64_t q_len,
   const int64_t rows = broadcast_q ? batch * q_len : total_kv;
   if (batch >= lim || total_kv >= lim || q_len >= lim || heads >= 4096 || rows >= ((int64_t)1 << 36))
     return {false, "problem too large for this library build", JFA_ERR_UNSUPPORTED};
-  if ((total_kv / jfa::kBwdBN + batch) * heads >= lim)
+  if ((total_kv / 128 + batch) * heads >= lim)
     return {false, "too many tiles for this library build", JFA_ERR_UNSUPPORTED};
   return {true, "", JFA_OK};
 }

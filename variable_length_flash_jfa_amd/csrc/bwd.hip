@@ -7,22 +7,25 @@
 //      Eliminations", the Di preprocessing) -- and zeroing of the fp32 dQ
 //      accumulator;
 //   2. the backward tile planner (plan.hip);
-//   3. bwd_kernel: persistent workgroups over valid (sequence, 128-key block, head)
-//      tiles.  Four waves own 32 keys each, hold dK^T / dV^T accumulators and
+//   3. bwd_kernel: persistent workgroups over valid (sequence, 256-key block, head)
+//      tiles.  Eight waves own 32 keys each, hold dK^T / dV^T accumulators and
 //      their V fragment in registers, and stream the tile's query rows in blocks
-//      of 32 straight from HBM into double-buffered LDS (gfx950 direct LDS loads).  Per query block every wave recomputes
-//      P from the saved LSE and forms dV^T += dO^T P, dP = dO V^T,
-//      dS = P (dP - delta), dK^T += Q^T dS on v_mfma_f32_32x32x16_bf16;
-//   4. the dQ contribution of the whole 128-key tile is reduced in LDS first: the
-//      waves publish dS^T to LDS and each computes a 32-column slice of
-//      dQ_block = dS K over all 128 keys, so a tile adds one fp32 partial per query
-//      row into HBM instead of one per wave.  In broadcast-Q mode every sequence
+//      of 32 straight from HBM into double-buffered LDS (gfx950 direct LDS loads).
+//      Per query block every wave recomputes P from the saved LSE and forms
+//      dV^T += dO^T P, dP = dO V^T, dS = P (dP - delta), dK^T += Q^T dS on
+//      v_mfma_f32_32x32x16_bf16.  Waves whose 32 keys all lie past the sequence
+//      end skip their work;
+//   4. the dQ contribution of the whole 256-key tile is reduced on chip first: the
+//      waves publish dS^T to LDS, each computes one 32-column slice of dS K over
+//      one part of the keys, the parts are summed through LDS, and a tile adds one
+//      fp32 partial per query row into HBM.  In broadcast-Q mode every sequence
 //      adds into the same dQ ("Meta's TLX attention kernel outpaces
 //      FlashAttention-4 on B200", section "GEM's sequences do not fit a fixed
-//      grid"), so the accumulator is striped per XCD (8 fp32 copies) to keep the
-//      reduce-adds inside each XCD's L2 (the pages stage this reduction through a
-//      double-buffered on-chip pipeline: section "Five changes unlocked the
-//      gains", item 3);
+//      grid"), so the accumulator is striped per XCD (8 fp32 copies).  The
+//      reduce-adds of a block are issued behind the loads of the next one and
+//      stay in flight while it computes (the pages pipeline this reduction through
+//      a double-buffered on-chip stage: section "Five changes unlocked the gains",
+//      item 3);
 //   5. dq_finalize_kernel: sum of the stripes, times the softmax scale -> bf16.
 #include "jfa_device.h"
 #include "jfa_internal.h"
@@ -89,35 +92,41 @@ struct BwdArgs {
   int sched;
 };
 
-template <int D, bool BCAST, bool CAUSAL>
+template <int D, int NW, bool BCAST, bool CAUSAL>
 struct BwdKernel {
-  static constexpr int BN = kBwdBN;     // keys per tile (4 waves x 32)
-  static constexpr int BQ = kBwdBQ;     // query rows per block
-  static constexpr int NT = 64 * kBwdWaves;
-  static constexpr int CH = D / 8;
-  static constexpr int DT = D / 32;
-  static constexpr int KS = D / 16;
+  static constexpr int BN = 32 * NW;         // keys per tile (NW waves x 32)
+  static constexpr int BQ = kBwdBQ;          // query rows per block
+  static constexpr int NT = 64 * NW;
+  static constexpr int DT = D / 32;          // 32-wide d tiles
+  static constexpr int KS = D / 16;          // 16-deep k steps over d
+  static constexpr int KP = NW / DT;         // key parts of the dQ product
+  static constexpr int KPART = BN / KP;      // keys per part
   static constexpr int KT_BYTES = BN * D * 2;
   static constexpr int QT_BYTES = BQ * D * 2;
   static constexpr int DS_BYTES = BN * BQ * 2;
+  static constexpr int DQP_BYTES = KP > 1 ? KP * DT * 32 * 32 * 4 : 0;
   // LDS map
   static constexpr int OFF_K = 0;
   static constexpr int OFF_Q = OFF_K + KT_BYTES;              // 2 buffers
   static constexpr int OFF_DO = OFF_Q + 2 * QT_BYTES;         // 2 buffers
   static constexpr int OFF_DS = OFF_DO + 2 * QT_BYTES;
-  static constexpr int OFF_ROW = OFF_DS + DS_BYTES;           // [2][lse, delta][64] fp32
+  static constexpr int OFF_DQP = OFF_DS + DS_BYTES;           // dQ partials of the KP key parts
+  static constexpr int OFF_ROW = OFF_DQP + DQP_BYTES;         // [2][lse, delta][64] fp32
   static constexpr int SMEM = OFF_ROW + 2 * 2 * 64 * 4;
-  static_assert((BQ * D * 2 / 1024) % kBwdWaves == 0, "a query block must split evenly over the waves");
+  static_assert(BN == 32 * NW && KP * DT == NW && KPART % 16 == 0, "tile shape");
 
   BwdArgs a;
   char* smem;
   int lane, wave, c32, hf;
   int64_t rs;
+  int dq_dt, dq_part;    // this wave's d tile and key part in the dQ product
 
   // per tile
   int64_t kv0, n, j0;
   int h, q_rows;
-  int64_t grow0;        // first dO / LSE row of the sequence
+  int nvalid;            // keys of this tile inside the sequence (1..BN)
+  bool active;           // this wave owns at least one key inside the sequence
+  int64_t grow0;         // first dO / LSE row of the sequence
   bf16x8 vf[KS];
   f32x16 dvt[DT], dkt[DT];
   // lane parts of the LDS addresses (see row_read_base / tr_read_base)
@@ -129,10 +138,12 @@ struct BwdKernel {
 
   __device__ BwdKernel(const BwdArgs& args, char* sm) : a(args), smem(sm) {
     lane = threadIdx.x & 63;
-    wave = threadIdx.x >> 6;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
     c32 = lane & 31;
     hf = lane >> 5;
     rs = (int64_t)a.heads * D;
+    dq_dt = wave % DT;
+    dq_part = wave / DT;
     row_base = row_read_base<D>(lane);
     tr4_base = tr_read_base<D>(lane, 4 * hf);
     tr8_base = tr_read_base<D>(lane, 8 * hf);
@@ -142,13 +153,17 @@ struct BwdKernel {
     const int t = lane & 15;
     const int unit = 4 * ((lane >> 4) & 1) + (t & 3);
     ds_tr_base = (uint32_t)((8 * hf + (t >> 2)) * (BQ * 2) + ((unit ^ (2 * hf)) << 3));
-    dq_lane_off = (uint32_t)(((4 * hf) * a.heads * D + 32 * wave + c32) * 4);
+    dq_lane_off = (uint32_t)(((4 * hf) * a.heads * D + 32 * dq_dt + c32) * 4);
   }
 
   __device__ __forceinline__ char* qbuf(int b) { return smem + OFF_Q + b * QT_BYTES; }
   __device__ __forceinline__ char* gbuf(int b) { return smem + OFF_DO + b * QT_BYTES; }
   __device__ __forceinline__ float* rowbuf(int b) {
     return reinterpret_cast<float*>(smem + OFF_ROW) + b * 2 * 64;
+  }
+  // partial of key part p, d tile dt: 32 x 32 fp32 in MFMA C layout
+  __device__ __forceinline__ float* dq_partial(int p, int dt) {
+    return reinterpret_cast<float*>(smem + OFF_DQP) + (p * DT + dt) * 32 * 32;
   }
 
   // Issues the direct LDS loads of query block [qi0, qi0 + BQ): Q and dO rows, and
@@ -160,9 +175,9 @@ struct BwdKernel {
     const uint32_t bytes = (uint32_t)(rows * rs * 2);
     const bf16* qsrc = a.q + ((BCAST ? 0 : kv0) + qi0) * rs + (int64_t)h * D;
     const bf16* gsrc = a.d_o + (grow0 + qi0) * rs + (int64_t)h * D;
-    lds_load_tile<D, kBwdWaves>(qbuf(buf), BQ, wave, lane, make_rsrc_sgpr(qsrc, bytes), row_bytes);
-    lds_load_tile<D, kBwdWaves>(gbuf(buf), BQ, wave, lane, make_rsrc_sgpr(gsrc, bytes), row_bytes);
-    if (wave == kBwdWaves - 1) {
+    lds_load_tile<D, NW>(qbuf(buf), BQ, wave, lane, make_rsrc_sgpr(qsrc, bytes), row_bytes);
+    lds_load_tile<D, NW>(gbuf(buf), BQ, wave, lane, make_rsrc_sgpr(gsrc, bytes), row_bytes);
+    if (wave == NW - 1) {
       const int64_t r0 = (int64_t)h * a.rows + grow0 + qi0;
       const uint32_t rb = (uint32_t)(rows * 4);
       lds_load4(make_rsrc_sgpr(a.lse + r0, rb), (uint32_t)lane * 4u, reinterpret_cast<char*>(rowbuf(buf)));
@@ -170,67 +185,89 @@ struct BwdKernel {
     }
   }
 
-  template <bool MASKED>
+  // S, dP, P, dS for this wave's 32 keys, dS^T -> LDS and dV^T / dK^T accumulation.
+  // With MID_BAR the barrier that retires the previous block's dS^T readers comes
+  // last, right before the dS^T write (every wave reaches it, active or not);
+  // otherwise the caller has passed it.
+  template <bool MASKED, bool MID_BAR>
   __device__ __forceinline__ void qblock(int buf, int64_t qi0) {
     const char* kt = smem + OFF_K;
     const char* qt = qbuf(buf);
     const char* gt = gbuf(buf);
-    const float* lse2 = rowbuf(buf);   // natural-log LSE
+    const float* lse = rowbuf(buf);   // natural-log LSE
     const float* dl = rowbuf(buf) + 64;
     char* dst = smem + OFF_DS;
-
-    // S = Q K^T and dP = dO V^T for this wave's 32 keys (C: m = query i, n = key j)
-    // Operands are read one step ahead of their MFMAs; the scheduling fences keep
-    // the compiler from hoisting every read of the unrolled loop (which would push
-    // the live registers past the 256 that two waves per SIMD allow).
-    const uint32_t rb = launder(row_base);
-    const char* kw = kt + 32 * wave * 2 * D;   // this wave's 32 keys
-    f32x16 s = zero16(), dp = zero16();
-    bf16x8 qa = lds_read8(qt, row_read_addr(rb, 0));
-    bf16x8 kb = lds_read8(kw, row_read_addr(rb, 0));
-    bf16x8 ga = lds_read8(gt, row_read_addr(rb, 0));
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 qa_n = qa, kb_n = kb, ga_n = ga;
-      if (ks + 1 < KS) {
-        qa_n = lds_read8(qt, row_read_addr(rb, ks + 1));
-        kb_n = lds_read8(kw, row_read_addr(rb, ks + 1));
-        ga_n = lds_read8(gt, row_read_addr(rb, ks + 1));
-      }
-      s = mfma32(qa, kb, s);
-      dp = mfma32(ga, vf[ks], dp);
-      qa = qa_n;
-      kb = kb_n;
-      ga = ga_n;
-      __builtin_amdgcn_sched_barrier(0);
+    if (!active) {
+      if constexpr (MID_BAR) __syncthreads();
+      return;
     }
-    // P = exp2(S c log2e - LSE log2e); dS = P (dP - delta)
     bf16x8 pb[2], sb[2];
+    {
+      // S = Q K^T and dP = dO V^T for this wave's 32 keys (C: m = query i, n = key j).
+      // Operands are read one step ahead of their MFMAs; the scheduling fences keep
+      // the compiler from hoisting every read of the unrolled loop (which would push
+      // the live registers past the 256 that two waves per SIMD allow).
+      const uint32_t rb = launder(row_base);
+      const char* kw = kt + 32 * wave * 2 * D;   // this wave's 32 keys
+      f32x16 s = zero16(), dp = zero16();
+      bf16x8 qa = lds_read8(qt, row_read_addr(rb, 0));
+      bf16x8 kb = lds_read8(kw, row_read_addr(rb, 0));
+      bf16x8 ga = lds_read8(gt, row_read_addr(rb, 0));
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + 8 * q4 + 4 * hf);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + 8 * q4 + 4 * hf);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * q4 + e;
-        float p = fast_exp2(fmaf(s[r], a.scale_log2, -l4[e] * kLog2e));
-        if constexpr (MASKED) {
-          // rows past the query end, keys past the sequence end, and (causal) keys
-          // after the query get zero probability
-          const int64_t ipos = qi0 + 8 * q4 + 4 * hf + e;
-          const int64_t jpos = j0 + 32 * wave + c32;
-          bool vis = jpos < n && ipos < q_rows;
-          if constexpr (CAUSAL) vis = vis && jpos <= ipos;
-          if (!vis) p = 0.f;
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 qa_n = qa, kb_n = kb, ga_n = ga;
+        if (ks + 1 < KS) {
+          qa_n = lds_read8(qt, row_read_addr(rb, ks + 1));
+          kb_n = lds_read8(kw, row_read_addr(rb, ks + 1));
+          ga_n = lds_read8(gt, row_read_addr(rb, ks + 1));
         }
-        const float ds = p * (dp[r] - d4[e]);
-        pb[r >> 3][r & 7] = (bf16)p;
-        sb[r >> 3][r & 7] = (bf16)ds;
+        s = mfma32(qa, kb, s);
+        dp = mfma32(ga, vf[ks], dp);
+        qa = qa_n;
+        kb = kb_n;
+        ga = ga_n;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // P = exp2(S c log2e - LSE log2e); dS = P (dP - delta)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse + 8 * q4 + 4 * hf);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + 8 * q4 + 4 * hf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q4 + e;
+          float p = fast_exp2(fmaf(s[r], a.scale_log2, -l4[e] * kLog2e));
+          if constexpr (MASKED) {
+            // rows past the query end, keys past the sequence end, and (causal) keys
+            // after the query get zero probability
+            const int64_t ipos = qi0 + 8 * q4 + 4 * hf + e;
+            const int64_t jpos = j0 + 32 * wave + c32;
+            bool vis = jpos < n && ipos < q_rows;
+            if constexpr (CAUSAL) vis = vis && jpos <= ipos;
+            if (!vis) p = 0.f;
+          }
+          const float ds = p * (dp[r] - d4[e]);
+          pb[r >> 3][r & 7] = (bf16)p;
+          sb[r >> 3][r & 7] = (bf16)ds;
+        }
       }
     }
-    // dV^T += dO^T P and dK^T += Q^T dS (C: m = d, n = key j); query rows
-    // 16 kc + 4 (lane / 32) + e and + 8 pair with the P / dS registers
+    // publish dS^T [key][query] (bf16)
+    auto publish_ds = [&]() {
+      const int j = 32 * wave + c32;
+      const int sw = (j >> 2) & 7;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = sb[q4 >> 1][4 * (q4 & 1) + e];
+        *reinterpret_cast<bf16x4*>(dst + j * (BQ * 2) + (((2 * q4 + hf) ^ sw) << 3)) = w;
+      }
+    };
+    if constexpr (!MID_BAR) publish_ds();
     {
+      // dV^T += dO^T P and dK^T += Q^T dS (C: m = d, n = key j); query rows
+      // 16 kc + 4 (lane / 32) + e and + 8 pair with the P / dS registers
       const uint32_t tb = launder(tr4_base);
       bf16x8 g_op = lds_operand_tr<D>(gt, tb, 0, 8, 0);
       bf16x8 q_op = lds_operand_tr<D>(qt, tb, 0, 8, 0);
@@ -250,57 +287,71 @@ struct BwdKernel {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // publish dS^T [key][query] (bf16) once the previous block's dQ reads are done
-    __syncthreads();
-    {
-      const int j = 32 * wave + c32;
-      const int sw = (j >> 2) & 7;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = sb[q4 >> 1][4 * (q4 & 1) + e];
-        *reinterpret_cast<bf16x4*>(dst + j * (BQ * 2) + (((2 * q4 + hf) ^ sw) << 3)) = w;
-      }
+    if constexpr (MID_BAR) {
+      __syncthreads();   // the previous block's dS^T readers are done
+      publish_ds();
     }
   }
 
-  // dQ_block[:, 32w .. 32w+31] = dS K over the tile's 128 keys, reduce-added into
-  // the fp32 accumulator with buffer atomics (rows past the query end fall outside
-  // the buffer range and are dropped by the hardware).
-  __device__ __forceinline__ void dq_block(int64_t qi0) {
-    if (wave >= DT) return;
+  // dQ partial of the block whose dS^T is in LDS: this wave's 32-column slice
+  // (d tile dq_dt) over the keys of its part.
+  __device__ __forceinline__ f32x16 dq_compute() {
     const char* kt = smem + OFF_K;
     const char* dst = smem + OFF_DS;
     const uint32_t dsb = launder(ds_tr_base);
     const uint32_t kb8 = launder(tr8_base);
-    // two independent accumulators halve the dependent-MFMA chain
-    f32x16 dq = zero16(), dq2 = zero16();
+    const int k_lo = dq_part * KPART;
+    const int k_hi = min(k_lo + KPART, (nvalid + 31) & ~31);   // keys of inactive waves are skipped
+    f32x16 acc0 = zero16(), acc1 = zero16();
     auto ds_op = [&](int jb) {   // dS[query l % 32][keys jb + 8 (l / 32) + e]
       const uint32_t x = (uint32_t)(((jb >> 2) & 4) << 3);
       return cat(lds_read_tr(dst + ((dsb ^ x) + jb * (BQ * 2))),
                  lds_read_tr(dst + ((dsb ^ x ^ 8u) + (jb + 4) * (BQ * 2))));
     };
-    bf16x8 sa = ds_op(0);
-    bf16x8 kb = lds_operand_tr<D>(kt, kb8, 0, 4, wave);
+    if (k_lo < k_hi) {
+      bf16x8 sa = ds_op(k_lo);
+      bf16x8 kb = lds_operand_tr<D>(kt, kb8, k_lo, k_lo + 4, dq_dt);
+      // Static trip count with an early exit: the accumulator each step feeds must be
+      // known at compile time (a runtime-selected accumulator gave wrong results).
 #pragma unroll
-    for (int jb = 0; jb < BN; jb += 16) {
-      bf16x8 sa_n = sa, kb_n = kb;
-      if (jb + 16 < BN) {
-        sa_n = ds_op(jb + 16);
-        kb_n = lds_operand_tr<D>(kt, kb8, jb + 16, jb + 20, wave);
+      for (int jj = 0; jj < KPART; jj += 16) {
+        const int jb = k_lo + jj;
+        if (jb >= k_hi) break;
+        bf16x8 sa_n = sa, kb_n = kb;
+        if (jb + 16 < k_hi) {
+          sa_n = ds_op(jb + 16);
+          kb_n = lds_operand_tr<D>(kt, kb8, jb + 16, jb + 20, dq_dt);
+        }
+        if ((jj / 16) & 1) {
+          acc1 = mfma32(sa, kb, acc1);
+        } else {
+          acc0 = mfma32(sa, kb, acc0);
+        }
+        sa = sa_n;
+        kb = kb_n;
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if ((jb / 16) & 1) {
-        dq2 = mfma32(sa, kb, dq2);
-      } else {
-        dq = mfma32(sa, kb, dq);
-      }
-      sa = sa_n;
-      kb = kb_n;
-      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dq[r] += dq2[r];
+    for (int r = 0; r < 16; ++r) acc0[r] += acc1[r];
+    return acc0;
+  }
+
+  // Several key parts: every part publishes its partial to LDS (summed by dq_flush
+  // after the next barrier).
+  __device__ __forceinline__ void dq_publish(const f32x16& acc) {
+    float* dstp = dq_partial(dq_part, dq_dt);
+#pragma unroll
+    for (int r = 0; r < 16; r += 4) {
+      const f32x4 v4 = {acc[r], acc[r + 1], acc[r + 2], acc[r + 3]};
+      *reinterpret_cast<f32x4*>(dstp + (r / 4) * 256 + lane * 4) = v4;
+    }
+  }
+
+  // Reduce-add of a block's dQ slice into the fp32 accumulator with buffer atomics
+  // (rows past the query end fall outside the buffer range and are dropped by the
+  // hardware).
+  __device__ __forceinline__ void dq_atomics(const f32x16& dq, int64_t qi0) {
     const int64_t rows = min((int64_t)q_rows - qi0, (int64_t)BQ);
     const int64_t qrow0 = BCAST ? (int64_t)(blockIdx.x & (kDqStripes - 1)) * a.q_len + qi0 : kv0 + qi0;
     const rsrc_t acc = make_rsrc(a.dq_acc + (qrow0 * a.heads + h) * D, (uint32_t)(rows * a.heads * D * 4));
@@ -313,18 +364,48 @@ struct BwdKernel {
     }
   }
 
-  // Query-block loop.  Iteration t issues the LDS loads of block t + 1, then the
-  // dQ reduce-adds of block t - 1, then block t.  Vector memory operations retire in
-  // issue order, so the wait before the barrier (for the loads) leaves the 16
+  // After a barrier: part-0 waves sum the parts' partials and reduce-add them.
+  __device__ __forceinline__ void dq_flush(int64_t qi0) {
+    if (dq_part != 0) return;
+    f32x16 dq = zero16();
+#pragma unroll
+    for (int p = 0; p < KP; ++p) {
+      const float* srcp = dq_partial(p, dq_dt);
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        const f32x4 v4 = *reinterpret_cast<const f32x4*>(srcp + (r / 4) * 256 + lane * 4);
+        dq[r] += v4[0];
+        dq[r + 1] += v4[1];
+        dq[r + 2] += v4[2];
+        dq[r + 3] += v4[3];
+      }
+    }
+    dq_atomics(dq, qi0);
+  }
+
+  // Query-block loop.  Iteration t issues the LDS loads of block t + 1, computes the
+  // dQ partial of block t - 1 (its dS^T is still in LDS), then block t.  With one key
+  // part a wave reduce-adds its partial at once and the barrier that retires the
+  // readers of dS^T(t - 1) sits inside block t, before its dS^T write; with
+  // several, the partials are published to LDS, a barrier follows, and part 0 sums
+  // and reduce-adds them before block t.  Vector memory operations retire in issue
+  // order, so the wait before the closing barrier (for the loads) leaves the 16
   // reduce-adds issued after them in flight.
   template <bool MASKED>
   __device__ __forceinline__ void run(int64_t qs, int64_t qe, int64_t q_last, int64_t& pending) {
     for (int64_t qi0 = qs; qi0 < qe; qi0 += BQ) {
       const int buf = (int)((qi0 / BQ) & 1);
       if (qi0 + BQ < q_last) load_qblock(qi0 + BQ, buf ^ 1);   // one block ahead
-      if (pending >= 0) dq_block(pending);
-      qblock<MASKED>(buf, qi0);
-      if (pending >= 0 && wave < DT) {
+      if constexpr (KP == 1) {
+        if (pending >= 0) dq_atomics(dq_compute(), pending);
+        qblock<MASKED, true>(buf, qi0);
+      } else {
+        if (pending >= 0) dq_publish(dq_compute());
+        __syncthreads();
+        if (pending >= 0) dq_flush(pending);
+        qblock<MASKED, false>(buf, qi0);
+      }
+      if (pending >= 0 && dq_part == 0) {
         wait_lds_loads_but_16();
       } else {
         wait_lds_loads();
@@ -339,6 +420,8 @@ struct BwdKernel {
     kv0 = load_offset(a.offsets, a.off64, b);
     n = load_offset(a.offsets, a.off64, b + 1) - kv0;
     j0 = (int64_t)jblk * BN;
+    nvalid = (int)min(n - j0, (int64_t)BN);
+    active = 32 * wave < nvalid;
     q_rows = BCAST ? a.q_len : (int)n;
     grow0 = BCAST ? (int64_t)b * a.q_len : kv0;
 
@@ -346,10 +429,9 @@ struct BwdKernel {
     // K tile -> LDS (rows past the end read as zeros and are masked); this wave's
     // V fragment -> registers
     {
-      const int64_t rows = min(n - j0, (int64_t)BN);
-      lds_load_tile<D, kBwdWaves>(smem + OFF_K, BN, wave, lane,
-                                  make_rsrc_sgpr(a.k + (kv0 + j0) * rs + (int64_t)h * D, (uint32_t)(rows * rs * 2)),
-                                  (uint32_t)(rs * 2));
+      lds_load_tile<D, NW>(smem + OFF_K, BN, wave, lane,
+                           make_rsrc_sgpr(a.k + (kv0 + j0) * rs + (int64_t)h * D, (uint32_t)(nvalid * rs * 2)),
+                           (uint32_t)(rs * 2));
       const int64_t j = j0 + 32 * wave + c32;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
@@ -376,11 +458,19 @@ struct BwdKernel {
     if constexpr (CAUSAL) qm = min(q_last, ((j0 + BN - 1 + BQ - 1) / BQ) * BQ);
     if (kv_tail) qm = q_last;
     const int64_t qfull = max(qm, (q_last / BQ) * BQ);
-    int64_t pending = -1;   // query block whose dQ reduce-add is still to be issued
+    int64_t pending = -1;   // query block whose dQ is still to be reduced
     run<true>(qs, qm, q_last, pending);
     run<false>(qm, qfull, q_last, pending);
     run<true>(qfull, q_last, q_last, pending);
-    if (pending >= 0) dq_block(pending);
+    if (pending >= 0) {
+      if constexpr (KP == 1) {
+        dq_atomics(dq_compute(), pending);
+      } else {
+        dq_publish(dq_compute());
+        __syncthreads();
+        dq_flush(pending);
+      }
+    }
 
     // dK = c dS^T Q and dV -> bf16
     const int64_t j = j0 + 32 * wave + c32;
@@ -405,10 +495,10 @@ struct BwdKernel {
   }
 };
 
-template <int D, bool BCAST, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+template <int D, int NW, bool BCAST, bool CAUSAL>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_kernel(BwdArgs a) {
-  using K = BwdKernel<D, BCAST, CAUSAL>;
+  using K = BwdKernel<D, NW, BCAST, CAUSAL>;
   __shared__ __attribute__((aligned(16))) char smem[K::SMEM];
   __shared__ int claimed;
   K kern(a, smem);
@@ -458,25 +548,43 @@ __global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restric
   reinterpret_cast<bf16x4*>(dq)[i] = o;
 }
 
-template <int D, bool BCAST, bool CAUSAL>
+template <int D, int NW, bool BCAST, bool CAUSAL>
 hipError_t launch_bwd_inst(const BwdArgs& a, hipStream_t s, int64_t max_tiles) {
-  const void* fn = reinterpret_cast<const void*>(&bwd_kernel<D, BCAST, CAUSAL>);
-  const int grid = persistent_grid(fn, 256, max_tiles);
-  hipLaunchKernelGGL((bwd_kernel<D, BCAST, CAUSAL>), dim3(grid), dim3(256), 0, s, a);
+  const void* fn = reinterpret_cast<const void*>(&bwd_kernel<D, NW, BCAST, CAUSAL>);
+  const int grid = persistent_grid(fn, 64 * NW, max_tiles);
+  hipLaunchKernelGGL((bwd_kernel<D, NW, BCAST, CAUSAL>), dim3(grid), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
+}
+
+template <int D, int NW>
+hipError_t launch_bwd_dw(const Problem& p, const BwdArgs& a, hipStream_t s) {
+  const int64_t max_tiles = bwd_max_items(p) * p.heads;
+  if (p.broadcast) return launch_bwd_inst<D, NW, true, false>(a, s, max_tiles);
+  if (p.causal) return launch_bwd_inst<D, NW, false, true>(a, s, max_tiles);
+  return launch_bwd_inst<D, NW, false, false>(a, s, max_tiles);
 }
 
 template <int D>
 hipError_t launch_bwd_d(const Problem& p, const BwdArgs& a, hipStream_t s) {
-  const int64_t max_tiles = bwd_max_items(p) * p.heads;
-  if (p.broadcast) return launch_bwd_inst<D, true, false>(a, s, max_tiles);
-  if (p.causal) return launch_bwd_inst<D, false, true>(a, s, max_tiles);
-  return launch_bwd_inst<D, false, false>(a, s, max_tiles);
+  return bwd_waves(p) == 8 ? launch_bwd_dw<D, 8>(p, a, s) : launch_bwd_dw<D, 4>(p, a, s);
 }
 
 }  // namespace
 
-int64_t bwd_max_items(const Problem& p) { return (p.total_kv + kBwdBN - 1) / kBwdBN + p.batch; }
+// Eight waves (256-key tiles) halve the dQ reduce-adds per key.  In broadcast mode
+// every tile adds into the one shared dQ, so that always pays; in self mode it pays
+// when a tile's query loop is long, and four waves (128-key tiles) waste less on
+// short sequences.
+int bwd_waves(const Problem& p) {
+  if (p.broadcast) return 8;
+  const int64_t mean_len = p.batch > 0 ? p.total_kv / p.batch : 0;
+  return mean_len >= 512 ? 8 : 4;
+}
+
+int64_t bwd_max_items(const Problem& p) {
+  const int bn = 32 * bwd_waves(p);
+  return (p.total_kv + bn - 1) / bn + p.batch;
+}
 
 hipError_t launch_bwd_pre(const Problem& p, const void* o, const void* d_o, float* delta,
                           float* dq_acc, int64_t dq_acc_elems, hipStream_t s) {

@@ -77,7 +77,7 @@ struct FwdKernel {
 
   __device__ FwdKernel(const FwdArgs& args, char* sm) : a(args), smem(sm) {
     lane = threadIdx.x & 63;
-    wave = threadIdx.x >> 6;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
     c32 = lane & 31;
     hf = lane >> 5;
     rs = (int64_t)a.heads * D;

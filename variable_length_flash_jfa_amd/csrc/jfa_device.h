@@ -229,13 +229,15 @@ __device__ __forceinline__ void lds_load_tile(char* tile, int nrows, int wave, i
                                               uint32_t row_bytes) {
   constexpr int CH = D / 8;
   constexpr int RPI = 64 / CH;
-  const int per_wave = nrows / RPI / NW;
+  const int ninstr = nrows / RPI;
 #pragma unroll
-  for (int k = 0; k < per_wave; ++k) {
+  for (int k = 0; k < (ninstr + NW - 1) / NW; ++k) {
     const int u = wave + k * NW;
-    const int row = u * RPI + lane / CH;
-    const int chunk = swz_chunk<D>(row, lane % CH);
-    lds_load16(r, (uint32_t)row * row_bytes + (uint32_t)chunk * 16u, tile + u * 1024);
+    if (u < ninstr) {
+      const int row = u * RPI + lane / CH;
+      const int chunk = swz_chunk<D>(row, lane % CH);
+      lds_load16(r, (uint32_t)row * row_bytes + (uint32_t)chunk * 16u, tile + u * 1024);
+    }
   }
 }
 

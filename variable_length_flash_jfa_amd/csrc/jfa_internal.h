@@ -10,11 +10,9 @@ namespace jfa {
 // Forward tile geometry.  A forward tile is (sequence, block of BM query rows, head);
 // every wave owns 32 query rows and K/V stream through LDS in blocks of kFwdBN keys.
 constexpr int kFwdBN = 64;
-// Backward tile geometry: a tile is (sequence, block of kBwdBN keys, head); four
-// waves own 32 keys each and stream the query rows in blocks of kBwdBQ.
-constexpr int kBwdBN = 128;
+// Backward tile geometry: a tile is (sequence, block of 32 * bwd_waves(p) keys,
+// head); every wave owns 32 keys and the query rows stream in blocks of kBwdBQ.
 constexpr int kBwdBQ = 32;
-constexpr int kBwdWaves = 4;
 // Broadcast-mode dQ accumulates into one fp32 stripe per XCD.
 constexpr int kDqStripes = 8;
 
@@ -46,6 +44,7 @@ struct Plan {
 int fwd_waves(const Problem& p);                 // waves per forward workgroup
 int64_t fwd_max_items(const Problem& p);         // capacity of the forward item list
 int64_t bwd_max_items(const Problem& p);         // capacity of the backward item list
+int bwd_waves(const Problem& p);                 // waves per backward workgroup (4 or 8)
 
 hipError_t launch_plan_fwd(const Problem& p, const Plan& plan, int sched, hipStream_t s);
 hipError_t launch_fwd(const Problem& p, const Plan& plan, int sched, void* o, float* lse,

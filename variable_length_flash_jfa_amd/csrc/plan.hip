@@ -194,6 +194,7 @@ struct PlanBwdArgs {
   int off64;
   int batch;
   int heads;
+  int bn;          // keys per backward tile
   int2* items;
   int* meta;
 };
@@ -208,13 +209,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_bwd_kernel(PlanBwdArgs a) {
   int count = 0;
   for (int b = b_begin; b < b_end; ++b) {
     const int64_t n = load_offset(a.offsets, a.off64, b + 1) - load_offset(a.offsets, a.off64, b);
-    count += (int)((n + kBwdBN - 1) / kBwdBN);
+    count += (int)((n + a.bn - 1) / a.bn);
   }
   int total = 0;
   int pos = block_exclusive_scan(count, wave_sums, &total);
   for (int b = b_begin; b < b_end; ++b) {
     const int64_t n = load_offset(a.offsets, a.off64, b + 1) - load_offset(a.offsets, a.off64, b);
-    const int nb = (int)((n + kBwdBN - 1) / kBwdBN);
+    const int nb = (int)((n + a.bn - 1) / a.bn);
     for (int j = 0; j < nb; ++j) a.items[pos++] = make_int2(b, j);
   }
   if (tid == 0) {
@@ -249,6 +250,7 @@ hipError_t launch_plan_bwd(const Problem& p, const Plan& plan, int /*sched*/, hi
   a.off64 = p.off64;
   a.batch = p.batch;
   a.heads = p.heads;
+  a.bn = 32 * bwd_waves(p);
   a.items = plan.items;
   a.meta = plan.meta;
   hipLaunchKernelGGL(plan_bwd_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
