@@ -36,6 +36,37 @@ int check() {
       }
     }
   }
+  // lds_load_tile: lane offset (base ^ mask(u RPI) << 4) + u RPI row_bytes equals
+  // row * row_bytes + swz_chunk(row, slot) * 16 for row = u RPI + lane / CH
+  {
+    constexpr int CH = D / 8, RPI = 64 / CH;
+    for (uint32_t row_bytes : {2u * D, 4u * D, 8u * D, 64u * D})
+      for (int lane = 0; lane < 64; ++lane) {
+        const uint32_t r0 = lane / CH;
+        const uint32_t base = r0 * row_bytes + (((uint32_t)(lane % CH) ^ (uint32_t)swz_mask<D>((int)r0)) << 4);
+        for (int u = 0; u < 64; ++u) {
+          const uint32_t fast = (base ^ ((uint32_t)swz_mask<D>(u * RPI) << 4)) + (uint32_t)(u * RPI) * row_bytes;
+          const int row = u * RPI + lane / CH;
+          const uint32_t ref = (uint32_t)row * row_bytes + (uint32_t)swz_chunk<D>(row, lane % CH) * 16u;
+          if (fast != ref) ++bad;
+        }
+      }
+  }
+  // store_acc_rows read-back: (loff ^ ((RPI i mod CH) << 4)) + RPI i 2D addresses
+  // row RPI i + lane / CH, chunk lane % CH of the slot swizzled by (row mod CH)
+  {
+    constexpr int CH = D / 8, RPI = 64 / CH;
+    for (int lane = 0; lane < 64; ++lane) {
+      const uint32_t c = lane % CH, r0 = lane / CH;
+      const uint32_t loff = r0 * (2 * D) + ((c ^ r0) << 4);
+      for (int i = 0; i < 32 / RPI; ++i) {
+        const uint32_t fast = (loff ^ (uint32_t)(((RPI * i) & (CH - 1)) << 4)) + (uint32_t)(RPI * i * 2 * D);
+        const uint32_t row = RPI * i + r0;
+        const uint32_t ref = row * (2 * D) + ((c ^ (row & (CH - 1))) << 4);
+        if (fast != ref) ++bad;
+      }
+    }
+  }
   // the swizzle is a permutation of the 16-byte chunks of every row
   for (int row = 0; row < 64; ++row) {
     unsigned seen = 0;

@@ -95,7 +95,7 @@ size_t fwd_ws_bytes(const jfa::Problem& p) {
 size_t bwd_ws_bytes(const jfa::Problem& p) {
   const int64_t q_rows = p.broadcast ? (int64_t)p.q_len * jfa::kDqStripes : p.total_kv;
   return kAlign + align_up(64) + align_up((size_t)jfa::bwd_max_items(p) * sizeof(int2)) +
-         align_up((size_t)p.heads * p.rows * sizeof(float)) +
+         align_up((size_t)p.heads * p.rows * 2 * sizeof(float)) +
          align_up((size_t)q_rows * p.heads * p.head_dim * sizeof(float));
 }
 
@@ -280,21 +280,21 @@ jfa_status_t jfa_bwd(const void* q, const void* k, const void* v, const void* of
   plan.meta = reinterpret_cast<int*>(carve(cur, 64));
   plan.max_items = jfa::bwd_max_items(p);
   plan.items = reinterpret_cast<int2*>(carve(cur, plan.max_items * sizeof(int2)));
-  float* delta = reinterpret_cast<float*>(carve(cur, (size_t)p.heads * p.rows * sizeof(float)));
+  float* rowstat = reinterpret_cast<float*>(carve(cur, (size_t)p.heads * p.rows * 2 * sizeof(float)));
   const int64_t q_rows = p.broadcast ? (int64_t)p.q_len * jfa::kDqStripes : p.total_kv;
   const int64_t acc_elems = q_rows * p.heads * p.head_dim;
   float* dq_acc = reinterpret_cast<float*>(carve(cur, (size_t)acc_elems * sizeof(float)));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int sched = g_schedule.load();
   hipError_t e = timed_launch("bwd_pre", s, [&] {
-    return jfa::launch_bwd_pre(p, o, d_o, delta, dq_acc, acc_elems, s);
+    return jfa::launch_bwd_pre(p, o, d_o, lse, rowstat, dq_acc, acc_elems, s);
   });
   if (e != hipSuccess) return hip_fail(e, "jfa_bwd: delta launch");
   if (p.total_kv > 0) {
     e = timed_launch("plan_bwd", s, [&] { return jfa::launch_plan_bwd(p, plan, sched, s); });
     if (e != hipSuccess) return hip_fail(e, "jfa_bwd: plan launch");
     e = timed_launch("bwd", s, [&] {
-      return jfa::launch_bwd(p, plan, sched, lse, d_o, delta, dq_acc, dk, dv, s);
+      return jfa::launch_bwd(p, plan, sched, rowstat, d_o, dq_acc, dk, dv, s);
     });
     if (e != hipSuccess) return hip_fail(e, "jfa_bwd: kernel launch");
   }

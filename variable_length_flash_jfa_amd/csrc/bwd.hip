@@ -34,32 +34,38 @@ namespace jfa {
 namespace {
 
 // ---------------------------------------------------------------------------
-// 1. delta = rowsum(dO * O) and dQ accumulator zeroing
+// 1. per-row statistics (LSE log2e, delta = rowsum(dO * O)) and dQ accumulator
+//    zeroing
 // ---------------------------------------------------------------------------
+// rowstat[(h rows + row) 2 + 0] = LSE[h][row] log2(e) (so that P = exp2(S c log2 e -
+// that) needs no multiply per score), rowstat[... + 1] = delta[h][row]; one 8-byte
+// pair per row lets a single direct load bring both values of 32 rows into LDS.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o,
                                                        const bf16* __restrict__ d_o,
-                                                       float* __restrict__ delta, int64_t rows,
+                                                       const float* __restrict__ lse,
+                                                       float2* __restrict__ rowstat, int64_t rows,
                                                        int heads, float* __restrict__ dq_acc,
                                                        int64_t acc_vec4) {
-  constexpr int TPR = D / 8;                 // threads per (row, head)
-  const int64_t pair = ((int64_t)blockIdx.x * 256 + threadIdx.x) / TPR;
+  constexpr int TPR = D / 8;                 // threads per (head, row)
+  const int64_t pair = ((int64_t)blockIdx.x * 256 + threadIdx.x) / TPR;   // h * rows + row
   const int part = threadIdx.x % TPR;
   const int64_t npairs = rows * heads;
   float s = 0.f;
+  int64_t row = 0;
+  int h = 0;
   if (pair < npairs) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + pair * D + part * 8);
-    const bf16x8 b = *reinterpret_cast<const bf16x8*>(d_o + pair * D + part * 8);
+    h = (int)(pair / rows);
+    row = pair - (int64_t)h * rows;
+    const int64_t off = (row * heads + h) * D + part * 8;
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(o + off);
+    const bf16x8 y = *reinterpret_cast<const bf16x8*>(d_o + off);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s += (float)a[e] * (float)b[e];
+    for (int e = 0; e < 8; ++e) s += (float)x[e] * (float)y[e];
   }
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
-  if (pair < npairs && part == 0) {
-    const int64_t row = pair / heads;
-    const int h = (int)(pair % heads);
-    delta[(int64_t)h * rows + row] = s;
-  }
+  if (pair < npairs && part == 0) rowstat[pair] = make_float2(lse[pair] * kLog2e, s);
   // grid-stride zero fill of the dQ accumulator
   const int64_t nthreads = (int64_t)gridDim.x * 256;
   float4* acc = reinterpret_cast<float4*>(dq_acc);
@@ -75,8 +81,7 @@ struct BwdArgs {
   const bf16* k;
   const bf16* v;
   const bf16* d_o;
-  const float* lse;
-  const float* delta;
+  const float2* rowstat;
   const void* offsets;
   int off64;
   int heads;
@@ -92,6 +97,12 @@ struct BwdArgs {
   int sched;
 };
 
+// LDS offsets below are byte offsets from the start of the kernel's LDS block.  A
+// lane's part of every access pattern lives in one VGPR; runtime tile offsets
+// (buffer parity, wave, key part) are multiples of 256 (128 for D = 64) and are
+// added to that VGPR once, which commutes with the per-read XOR of the swizzle
+// (the XOR only touches the low 8 (7) bits).  Each read then costs at most one
+// XOR and its constant part rides in the instruction's offset field.
 template <int D, int NW, bool BCAST, bool CAUSAL>
 struct BwdKernel {
   static constexpr int BN = 32 * NW;         // keys per tile (NW waves x 32)
@@ -105,15 +116,22 @@ struct BwdKernel {
   static constexpr int QT_BYTES = BQ * D * 2;
   static constexpr int DS_BYTES = BN * BQ * 2;
   static constexpr int DQP_BYTES = KP > 1 ? KP * DT * 32 * 32 * 4 : 0;
+  static constexpr int ROW_BYTES = BQ * 8;   // (LSE log2 e, delta) per query row
   // LDS map
   static constexpr int OFF_K = 0;
   static constexpr int OFF_Q = OFF_K + KT_BYTES;              // 2 buffers
   static constexpr int OFF_DO = OFF_Q + 2 * QT_BYTES;         // 2 buffers
   static constexpr int OFF_DS = OFF_DO + 2 * QT_BYTES;
-  static constexpr int OFF_DQP = OFF_DS + DS_BYTES;           // dQ partials of the KP key parts
-  static constexpr int OFF_ROW = OFF_DQP + DQP_BYTES;         // [2][lse, delta][64] fp32
-  static constexpr int SMEM = OFF_ROW + 2 * 2 * 64 * 4;
+  static constexpr int OFF_DQP = OFF_DS + DS_BYTES;           // dQ partials of the key parts
+  static constexpr int OFF_ROW = OFF_DQP + DQP_BYTES;         // 2 buffers
+  static constexpr int SMEM = OFF_ROW + 2 * ROW_BYTES;
+  static constexpr uint32_t GQ = OFF_DO - OFF_Q;              // dO tile minus Q tile, same buffer
+  static constexpr int XB = D == 128 ? 256 : 128;             // the XOR-free granule
   static_assert(BN == 32 * NW && KP * DT == NW && KPART % 16 == 0, "tile shape");
+  static_assert(NW * 32 * 2 * D <= KT_BYTES, "epilogue slots must fit in the K tile region");
+  static_assert(OFF_Q % XB == 0 && QT_BYTES % XB == 0 && GQ % XB == 0 && (KPART * 2 * D) % XB == 0 &&
+                    (32 * 2 * D) % XB == 0 && OFF_DS % 64 == 0 && (KPART * BQ * 2) % 64 == 0,
+                "tile offsets must commute with the swizzle XOR");
 
   BwdArgs a;
   char* smem;
@@ -122,18 +140,21 @@ struct BwdKernel {
   int dq_dt, dq_part;    // this wave's d tile and key part in the dQ product
 
   // per tile
-  int64_t kv0, n, j0;
-  int h, q_rows;
-  int nvalid;            // keys of this tile inside the sequence (1..BN)
-  bool active;           // this wave owns at least one key inside the sequence
+  int64_t kv0;           // first K/V row of the sequence
   int64_t grow0;         // first dO / LSE row of the sequence
+  int n, j0, h, q_rows;
+  int nvalid;            // keys of this tile inside the sequence (1..BN)
+  int nparts;            // key parts holding at least one of them
+  bool active;           // this wave owns at least one key inside the sequence
   bf16x8 vf[KS];
   f32x16 dvt[DT], dkt[DT];
   // lane parts of the LDS addresses (see row_read_base / tr_read_base)
-  uint32_t row_base;     // Q, dO, K row reads
-  uint32_t tr4_base;     // Q^T, dO^T transposing reads (k offset 4 (lane / 32))
-  uint32_t tr8_base;     // K transposing reads for dQ (k offset 8 (lane / 32))
-  uint32_t ds_tr_base;   // dS^T transposing reads for dQ
+  uint32_t row_base;     // Q / dO row reads (add the tile offset)
+  uint32_t k_row_base;   // this wave's K rows
+  uint32_t tr4_base;     // Q^T / dO^T transposing reads (add the tile offset)
+  uint32_t kq_base;      // K transposing reads of this wave's dQ slice and key part
+  uint32_t dsq_base;     // dS^T transposing reads of this wave's key part
+  uint32_t dsw_base;     // dS^T writes of this lane's key row
   uint32_t dq_lane_off;  // byte offset of this lane's dQ element within a query block
 
   __device__ BwdKernel(const BwdArgs& args, char* sm) : a(args), smem(sm) {
@@ -145,43 +166,44 @@ struct BwdKernel {
     dq_dt = wave % DT;
     dq_part = wave / DT;
     row_base = row_read_base<D>(lane);
+    k_row_base = row_base + (uint32_t)(OFF_K + 32 * wave * 2 * D);
     tr4_base = tr_read_base<D>(lane, 4 * hf);
-    tr8_base = tr_read_base<D>(lane, 8 * hf);
+    kq_base = (tr_read_base<D>(lane, 8 * hf) ^ (uint32_t)((4 * dq_dt) << 4)) +
+              (uint32_t)(OFF_K + dq_part * KPART * 2 * D);
     // dS^T tile [BN keys][BQ queries] bf16, 64-byte rows of eight 8-byte units; unit u
     // of row j is stored at u ^ ((j >> 2) & 7), which keeps both the 32-row writes
     // and the 4-row transposing reads free of bank conflicts.
     const int t = lane & 15;
     const int unit = 4 * ((lane >> 4) & 1) + (t & 3);
-    ds_tr_base = (uint32_t)((8 * hf + (t >> 2)) * (BQ * 2) + ((unit ^ (2 * hf)) << 3));
+    dsq_base = (uint32_t)(OFF_DS + dq_part * KPART * (BQ * 2) + (8 * hf + (t >> 2)) * (BQ * 2) +
+                          ((unit ^ (2 * hf)) << 3));
+    const int j = 32 * wave + c32;
+    dsw_base = (uint32_t)(OFF_DS + j * (BQ * 2) + ((hf ^ ((j >> 2) & 7)) << 3));
     dq_lane_off = (uint32_t)(((4 * hf) * a.heads * D + 32 * dq_dt + c32) * 4);
   }
 
-  __device__ __forceinline__ char* qbuf(int b) { return smem + OFF_Q + b * QT_BYTES; }
-  __device__ __forceinline__ char* gbuf(int b) { return smem + OFF_DO + b * QT_BYTES; }
-  __device__ __forceinline__ float* rowbuf(int b) {
-    return reinterpret_cast<float*>(smem + OFF_ROW) + b * 2 * 64;
-  }
+  __device__ __forceinline__ char* rowbuf(int b) { return smem + OFF_ROW + b * ROW_BYTES; }
   // partial of key part p, d tile dt: 32 x 32 fp32 in MFMA C layout
   __device__ __forceinline__ float* dq_partial(int p, int dt) {
     return reinterpret_cast<float*>(smem + OFF_DQP) + (p * DT + dt) * 32 * 32;
   }
 
   // Issues the direct LDS loads of query block [qi0, qi0 + BQ): Q and dO rows, and
-  // the LSE / delta values of those rows.  Rows past the end read as zeros; the
+  // the (LSE, delta) pairs of those rows.  Rows past the end read as zeros; the
   // masked path gives them zero weight.
-  __device__ __forceinline__ void load_qblock(int64_t qi0, int buf) {
-    const int64_t rows = min((int64_t)q_rows - qi0, (int64_t)BQ);
+  __device__ __forceinline__ void load_qblock(int qi0, int buf) {
+    const int rows = min(q_rows - qi0, BQ);
     const uint32_t row_bytes = (uint32_t)(rs * 2);
-    const uint32_t bytes = (uint32_t)(rows * rs * 2);
+    const uint32_t bytes = (uint32_t)rows * row_bytes;
     const bf16* qsrc = a.q + ((BCAST ? 0 : kv0) + qi0) * rs + (int64_t)h * D;
     const bf16* gsrc = a.d_o + (grow0 + qi0) * rs + (int64_t)h * D;
-    lds_load_tile<D, NW>(qbuf(buf), BQ, wave, lane, make_rsrc_sgpr(qsrc, bytes), row_bytes);
-    lds_load_tile<D, NW>(gbuf(buf), BQ, wave, lane, make_rsrc_sgpr(gsrc, bytes), row_bytes);
+    lds_load_tile<D, NW>(smem + OFF_Q + buf * QT_BYTES, BQ, wave, lane, make_rsrc_sgpr(qsrc, bytes),
+                         row_bytes);
+    lds_load_tile<D, NW>(smem + OFF_DO + buf * QT_BYTES, BQ, wave, lane, make_rsrc_sgpr(gsrc, bytes),
+                         row_bytes);
     if (wave == NW - 1) {
-      const int64_t r0 = (int64_t)h * a.rows + grow0 + qi0;
-      const uint32_t rb = (uint32_t)(rows * 4);
-      lds_load4(make_rsrc_sgpr(a.lse + r0, rb), (uint32_t)lane * 4u, reinterpret_cast<char*>(rowbuf(buf)));
-      lds_load4(make_rsrc_sgpr(a.delta + r0, rb), (uint32_t)lane * 4u, reinterpret_cast<char*>(rowbuf(buf) + 64));
+      const float2* src = a.rowstat + (int64_t)h * a.rows + grow0 + qi0;
+      lds_load4(make_rsrc_sgpr(src, (uint32_t)rows * 8u), (uint32_t)lane * 4u, rowbuf(buf));
     }
   }
 
@@ -190,63 +212,63 @@ struct BwdKernel {
   // last, right before the dS^T write (every wave reaches it, active or not);
   // otherwise the caller has passed it.
   template <bool MASKED, bool MID_BAR>
-  __device__ __forceinline__ void qblock(int buf, int64_t qi0) {
-    const char* kt = smem + OFF_K;
-    const char* qt = qbuf(buf);
-    const char* gt = gbuf(buf);
-    const float* lse = rowbuf(buf);   // natural-log LSE
-    const float* dl = rowbuf(buf) + 64;
-    char* dst = smem + OFF_DS;
+  __device__ __forceinline__ void qblock(int buf, int qi0) {
     if (!active) {
       if constexpr (MID_BAR) __syncthreads();
       return;
     }
+    const uint32_t boff = (uint32_t)(buf * QT_BYTES);
     bf16x8 pb[2], sb[2];
     {
       // S = Q K^T and dP = dO V^T for this wave's 32 keys (C: m = query i, n = key j).
       // Operands are read one step ahead of their MFMAs; the scheduling fences keep
       // the compiler from hoisting every read of the unrolled loop (which would push
       // the live registers past the 256 that two waves per SIMD allow).
-      const uint32_t rb = launder(row_base);
-      const char* kw = kt + 32 * wave * 2 * D;   // this wave's 32 keys
+      const uint32_t qb = launder(row_base + (uint32_t)OFF_Q + boff);
+      const uint32_t kb = launder(k_row_base);
       f32x16 s = zero16(), dp = zero16();
-      bf16x8 qa = lds_read8(qt, row_read_addr(rb, 0));
-      bf16x8 kb = lds_read8(kw, row_read_addr(rb, 0));
-      bf16x8 ga = lds_read8(gt, row_read_addr(rb, 0));
+      bf16x8 qa = lds_read8(smem, qb);
+      bf16x8 kk = lds_read8(smem, kb);
+      bf16x8 ga = lds_read8(smem + GQ, qb);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 qa_n = qa, kb_n = kb, ga_n = ga;
+        bf16x8 qa_n = qa, kk_n = kk, ga_n = ga;
         if (ks + 1 < KS) {
-          qa_n = lds_read8(qt, row_read_addr(rb, ks + 1));
-          kb_n = lds_read8(kw, row_read_addr(rb, ks + 1));
-          ga_n = lds_read8(gt, row_read_addr(rb, ks + 1));
+          const uint32_t x = (uint32_t)((ks + 1) << 5);
+          qa_n = lds_read8(smem, qb ^ x);
+          kk_n = lds_read8(smem, kb ^ x);
+          ga_n = lds_read8(smem + GQ, qb ^ x);
         }
-        s = mfma32(qa, kb, s);
+        s = mfma32(qa, kk, s);
         dp = mfma32(ga, vf[ks], dp);
         qa = qa_n;
-        kb = kb_n;
+        kk = kk_n;
         ga = ga_n;
         __builtin_amdgcn_sched_barrier(0);
       }
-      // P = exp2(S c log2e - LSE log2e); dS = P (dP - delta)
+      // P = exp2(S c log2 e - LSE log2 e); dS = P (dP - delta)
+      const char* rowp = rowbuf(buf) + 32 * hf;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse + 8 * q4 + 4 * hf);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + 8 * q4 + 4 * hf);
+        // rows 8 q4 + 4 hf + 0..3: (lse2, delta) pairs
+        const f32x4 r01 = *reinterpret_cast<const f32x4*>(rowp + 64 * q4);
+        const f32x4 r23 = *reinterpret_cast<const f32x4*>(rowp + 64 * q4 + 16);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * q4 + e;
-          float p = fast_exp2(fmaf(s[r], a.scale_log2, -l4[e] * kLog2e));
+          const float l2 = e < 2 ? r01[2 * e] : r23[2 * (e - 2)];
+          const float dl = e < 2 ? r01[2 * e + 1] : r23[2 * (e - 2) + 1];
+          float p = fast_exp2(fmaf(s[r], a.scale_log2, -l2));
           if constexpr (MASKED) {
             // rows past the query end, keys past the sequence end, and (causal) keys
             // after the query get zero probability
-            const int64_t ipos = qi0 + 8 * q4 + 4 * hf + e;
-            const int64_t jpos = j0 + 32 * wave + c32;
+            const int ipos = qi0 + 8 * q4 + 4 * hf + e;
+            const int jpos = j0 + 32 * wave + c32;
             bool vis = jpos < n && ipos < q_rows;
             if constexpr (CAUSAL) vis = vis && jpos <= ipos;
             if (!vis) p = 0.f;
           }
-          const float ds = p * (dp[r] - d4[e]);
+          const float ds = p * (dp[r] - dl);
           pb[r >> 3][r & 7] = (bf16)p;
           sb[r >> 3][r & 7] = (bf16)ds;
         }
@@ -254,31 +276,30 @@ struct BwdKernel {
     }
     // publish dS^T [key][query] (bf16)
     auto publish_ds = [&]() {
-      const int j = 32 * wave + c32;
-      const int sw = (j >> 2) & 7;
+      const uint32_t wb = launder(dsw_base);
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         bf16x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = sb[q4 >> 1][4 * (q4 & 1) + e];
-        *reinterpret_cast<bf16x4*>(dst + j * (BQ * 2) + (((2 * q4 + hf) ^ sw) << 3)) = w;
+        *reinterpret_cast<bf16x4*>(smem + (wb ^ (uint32_t)(q4 << 4))) = w;
       }
     };
     if constexpr (!MID_BAR) publish_ds();
     {
       // dV^T += dO^T P and dK^T += Q^T dS (C: m = d, n = key j); query rows
       // 16 kc + 4 (lane / 32) + e and + 8 pair with the P / dS registers
-      const uint32_t tb = launder(tr4_base);
-      bf16x8 g_op = lds_operand_tr<D>(gt, tb, 0, 8, 0);
-      bf16x8 q_op = lds_operand_tr<D>(qt, tb, 0, 8, 0);
+      const uint32_t tb = launder(tr4_base + (uint32_t)OFF_Q + boff);
+      bf16x8 g_op = lds_operand_tr<D>(smem + GQ, tb, 0, 8, 0);
+      bf16x8 q_op = lds_operand_tr<D>(smem, tb, 0, 8, 0);
 #pragma unroll
       for (int step = 0; step < 2 * DT; ++step) {
         const int kc = step / DT, dt = step % DT;
         bf16x8 g_n = g_op, q_n = q_op;
         if (step + 1 < 2 * DT) {
           const int kc1 = (step + 1) / DT, dt1 = (step + 1) % DT;
-          g_n = lds_operand_tr<D>(gt, tb, 16 * kc1, 16 * kc1 + 8, dt1);
-          q_n = lds_operand_tr<D>(qt, tb, 16 * kc1, 16 * kc1 + 8, dt1);
+          g_n = lds_operand_tr<D>(smem + GQ, tb, 16 * kc1, 16 * kc1 + 8, dt1);
+          q_n = lds_operand_tr<D>(smem, tb, 16 * kc1, 16 * kc1 + 8, dt1);
         }
         dvt[dt] = mfma32(g_op, pb[kc], dvt[dt]);
         dkt[dt] = mfma32(q_op, sb[kc], dkt[dt]);
@@ -294,51 +315,44 @@ struct BwdKernel {
   }
 
   // dQ partial of the block whose dS^T is in LDS: this wave's 32-column slice
-  // (d tile dq_dt) over the keys of its part.
+  // (d tile dq_dt) over all keys of its part.  The rows of keys past the sequence
+  // end hold zeros (zero probability, or zeroed at the start of the tile for waves
+  // with no key inside), so the loop needs no bounds.
   __device__ __forceinline__ f32x16 dq_compute() {
-    const char* kt = smem + OFF_K;
-    const char* dst = smem + OFF_DS;
-    const uint32_t dsb = launder(ds_tr_base);
-    const uint32_t kb8 = launder(tr8_base);
-    const int k_lo = dq_part * KPART;
-    const int k_hi = min(k_lo + KPART, (nvalid + 31) & ~31);   // keys of inactive waves are skipped
+    const uint32_t dsb = launder(dsq_base);
+    const uint32_t kb8 = launder(kq_base);
     f32x16 acc0 = zero16(), acc1 = zero16();
-    auto ds_op = [&](int jb) {   // dS[query l % 32][keys jb + 8 (l / 32) + e]
-      const uint32_t x = (uint32_t)(((jb >> 2) & 4) << 3);
-      return cat(lds_read_tr(dst + ((dsb ^ x) + jb * (BQ * 2))),
-                 lds_read_tr(dst + ((dsb ^ x ^ 8u) + (jb + 4) * (BQ * 2))));
+    auto ds_op = [&](int jj) {   // dS[query l % 32][keys jj + 8 (l / 32) + e] of the part
+      const uint32_t x = (uint32_t)(((jj >> 2) & 4) << 3);
+      return cat(lds_read_tr(smem + ((dsb ^ x) + jj * (BQ * 2))),
+                 lds_read_tr(smem + ((dsb ^ x ^ 8u) + (jj + 4) * (BQ * 2))));
     };
-    if (k_lo < k_hi) {
-      bf16x8 sa = ds_op(k_lo);
-      bf16x8 kb = lds_operand_tr<D>(kt, kb8, k_lo, k_lo + 4, dq_dt);
-      // Static trip count with an early exit: the accumulator each step feeds must be
-      // known at compile time (a runtime-selected accumulator gave wrong results).
+    bf16x8 sa = ds_op(0);
+    bf16x8 kb = lds_operand_tr<D>(smem, kb8, 0, 4, 0);
 #pragma unroll
-      for (int jj = 0; jj < KPART; jj += 16) {
-        const int jb = k_lo + jj;
-        if (jb >= k_hi) break;
-        bf16x8 sa_n = sa, kb_n = kb;
-        if (jb + 16 < k_hi) {
-          sa_n = ds_op(jb + 16);
-          kb_n = lds_operand_tr<D>(kt, kb8, jb + 16, jb + 20, dq_dt);
-        }
-        if ((jj / 16) & 1) {
-          acc1 = mfma32(sa, kb, acc1);
-        } else {
-          acc0 = mfma32(sa, kb, acc0);
-        }
-        sa = sa_n;
-        kb = kb_n;
-        __builtin_amdgcn_sched_barrier(0);
+    for (int jj = 0; jj < KPART; jj += 16) {
+      bf16x8 sa_n = sa, kb_n = kb;
+      if (jj + 16 < KPART) {
+        sa_n = ds_op(jj + 16);
+        kb_n = lds_operand_tr<D>(smem, kb8, jj + 16, jj + 20, 0);
       }
+      // two independent accumulators halve the dependent-MFMA chain
+      if ((jj / 16) & 1) {
+        acc1 = mfma32(sa, kb, acc1);
+      } else {
+        acc0 = mfma32(sa, kb, acc0);
+      }
+      sa = sa_n;
+      kb = kb_n;
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc0[r] += acc1[r];
     return acc0;
   }
 
-  // Several key parts: every part publishes its partial to LDS (summed by dq_flush
-  // after the next barrier).
+  // Several key parts: every part with keys publishes its partial to LDS (summed by
+  // dq_flush after the next barrier).
   __device__ __forceinline__ void dq_publish(const f32x16& acc) {
     float* dstp = dq_partial(dq_part, dq_dt);
 #pragma unroll
@@ -348,36 +362,54 @@ struct BwdKernel {
     }
   }
 
-  // Reduce-add of a block's dQ slice into the fp32 accumulator with buffer atomics
-  // (rows past the query end fall outside the buffer range and are dropped by the
-  // hardware).
-  __device__ __forceinline__ void dq_atomics(const f32x16& dq, int64_t qi0) {
-    const int64_t rows = min((int64_t)q_rows - qi0, (int64_t)BQ);
+  // Reduce-add of a block's dQ slice into the fp32 accumulator with buffer atomics.
+  // Register r holds query row 8 (r / 4) + 4 (lane / 32) + r % 4; one descriptor per
+  // group of four rows bounds the group, so rows past the query end fall outside
+  // the buffer range and are dropped by the hardware.
+  __device__ __forceinline__ void dq_atomics(const f32x16& dq, int qi0) {
+    const int rows = min(q_rows - qi0, BQ);
     const int64_t qrow0 = BCAST ? (int64_t)(blockIdx.x & (kDqStripes - 1)) * a.q_len + qi0 : kv0 + qi0;
-    const rsrc_t acc = make_rsrc(a.dq_acc + (qrow0 * a.heads + h) * D, (uint32_t)(rows * a.heads * D * 4));
     const uint32_t row_bytes = (uint32_t)(a.heads * D * 4);
-    const uint32_t lo = launder(dq_lane_off);
+    float* base = a.dq_acc + (qrow0 * a.heads + h) * D;
+    const uint32_t o0 = launder(dq_lane_off);
+    const uint32_t o[4] = {o0, o0 + row_bytes, o0 + 2 * row_bytes, o0 + 3 * row_bytes};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const uint32_t off = lo + (uint32_t)(8 * (r >> 2) + (r & 3)) * row_bytes;
-      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dq[r], acc, off, 0, 0);
+    for (int g = 0; g < 4; ++g) {
+      const int grow = max(rows - 8 * g, 0);
+      const rsrc_t acc = make_rsrc(base + (int64_t)(8 * g) * a.heads * D, (uint32_t)grow * row_bytes);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dq[4 * g + e], acc, o[e], 0, 0);
     }
   }
 
   // After a barrier: part-0 waves sum the parts' partials and reduce-add them.
-  __device__ __forceinline__ void dq_flush(int64_t qi0) {
+  __device__ __forceinline__ void dq_flush(int qi0) {
     if (dq_part != 0) return;
-    f32x16 dq = zero16();
-#pragma unroll
-    for (int p = 0; p < KP; ++p) {
-      const float* srcp = dq_partial(p, dq_dt);
+    f32x16 dq;
+    {
+      const float* srcp = dq_partial(0, dq_dt);
 #pragma unroll
       for (int r = 0; r < 16; r += 4) {
         const f32x4 v4 = *reinterpret_cast<const f32x4*>(srcp + (r / 4) * 256 + lane * 4);
-        dq[r] += v4[0];
-        dq[r + 1] += v4[1];
-        dq[r + 2] += v4[2];
-        dq[r + 3] += v4[3];
+        dq[r] = v4[0];
+        dq[r + 1] = v4[1];
+        dq[r + 2] = v4[2];
+        dq[r + 3] = v4[3];
+      }
+    }
+#pragma unroll
+    for (int p = 1; p < KP; ++p) {
+      if (p < nparts) {
+        const float* srcp = dq_partial(p, dq_dt);
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          const f32x4 v4 = *reinterpret_cast<const f32x4*>(srcp + (r / 4) * 256 + lane * 4);
+          dq[r] += v4[0];
+          dq[r + 1] += v4[1];
+          dq[r + 2] += v4[2];
+          dq[r + 3] += v4[3];
+        }
       }
     }
     dq_atomics(dq, qi0);
@@ -392,15 +424,15 @@ struct BwdKernel {
   // order, so the wait before the closing barrier (for the loads) leaves the 16
   // reduce-adds issued after them in flight.
   template <bool MASKED>
-  __device__ __forceinline__ void run(int64_t qs, int64_t qe, int64_t q_last, int64_t& pending) {
-    for (int64_t qi0 = qs; qi0 < qe; qi0 += BQ) {
-      const int buf = (int)((qi0 / BQ) & 1);
+  __device__ __forceinline__ void run(int qs, int qe, int q_last, int& pending) {
+    for (int qi0 = qs; qi0 < qe; qi0 += BQ) {
+      const int buf = (qi0 / BQ) & 1;
       if (qi0 + BQ < q_last) load_qblock(qi0 + BQ, buf ^ 1);   // one block ahead
       if constexpr (KP == 1) {
         if (pending >= 0) dq_atomics(dq_compute(), pending);
         qblock<MASKED, true>(buf, qi0);
       } else {
-        if (pending >= 0) dq_publish(dq_compute());
+        if (pending >= 0 && dq_part < nparts) dq_publish(dq_compute());
         __syncthreads();
         if (pending >= 0) dq_flush(pending);
         qblock<MASKED, false>(buf, qi0);
@@ -418,21 +450,30 @@ struct BwdKernel {
   __device__ __forceinline__ void tile(int b, int jblk, int head) {
     h = head;
     kv0 = load_offset(a.offsets, a.off64, b);
-    n = load_offset(a.offsets, a.off64, b + 1) - kv0;
-    j0 = (int64_t)jblk * BN;
-    nvalid = (int)min(n - j0, (int64_t)BN);
+    n = (int)(load_offset(a.offsets, a.off64, b + 1) - kv0);
+    j0 = jblk * BN;
+    nvalid = min(n - j0, BN);
+    nparts = (nvalid + KPART - 1) / KPART;
     active = 32 * wave < nvalid;
-    q_rows = BCAST ? a.q_len : (int)n;
+    q_rows = BCAST ? a.q_len : n;
     grow0 = BCAST ? (int64_t)b * a.q_len : kv0;
 
     __syncthreads();   // previous tile's LDS readers are done
+    // a wave with no key inside the sequence never writes its dS^T rows in this
+    // tile: zero them once for the dQ products
+    if (!active) {
+      const uint32_t wb = dsw_base;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<bf16x4*>(smem + (wb ^ (uint32_t)(q4 << 4))) = bf16x4{};
+    }
     // K tile -> LDS (rows past the end read as zeros and are masked); this wave's
     // V fragment -> registers
     {
       lds_load_tile<D, NW>(smem + OFF_K, BN, wave, lane,
                            make_rsrc_sgpr(a.k + (kv0 + j0) * rs + (int64_t)h * D, (uint32_t)(nvalid * rs * 2)),
                            (uint32_t)(rs * 2));
-      const int64_t j = j0 + 32 * wave + c32;
+      const int j = j0 + 32 * wave + c32;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         vf[ks] = j < n ? *reinterpret_cast<const bf16x8*>(a.v + (kv0 + j) * rs + (int64_t)h * D + 16 * ks + 8 * hf)
@@ -444,21 +485,21 @@ struct BwdKernel {
       dkt[dt] = zero16();
     }
     // query rows that can see this tile's keys
-    int64_t qs = 0;
+    int qs = 0;
     if constexpr (CAUSAL) qs = (j0 / BQ) * BQ;
-    const int64_t q_last = q_rows;
-    if (qs < q_last) load_qblock(qs, (int)((qs / BQ) & 1));
+    const int q_last = q_rows;
+    if (qs < q_last) load_qblock(qs, (qs / BQ) & 1);
     wait_lds_loads();
     __syncthreads();
     // Peeled loops: query blocks that need a mask (causal diagonal, a partial K/V
     // block at the sequence end, or a partial last query block) run apart from the
     // branch-free bulk.
     const bool kv_tail = j0 + BN > n;
-    int64_t qm = qs;
+    int qm = qs;
     if constexpr (CAUSAL) qm = min(q_last, ((j0 + BN - 1 + BQ - 1) / BQ) * BQ);
     if (kv_tail) qm = q_last;
-    const int64_t qfull = max(qm, (q_last / BQ) * BQ);
-    int64_t pending = -1;   // query block whose dQ is still to be reduced
+    const int qfull = max(qm, (q_last / BQ) * BQ);
+    int pending = -1;   // query block whose dQ is still to be reduced
     run<true>(qs, qm, q_last, pending);
     run<false>(qm, qfull, q_last, pending);
     run<true>(qfull, q_last, q_last, pending);
@@ -466,31 +507,22 @@ struct BwdKernel {
       if constexpr (KP == 1) {
         dq_atomics(dq_compute(), pending);
       } else {
-        dq_publish(dq_compute());
+        if (dq_part < nparts) dq_publish(dq_compute());
         __syncthreads();
         dq_flush(pending);
       }
     }
 
-    // dK = c dS^T Q and dV -> bf16
-    const int64_t j = j0 + 32 * wave + c32;
-    if (j < n) {
-      bf16* dkp = a.dk + (kv0 + j) * rs + (int64_t)h * D;
-      bf16* dvp = a.dv + (kv0 + j) * rs + (int64_t)h * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          bf16x4 kk, vv;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            kk[e] = (bf16)(dkt[dt][4 * q4 + e] * a.scale);
-            vv[e] = (bf16)(dvt[dt][4 * q4 + e]);
-          }
-          *reinterpret_cast<bf16x4*>(dkp + 32 * dt + 8 * q4 + 4 * hf) = kk;
-          *reinterpret_cast<bf16x4*>(dvp + 32 * dt + 8 * q4 + 4 * hf) = vv;
-        }
-      }
+    // dK = c dS^T Q and dV -> bf16 rows, staged through this wave's slot of the K
+    // tile region (with one key part, wait until every wave's last dQ product has
+    // read the K tile)
+    if constexpr (KP == 1) __syncthreads();
+    {
+      const int nrows = min(max(n - (j0 + 32 * wave), 0), 32);
+      char* slot = smem + OFF_K + wave * (32 * 2 * D);
+      const int64_t off = (kv0 + j0 + 32 * wave) * rs + (int64_t)h * D;
+      store_acc_rows<D>(dkt, a.scale, slot, a.dk + off, rs, nrows, lane);
+      store_acc_rows<D>(dvt, 1.f, slot, a.dv + off, rs, nrows, lane);
     }
   }
 };
@@ -586,34 +618,33 @@ int64_t bwd_max_items(const Problem& p) {
   return (p.total_kv + bn - 1) / bn + p.batch;
 }
 
-hipError_t launch_bwd_pre(const Problem& p, const void* o, const void* d_o, float* delta,
-                          float* dq_acc, int64_t dq_acc_elems, hipStream_t s) {
+hipError_t launch_bwd_pre(const Problem& p, const void* o, const void* d_o, const float* lse,
+                          float* rowstat, float* dq_acc, int64_t dq_acc_elems, hipStream_t s) {
   const int64_t pairs = p.rows * p.heads;
   const int tpr = p.head_dim / 8;
   int64_t blocks = (pairs * tpr + 255) / 256;
   if (blocks < 1) blocks = 1;
   const int64_t vec4 = dq_acc_elems / 4;
+  float2* rs2 = reinterpret_cast<float2*>(rowstat);
   if (p.head_dim == 128)
     hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s,
-                       static_cast<const bf16*>(o), static_cast<const bf16*>(d_o), delta, p.rows,
+                       static_cast<const bf16*>(o), static_cast<const bf16*>(d_o), lse, rs2, p.rows,
                        p.heads, dq_acc, vec4);
   else
     hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s,
-                       static_cast<const bf16*>(o), static_cast<const bf16*>(d_o), delta, p.rows,
+                       static_cast<const bf16*>(o), static_cast<const bf16*>(d_o), lse, rs2, p.rows,
                        p.heads, dq_acc, vec4);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const Problem& p, const Plan& plan, int sched, const float* lse,
-                      const void* d_o, const float* delta, float* dq_acc, void* dk, void* dv,
-                      hipStream_t s) {
+hipError_t launch_bwd(const Problem& p, const Plan& plan, int sched, const float* rowstat,
+                      const void* d_o, float* dq_acc, void* dk, void* dv, hipStream_t s) {
   BwdArgs a;
   a.q = static_cast<const bf16*>(p.q);
   a.k = static_cast<const bf16*>(p.k);
   a.v = static_cast<const bf16*>(p.v);
   a.d_o = static_cast<const bf16*>(d_o);
-  a.lse = lse;
-  a.delta = delta;
+  a.rowstat = reinterpret_cast<const float2*>(rowstat);
   a.offsets = p.offsets;
   a.off64 = p.off64;
   a.heads = p.heads;

@@ -58,6 +58,7 @@ struct FwdKernel {
   static constexpr int DT = D / 32;              // 32-wide d tiles of O
   static constexpr int KS = D / 16;              // 16-deep k steps of Q K^T
   static_assert((BN * D * 2 / 1024) % NW == 0, "a K/V block must split evenly over the waves");
+  static_assert(NW * 32 * 2 * D <= 4 * TILE_BYTES, "epilogue slots must fit in the K/V buffers");
 
   // Tile-invariant per-wave state.
   FwdArgs a;
@@ -189,6 +190,7 @@ struct FwdKernel {
   }
 
   __device__ __forceinline__ void tile(int b, int m, int head) {
+    __syncthreads();   // the previous tile's epilogue is done with the K/V buffers
     h = head;
     kv0 = load_offset(a.offsets, a.off64, b);
     n = load_offset(a.offsets, a.off64, b + 1) - kv0;
@@ -223,21 +225,11 @@ struct FwdKernel {
     // epilogue
     const float lt = sum_across_halves(lsum);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (qvalid) {
-      bf16* op = a.o + ((out_row0 + qi) * rs + (int64_t)h * D);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          bf16x4 ov;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ov[e] = (bf16)(acc[dt][4 * q4 + e] * inv);
-          *reinterpret_cast<bf16x4*>(op + 32 * dt + 8 * q4 + 4 * hf) = ov;
-        }
-      }
-      if (hf == 0)
-        a.lse[(int64_t)h * a.rows + out_row0 + qi] = lt > 0.f ? (mrun + __log2f(lt)) * kLn2 : -INFINITY;
-    }
+    // O rows staged through this wave's slot of the (now idle) K/V buffers
+    store_acc_rows<D>(acc, inv, smem + wave * (32 * 2 * D), a.o + ((out_row0 + i0) * rs + (int64_t)h * D), rs,
+                      min(max(q_rows - i0, 0), 32), lane);
+    if (qvalid && hf == 0)
+      a.lse[(int64_t)h * a.rows + out_row0 + qi] = lt > 0.f ? (mrun + __log2f(lt)) * kLn2 : -INFINITY;
   }
 };
 

@@ -220,23 +220,28 @@ __device__ __forceinline__ void wait_lds_loads() { __builtin_amdgcn_s_waitcnt(0x
 __device__ __forceinline__ void wait_lds_loads_but_16() { __builtin_amdgcn_s_waitcnt(0x4F70); }
 
 // Copies rows [0, nrows) of a [rows][D] bf16 tile (row r at byte r * row_bytes of
-// the buffer) into a swizzled LDS tile.  Each wave instruction covers 1024 bytes =
-// 1024 / (2 D) rows; instruction u goes to wave u % NW.  Lane i of an instruction
-// fills LDS chunk slot (i % CH) of its row, so it fetches logical chunk
-// swz_chunk(row, slot) (the swizzle is an XOR involution).
+// the buffer, row_bytes a multiple of 2 D) into a swizzled LDS tile.  Each wave
+// instruction covers 1024 bytes = RPI = 1024 / (2 D) rows; instruction u goes to
+// wave u % NW.  Lane i of an instruction fills LDS chunk slot (i % CH) of row
+// u RPI + i / CH, so it fetches logical chunk swz_chunk(row, slot) (the swizzle is
+// an XOR involution).  The row mask splits as swz_mask(r0) ^ swz_mask(u RPI) for
+// r0 < RPI, so the lane's offset is one base XOR a wave-uniform constant plus a
+// wave-uniform row offset.
 template <int D, int NW>
 __device__ __forceinline__ void lds_load_tile(char* tile, int nrows, int wave, int lane, u32x4 r,
                                               uint32_t row_bytes) {
   constexpr int CH = D / 8;
   constexpr int RPI = 64 / CH;
   const int ninstr = nrows / RPI;
+  const uint32_t l = launder((uint32_t)lane);
+  const uint32_t r0 = l / CH;
+  const uint32_t base = r0 * row_bytes + ((((uint32_t)l % CH) ^ (uint32_t)swz_mask<D>((int)r0)) << 4);
 #pragma unroll
   for (int k = 0; k < (ninstr + NW - 1) / NW; ++k) {
     const int u = wave + k * NW;
     if (u < ninstr) {
-      const int row = u * RPI + lane / CH;
-      const int chunk = swz_chunk<D>(row, lane % CH);
-      lds_load16(r, (uint32_t)row * row_bytes + (uint32_t)chunk * 16u, tile + u * 1024);
+      const uint32_t voff = (base ^ ((uint32_t)swz_mask<D>(u * RPI) << 4)) + (uint32_t)(u * RPI) * row_bytes;
+      lds_load16(r, voff, tile + u * 1024);
     }
   }
 }
@@ -257,6 +262,57 @@ enum Schedule : int { kSortedZigzag = 0, kIdentity = 1, kDynamic = 2 };
 __device__ __forceinline__ int xcd_logical_wg(int wg, int num_wg) {
   const int per = num_wg >> 3;            // num_wg is a multiple of 8
   return (wg & 7) * per + (wg >> 3);
+}
+
+// ---- transposed accumulator tiles -> bf16 rows ----------------------------------
+
+// Writes a wave's 32 x D result, held as D / 32 MFMA accumulators with rows in the
+// n index (acc[dt] register r = C[m = d - 32 dt][n = row]: lane l owns row l % 32
+// and d = 32 dt + 8 (r / 4) + 4 (l / 32) + r % 4), to 32 consecutive rows of a bf16
+// array with a row pitch of `ld` elements, times the lane's `scale`.  Straight from
+// registers every store would cover 8 bytes of 32 different rows; instead the tile
+// is staged through a private LDS slot of 64 D bytes (16-byte chunks XOR-swizzled
+// by row) and read back so that each store instruction writes whole rows in
+// 16-byte pieces.  The stores go through a buffer descriptor spanning `nrows` rows,
+// so rows past the end are dropped by the hardware range check.
+template <int D>
+__device__ __forceinline__ void store_acc_rows(const f32x16 (&acc)[D / 32], float scale, char* slot,
+                                               bf16* dst, int64_t ld, int nrows, int lane) {
+  constexpr int CH = D / 8;       // 16-byte chunks per row
+  constexpr int RPI = 64 / CH;    // rows per read instruction
+  const int r = lane & 31, hf = lane >> 5;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[dt][4 * q4 + e] * scale);
+      const int c = 4 * dt + q4;   // chunk of d = 32 dt + 8 q4 + 4 hf + e
+      *reinterpret_cast<bf16x4*>(slot + r * (2 * D) + ((c ^ (r & (CH - 1))) << 4) + 8 * hf) = w;
+    }
+  }
+  // LDS operations of a wave execute in order; the fences only keep the compiler
+  // from moving the reads above the other lanes' writes.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint32_t pitch = (uint32_t)(ld * 2);
+  const rsrc_t out = make_rsrc(dst, (uint32_t)max(nrows, 0) * pitch);
+  // lane-derived offsets are recomputed here rather than hoisted across tiles
+  const uint32_t l = launder((uint32_t)lane);
+  const uint32_t c = l % CH, r0 = l / CH;
+  const uint32_t voff = r0 * pitch + 16u * c;
+  const uint32_t loff = r0 * (2 * D) + ((c ^ r0) << 4);
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    // row RPI i + r0 with r0 < RPI: its swizzle mask is r0 ^ (RPI i mod CH)
+    const uint32_t la = (loff ^ (uint32_t)(((RPI * i) & (CH - 1)) << 4)) + (uint32_t)(RPI * i * 2 * D);
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(slot + la);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), out,
+                                           voff + (uint32_t)(RPI * i) * pitch, 0, 0);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 }  // namespace jfa

@@ -50,12 +50,12 @@ hipError_t launch_plan_fwd(const Problem& p, const Plan& plan, int sched, hipStr
 hipError_t launch_fwd(const Problem& p, const Plan& plan, int sched, void* o, float* lse,
                       hipStream_t s);
 
-hipError_t launch_bwd_pre(const Problem& p, const void* o, const void* d_o, float* delta,
-                          float* dq_acc, int64_t dq_acc_elems, hipStream_t s);
+// rowstat: [heads][rows] pairs (LSE log2 e, delta = rowsum(dO * O)), 2 floats each.
+hipError_t launch_bwd_pre(const Problem& p, const void* o, const void* d_o, const float* lse,
+                          float* rowstat, float* dq_acc, int64_t dq_acc_elems, hipStream_t s);
 hipError_t launch_plan_bwd(const Problem& p, const Plan& plan, int sched, hipStream_t s);
-hipError_t launch_bwd(const Problem& p, const Plan& plan, int sched, const float* lse,
-                      const void* d_o, const float* delta, float* dq_acc, void* dk, void* dv,
-                      hipStream_t s);
+hipError_t launch_bwd(const Problem& p, const Plan& plan, int sched, const float* rowstat,
+                      const void* d_o, float* dq_acc, void* dk, void* dv, hipStream_t s);
 hipError_t launch_dq_finalize(const Problem& p, const float* dq_acc, void* dq, hipStream_t s);
 
 // Number of compute units of the current device (cached per device).
