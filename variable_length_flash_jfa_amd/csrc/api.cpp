@@ -89,12 +89,12 @@ jfa::Problem make_problem(const void* q, const void* k, const void* v, const voi
 }
 
 size_t fwd_ws_bytes(const jfa::Problem& p) {
-  return kAlign + align_up(64) + align_up((size_t)jfa::fwd_max_items(p) * sizeof(int2));
+  return kAlign + align_up(64) + align_up((size_t)jfa::fwd_max_items(p) * sizeof(int4));
 }
 
 size_t bwd_ws_bytes(const jfa::Problem& p) {
   const int64_t q_rows = p.broadcast ? (int64_t)p.q_len * jfa::kDqStripes : p.total_kv;
-  return kAlign + align_up(64) + align_up((size_t)jfa::bwd_max_items(p) * sizeof(int2)) +
+  return kAlign + align_up(64) + align_up((size_t)jfa::bwd_max_items(p) * sizeof(int4)) +
          align_up((size_t)p.heads * p.rows * 2 * sizeof(float)) +
          align_up((size_t)q_rows * p.heads * p.head_dim * sizeof(float));
 }
@@ -240,7 +240,7 @@ jfa_status_t jfa_fwd(const void* q, const void* k, const void* v, const void* of
   jfa::Plan plan;
   plan.meta = reinterpret_cast<int*>(carve(cur, 64));
   plan.max_items = jfa::fwd_max_items(p);
-  plan.items = reinterpret_cast<int2*>(carve(cur, plan.max_items * sizeof(int2)));
+  plan.items = reinterpret_cast<int4*>(carve(cur, plan.max_items * sizeof(int4)));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int sched = g_schedule.load();
   hipError_t e = timed_launch("plan_fwd", s, [&] { return jfa::launch_plan_fwd(p, plan, sched, s); });
@@ -279,7 +279,7 @@ jfa_status_t jfa_bwd(const void* q, const void* k, const void* v, const void* of
   jfa::Plan plan;
   plan.meta = reinterpret_cast<int*>(carve(cur, 64));
   plan.max_items = jfa::bwd_max_items(p);
-  plan.items = reinterpret_cast<int2*>(carve(cur, plan.max_items * sizeof(int2)));
+  plan.items = reinterpret_cast<int4*>(carve(cur, plan.max_items * sizeof(int4)));
   float* rowstat = reinterpret_cast<float*>(carve(cur, (size_t)p.heads * p.rows * 2 * sizeof(float)));
   const int64_t q_rows = p.broadcast ? (int64_t)p.q_len * jfa::kDqStripes : p.total_kv;
   const int64_t acc_elems = q_rows * p.heads * p.head_dim;

@@ -47,25 +47,24 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o
                                                        float2* __restrict__ rowstat, int64_t rows,
                                                        int heads, float* __restrict__ dq_acc,
                                                        int64_t acc_vec4) {
-  constexpr int TPR = D / 8;                 // threads per (head, row)
-  const int64_t pair = ((int64_t)blockIdx.x * 256 + threadIdx.x) / TPR;   // h * rows + row
+  constexpr int TPR = D / 8;                 // threads per (row, head)
+  const int64_t pair = ((int64_t)blockIdx.x * 256 + threadIdx.x) / TPR;   // row * heads + h
   const int part = threadIdx.x % TPR;
   const int64_t npairs = rows * heads;
   float s = 0.f;
-  int64_t row = 0;
-  int h = 0;
   if (pair < npairs) {
-    h = (int)(pair / rows);
-    row = pair - (int64_t)h * rows;
-    const int64_t off = (row * heads + h) * D + part * 8;
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(o + off);
-    const bf16x8 y = *reinterpret_cast<const bf16x8*>(d_o + off);
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(o + pair * D + part * 8);
+    const bf16x8 y = *reinterpret_cast<const bf16x8*>(d_o + pair * D + part * 8);
 #pragma unroll
     for (int e = 0; e < 8; ++e) s += (float)x[e] * (float)y[e];
   }
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
-  if (pair < npairs && part == 0) rowstat[pair] = make_float2(lse[pair] * kLog2e, s);
+  if (pair < npairs && part == 0) {
+    const int64_t row = pair / heads;
+    const int64_t i = (pair - row * heads) * rows + row;   // [head][row]
+    rowstat[i] = make_float2(lse[i] * kLog2e, s);
+  }
   // grid-stride zero fill of the dQ accumulator
   const int64_t nthreads = (int64_t)gridDim.x * 256;
   float4* acc = reinterpret_cast<float4*>(dq_acc);
@@ -92,7 +91,7 @@ struct BwdArgs {
   float* dq_acc;
   bf16* dk;
   bf16* dv;
-  const int2* items;
+  const int4* items;
   int* meta;
   int sched;
 };
@@ -128,7 +127,7 @@ struct BwdKernel {
   static constexpr uint32_t GQ = OFF_DO - OFF_Q;              // dO tile minus Q tile, same buffer
   static constexpr int XB = D == 128 ? 256 : 128;             // the XOR-free granule
   static_assert(BN == 32 * NW && KP * DT == NW && KPART % 16 == 0, "tile shape");
-  static_assert(NW * 32 * 2 * D <= KT_BYTES, "epilogue slots must fit in the K tile region");
+  static_assert(OFF_Q + NW * 32 * 2 * D <= SMEM, "epilogue slots must fit behind the K tile region");
   static_assert(OFF_Q % XB == 0 && QT_BYTES % XB == 0 && GQ % XB == 0 && (KPART * 2 * D) % XB == 0 &&
                     (32 * 2 * D) % XB == 0 && OFF_DS % 64 == 0 && (KPART * BQ * 2) % 64 == 0,
                 "tile offsets must commute with the swizzle XOR");
@@ -246,49 +245,54 @@ struct BwdKernel {
         ga = ga_n;
         __builtin_amdgcn_sched_barrier(0);
       }
-      // P = exp2(S c log2 e - LSE log2 e); dS = P (dP - delta)
-      const char* rowp = rowbuf(buf) + 32 * hf;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        // rows 8 q4 + 4 hf + 0..3: (lse2, delta) pairs
-        const f32x4 r01 = *reinterpret_cast<const f32x4*>(rowp + 64 * q4);
-        const f32x4 r23 = *reinterpret_cast<const f32x4*>(rowp + 64 * q4 + 16);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * q4 + e;
-          const float l2 = e < 2 ? r01[2 * e] : r23[2 * (e - 2)];
-          const float dl = e < 2 ? r01[2 * e + 1] : r23[2 * (e - 2) + 1];
-          float p = fast_exp2(fmaf(s[r], a.scale_log2, -l2));
-          if constexpr (MASKED) {
-            // rows past the query end, keys past the sequence end, and (causal) keys
-            // after the query get zero probability
-            const int ipos = qi0 + 8 * q4 + 4 * hf + e;
-            const int jpos = j0 + 32 * wave + c32;
-            bool vis = jpos < n && ipos < q_rows;
-            if constexpr (CAUSAL) vis = vis && jpos <= ipos;
-            if (!vis) p = 0.f;
-          }
-          const float ds = p * (dp[r] - dl);
-          pb[r >> 3][r & 7] = (bf16)p;
-          sb[r >> 3][r & 7] = (bf16)ds;
+      // P = exp2(S c log2 e - LSE log2 e); dS = P (dP - delta) for query rows
+      // 8 q4 + 4 hf + e (register r = 4 q4 + e); (rs01, rs23) hold the (LSE log2 e,
+      // delta) pairs of rows e = 0, 1 and e = 2, 3
+      auto softmax = [&](int q4, int e, const f32x4& rs01, const f32x4& rs23) {
+        const int r = 4 * q4 + e;
+        const float l2 = e < 2 ? rs01[2 * e] : rs23[2 * (e - 2)];
+        const float dl = e < 2 ? rs01[2 * e + 1] : rs23[2 * (e - 2) + 1];
+        float p = fast_exp2(fmaf(s[r], a.scale_log2, -l2));
+        if constexpr (MASKED) {
+          // rows past the query end, keys past the sequence end, and (causal) keys
+          // after the query get zero probability
+          const int ipos = qi0 + 8 * q4 + 4 * hf + e;
+          const int jpos = j0 + 32 * wave + c32;
+          bool vis = jpos < n && ipos < q_rows;
+          if constexpr (CAUSAL) vis = vis && jpos <= ipos;
+          if (!vis) p = 0.f;
         }
-      }
-    }
-    // publish dS^T [key][query] (bf16)
-    auto publish_ds = [&]() {
-      const uint32_t wb = launder(dsw_base);
+        const float ds = p * (dp[r] - dl);
+        pb[r >> 3][r & 7] = (bf16)p;
+        sb[r >> 3][r & 7] = (bf16)ds;
+      };
+      const char* rowp = rowbuf(buf) + 32 * hf;
+      // rows of query block half 0 (registers 0..7) now; those of half 1 are formed
+      // between the dV / dK products of half 0, which do not depend on them
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 w;
+      for (int q4 = 0; q4 < 2; ++q4) {
+        const f32x4 rs01 = *reinterpret_cast<const f32x4*>(rowp + 64 * q4);
+        const f32x4 rs23 = *reinterpret_cast<const f32x4*>(rowp + 64 * q4 + 16);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = sb[q4 >> 1][4 * (q4 & 1) + e];
-        *reinterpret_cast<bf16x4*>(smem + (wb ^ (uint32_t)(q4 << 4))) = w;
+        for (int e = 0; e < 4; ++e) softmax(q4, e, rs01, rs23);
       }
-    };
-    if constexpr (!MID_BAR) publish_ds();
-    {
+      // (LSE, delta) of q4 = 2 now, of q4 = 3 once q4 = 2 is done
+      f32x4 h01 = *reinterpret_cast<const f32x4*>(rowp + 128);
+      f32x4 h23 = *reinterpret_cast<const f32x4*>(rowp + 128 + 16);
+      // publish dS^T [key][query] (bf16)
+      auto publish_ds = [&]() {
+        const uint32_t wb = launder(dsw_base);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = sb[q4 >> 1][4 * (q4 & 1) + e];
+          *reinterpret_cast<bf16x4*>(smem + (wb ^ (uint32_t)(q4 << 4))) = w;
+        }
+      };
       // dV^T += dO^T P and dK^T += Q^T dS (C: m = d, n = key j); query rows
       // 16 kc + 4 (lane / 32) + e and + 8 pair with the P / dS registers
+      constexpr int EPS = 8 / DT;   // half-1 softmax elements per half-0 step
       const uint32_t tb = launder(tr4_base + (uint32_t)OFF_Q + boff);
       bf16x8 g_op = lds_operand_tr<D>(smem + GQ, tb, 0, 8, 0);
       bf16x8 q_op = lds_operand_tr<D>(smem, tb, 0, 8, 0);
@@ -302,15 +306,36 @@ struct BwdKernel {
           q_n = lds_operand_tr<D>(smem, tb, 16 * kc1, 16 * kc1 + 8, dt1);
         }
         dvt[dt] = mfma32(g_op, pb[kc], dvt[dt]);
+        if (kc == 0) {
+#pragma unroll
+          for (int k = 0; k < EPS / 2; ++k) {
+            const int el = EPS * step + k;   // 0..7 -> (q4 2 + el / 4, e el % 4)
+            softmax(2 + el / 4, el % 4, h01, h23);
+          }
+        }
         dkt[dt] = mfma32(q_op, sb[kc], dkt[dt]);
+        if (kc == 0) {
+#pragma unroll
+          for (int k = EPS / 2; k < EPS; ++k) {
+            const int el = EPS * step + k;
+            softmax(2 + el / 4, el % 4, h01, h23);
+          }
+          if (EPS * (step + 1) == 4) {
+            h01 = *reinterpret_cast<const f32x4*>(rowp + 192);
+            h23 = *reinterpret_cast<const f32x4*>(rowp + 192 + 16);
+          }
+        }
         g_op = g_n;
         q_op = q_n;
+        if constexpr (!MID_BAR) {
+          if (step == DT - 1) publish_ds();
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    if constexpr (MID_BAR) {
-      __syncthreads();   // the previous block's dS^T readers are done
-      publish_ds();
+      if constexpr (MID_BAR) {
+        __syncthreads();   // the previous block's dS^T readers are done
+        publish_ds();
+      }
     }
   }
 
@@ -447,18 +472,57 @@ struct BwdKernel {
     }
   }
 
-  __device__ __forceinline__ void tile(int b, int jblk, int head) {
-    h = head;
-    kv0 = load_offset(a.offsets, a.off64, b);
-    n = (int)(load_offset(a.offsets, a.off64, b + 1) - kv0);
-    j0 = jblk * BN;
+  // Geometry of a tile from its plan item (sequence, key block, first row, length).
+  struct Geo {
+    int64_t kv0;
+    int b, n, j0, h;
+  };
+  __device__ __forceinline__ Geo geometry(int4 it, int head) const {
+    Geo g;
+    g.b = __builtin_amdgcn_readfirstlane(it.x);
+    g.j0 = __builtin_amdgcn_readfirstlane(it.y) * BN;
+    g.kv0 = __builtin_amdgcn_readfirstlane(it.z);
+    g.n = __builtin_amdgcn_readfirstlane(it.w);
+    g.h = head;
+    return g;
+  }
+
+  // Issues the loads of a tile's K (direct to LDS; rows past the end read as zeros
+  // and are masked) and of this wave's V fragment (to registers, zeros past the end).
+  // The caller ensures that nobody reads the K region or vf meanwhile.
+  __device__ __forceinline__ void issue_kv(const Geo& g) {
+    const int nv = min(g.n - g.j0, BN);
+    lds_load_tile<D, NW>(smem + OFF_K, BN, wave, lane,
+                         make_rsrc_sgpr(a.k + (g.kv0 + g.j0) * rs + (int64_t)g.h * D, (uint32_t)(nv * rs * 2)),
+                         (uint32_t)(rs * 2));
+    const int nw = min(max(nv - 32 * wave, 0), 32);   // this wave's keys inside the sequence
+    const rsrc_t vr = make_rsrc(a.v + (g.kv0 + g.j0 + 32 * wave) * rs + (int64_t)g.h * D,
+                                (uint32_t)(nw * rs * 2));
+    const uint32_t l = launder((uint32_t)lane);
+    const uint32_t vo = (l & 31) * (uint32_t)(rs * 2) + 16u * (l >> 5);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      vf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vr, vo + 32u * ks, 0, 0));
+  }
+
+  // One tile whose K/V loads have been issued.  `pre` runs after the first barrier;
+  // after the last dQ product and a barrier, `next(ng)` names the following tile (or
+  // returns false) and that tile's K/V loads are issued before this tile's dK / dV
+  // leave, so their latency overlaps the epilogue.
+  template <class Pre, class Next>
+  __device__ __forceinline__ bool process(const Geo& g, Pre&& pre, Next&& next, Geo& ng) {
+    h = g.h;
+    kv0 = g.kv0;
+    n = g.n;
+    j0 = g.j0;
     nvalid = min(n - j0, BN);
     nparts = (nvalid + KPART - 1) / KPART;
     active = 32 * wave < nvalid;
     q_rows = BCAST ? a.q_len : n;
-    grow0 = BCAST ? (int64_t)b * a.q_len : kv0;
+    grow0 = BCAST ? (int64_t)g.b * a.q_len : kv0;
 
-    __syncthreads();   // previous tile's LDS readers are done
+    __syncthreads();   // the previous tile's epilogue is done with its LDS slots
+    pre();
     // a wave with no key inside the sequence never writes its dS^T rows in this
     // tile: zero them once for the dQ products
     if (!active) {
@@ -466,18 +530,6 @@ struct BwdKernel {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
         *reinterpret_cast<bf16x4*>(smem + (wb ^ (uint32_t)(q4 << 4))) = bf16x4{};
-    }
-    // K tile -> LDS (rows past the end read as zeros and are masked); this wave's
-    // V fragment -> registers
-    {
-      lds_load_tile<D, NW>(smem + OFF_K, BN, wave, lane,
-                           make_rsrc_sgpr(a.k + (kv0 + j0) * rs + (int64_t)h * D, (uint32_t)(nvalid * rs * 2)),
-                           (uint32_t)(rs * 2));
-      const int j = j0 + 32 * wave + c32;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        vf[ks] = j < n ? *reinterpret_cast<const bf16x8*>(a.v + (kv0 + j) * rs + (int64_t)h * D + 16 * ks + 8 * hf)
-                       : zero_bf16x8();
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -512,18 +564,21 @@ struct BwdKernel {
         dq_flush(pending);
       }
     }
+    __syncthreads();   // every wave is past its last read of the K tile and dQ partials
 
-    // dK = c dS^T Q and dV -> bf16 rows, staged through this wave's slot of the K
-    // tile region (with one key part, wait until every wave's last dQ product has
-    // read the K tile)
-    if constexpr (KP == 1) __syncthreads();
+    const bool more = next(ng);
+    if (more) issue_kv(ng);
+
+    // dK = c dS^T Q and dV -> bf16 rows, staged through this wave's slot of the
+    // (idle) query-block region
     {
       const int nrows = min(max(n - (j0 + 32 * wave), 0), 32);
-      char* slot = smem + OFF_K + wave * (32 * 2 * D);
+      char* slot = smem + OFF_Q + wave * (32 * 2 * D);
       const int64_t off = (kv0 + j0 + 32 * wave) * rs + (int64_t)h * D;
       store_acc_rows<D>(dkt, a.scale, slot, a.dk + off, rs, nrows, lane);
       store_acc_rows<D>(dvt, 1.f, slot, a.dv + off, rs, nrows, lane);
     }
+    return more;
   }
 };
 
@@ -531,26 +586,46 @@ template <int D, int NW, bool BCAST, bool CAUSAL>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_kernel(BwdArgs a) {
   using K = BwdKernel<D, NW, BCAST, CAUSAL>;
+  using Geo = typename K::Geo;
   __shared__ __attribute__((aligned(16))) char smem[K::SMEM];
+  __shared__ __attribute__((aligned(16))) int next_item[64];   // DMA target, 16 bytes used
   __shared__ int claimed;
   K kern(a, smem);
   const int num_wg = gridDim.x;
   const int lwg = xcd_logical_wg(blockIdx.x, num_wg);
   const int ntiles = a.meta[2];
-  for (int r = 0;; ++r) {
-    int idx;
-    if (a.sched == kDynamic) {
-      if (threadIdx.x == 0) claimed = atomicAdd(a.meta + 1, 1);
-      __syncthreads();
-      idx = claimed;
-      __syncthreads();
-    } else {
-      idx = r * num_wg + lwg;
-    }
-    if (idx >= ntiles) break;
-    const int item = idx / a.heads;
-    const int2 it = a.items[item];
-    kern.tile(it.x, it.y, idx - item * a.heads);
+  const bool dyn = a.sched == kDynamic;
+  auto claim = [&]() {
+    if (threadIdx.x == 0) claimed = atomicAdd(a.meta + 1, 1);
+    __syncthreads();
+    const int v = claimed;
+    __syncthreads();
+    return v;
+  };
+  int idx = dyn ? claim() : lwg;
+  if (idx >= ntiles) return;
+  Geo g = kern.geometry(a.items[idx / a.heads], idx % a.heads);
+  kern.issue_kv(g);
+  for (;;) {
+    // static schedules know the next tile now: its item is copied into LDS while
+    // this tile runs (the copy completes at this tile's first load wait)
+    int nidx = dyn ? -1 : idx + num_wg;
+    auto pre = [&]() {
+      if (!dyn && nidx < ntiles && kern.wave == 0)
+        lds_load4(make_rsrc_sgpr(a.items + nidx / a.heads, 16u), (uint32_t)kern.lane * 4u,
+                  reinterpret_cast<char*>(next_item));
+    };
+    auto next = [&](Geo& out) -> bool {
+      if (dyn) nidx = claim();
+      if (nidx >= ntiles) return false;
+      const int4 it = dyn ? a.items[nidx / a.heads] : *reinterpret_cast<const int4*>(next_item);
+      out = kern.geometry(it, nidx % a.heads);
+      return true;
+    };
+    Geo ng;
+    if (!kern.process(g, pre, next, ng)) break;
+    g = ng;
+    idx = nidx;
   }
 }
 

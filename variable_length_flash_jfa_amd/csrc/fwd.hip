@@ -43,7 +43,7 @@ struct FwdArgs {
   float scale_log2;
   bf16* o;
   float* lse;
-  const int2* items;
+  const int4* items;
   int* meta;
   int sched;
 };
@@ -189,11 +189,12 @@ struct FwdKernel {
     }
   }
 
-  __device__ __forceinline__ void tile(int b, int m, int head) {
+  // Tile (sequence b with rows [kv0, kv0 + len), query block m, head).
+  __device__ __forceinline__ void tile(int b, int m, int head, int seq_kv0, int seq_len) {
     __syncthreads();   // the previous tile's epilogue is done with the K/V buffers
     h = head;
-    kv0 = load_offset(a.offsets, a.off64, b);
-    n = load_offset(a.offsets, a.off64, b + 1) - kv0;
+    kv0 = seq_kv0;
+    n = seq_len;
     q_rows = BCAST ? a.q_len : (int)n;
     m0 = m * BM;
     i0 = m0 + 32 * wave;
@@ -259,11 +260,13 @@ void fwd_kernel(FwdArgs a) {
     if (idx >= ntiles) break;
     const int item = idx / per_item;
     const int rem = idx - item * per_item;
-    const int2 it = a.items[item];
+    const int4 it = a.items[item];
+    const int b = __builtin_amdgcn_readfirstlane(it.x), blk = __builtin_amdgcn_readfirstlane(it.y);
+    const int s0 = __builtin_amdgcn_readfirstlane(it.z), len = __builtin_amdgcn_readfirstlane(it.w);
     if (BCAST) {
-      kern.tile(it.x, rem / a.heads, rem % a.heads);
+      kern.tile(b, rem / a.heads, rem % a.heads, s0, len);
     } else {
-      kern.tile(it.x, it.y, rem);
+      kern.tile(b, blk, rem, s0, len);
     }
   }
 }

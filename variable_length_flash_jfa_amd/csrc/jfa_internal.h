@@ -34,10 +34,11 @@ struct Problem {
 };
 
 // Plan written on the device: meta[0] = number of items, meta[1] = dynamic-schedule
-// counter, meta[2] = number of tiles.  items[i] = (sequence, block) pairs.
+// counter, meta[2] = number of tiles.  items[i] = (sequence b, block, offsets[b],
+// offsets[b + 1] - offsets[b]).
 struct Plan {
   int* meta;
-  int2* items;
+  int4* items;
   int64_t max_items;
 };
 

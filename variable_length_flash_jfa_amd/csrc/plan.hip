@@ -89,7 +89,7 @@ struct PlanFwdArgs {
   int causal;
   int heads;
   int sched;
-  int2* items;
+  int4* items;
   int* meta;
 };
 
@@ -127,7 +127,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fwd_kernel(PlanFwdArgs a) {
     for (int b = b_begin; b < b_end; ++b) {
       const int64_t n = load_offset(a.offsets, a.off64, b + 1) - load_offset(a.offsets, a.off64, b);
       const int mi = fwd_items_of(a, n);
-      for (int m = 0; m < mi; ++m) a.items[pos++] = make_int2(b, m);
+      const int kv0 = (int)load_offset(a.offsets, a.off64, b);
+      for (int m = 0; m < mi; ++m) a.items[pos++] = make_int4(b, m, kv0, (int)n);
     }
   } else {
     for (int i = tid; i < kKeys; i += kPlanThreads) hist[i] = 0;
@@ -164,18 +165,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fwd_kernel(PlanFwdArgs a) {
     // pass 2: scatter in cost order
     {
       int b = b_begin, m = 0;
-      int64_t n = 0;
+      int64_t n = 0, kv0 = 0;
       int mi = 0;
       for (int r = 0; r < rounds; ++r) {
         if (r < count) {
           while (m >= mi) {
-            n = load_offset(a.offsets, a.off64, b + 1) - load_offset(a.offsets, a.off64, b);
+            kv0 = load_offset(a.offsets, a.off64, b);
+            n = load_offset(a.offsets, a.off64, b + 1) - kv0;
             mi = fwd_items_of(a, n);
             m = 0;
             if (mi == 0) ++b;
           }
           const int pos = aggregated_increment(hist, fwd_cost(a, n, m));
-          a.items[pos] = make_int2(b, m);
+          a.items[pos] = make_int4(b, m, (int)kv0, (int)n);
           if (++m >= mi) ++b;
         }
       }
@@ -195,11 +197,13 @@ struct PlanBwdArgs {
   int batch;
   int heads;
   int bn;          // keys per backward tile
-  int2* items;
+  int4* items;
   int* meta;
 };
 
 // Valid (sequence, K/V block) pairs in natural order; tile t = (items[t / H], t % H).
+// Each item also carries the sequence's first row and length (int32: the library
+// rejects T >= 2^30), so a tile's geometry is one 16-byte load.
 __global__ __launch_bounds__(kPlanThreads) void plan_bwd_kernel(PlanBwdArgs a) {
   __shared__ int wave_sums[kPlanThreads / 64 + 1];
   const int tid = threadIdx.x;
@@ -214,9 +218,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_bwd_kernel(PlanBwdArgs a) {
   int total = 0;
   int pos = block_exclusive_scan(count, wave_sums, &total);
   for (int b = b_begin; b < b_end; ++b) {
-    const int64_t n = load_offset(a.offsets, a.off64, b + 1) - load_offset(a.offsets, a.off64, b);
+    const int64_t kv0 = load_offset(a.offsets, a.off64, b);
+    const int64_t n = load_offset(a.offsets, a.off64, b + 1) - kv0;
     const int nb = (int)((n + a.bn - 1) / a.bn);
-    for (int j = 0; j < nb; ++j) a.items[pos++] = make_int2(b, j);
+    for (int j = 0; j < nb; ++j) a.items[pos++] = make_int4(b, j, (int)kv0, (int)n);
   }
   if (tid == 0) {
     a.meta[0] = total;
