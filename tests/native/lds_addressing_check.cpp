@@ -77,4 +77,15 @@ int check() {
   return bad;
 }
 
-int main() { return (check<128>() + check<64>()) ? 1 : 0; }
+// join_u32 must not let a low word with bit 31 set leak into the high word (the
+// buffer descriptor base is rebuilt from two readfirstlane results).
+int check_join() {
+  int bad = 0;
+  if (join_u32(0x1u, 0x80000000u) != 0x180000000ull) ++bad;
+  if (join_u32(0x7f12u, 0xfffffff0u) != 0x7f12fffffff0ull) ++bad;
+  if (join_u32(0u, 0x12345678u) != 0x12345678ull) ++bad;
+  std::printf("join_u32 mismatches=%d\n", bad);
+  return bad;
+}
+
+int main() { return (check<128>() + check<64>() + check_join()) ? 1 : 0; }

@@ -462,10 +462,12 @@ struct BwdKernel {
         if (pending >= 0) dq_flush(pending);
         qblock<MASKED, false>(buf, qi0);
       }
-      if (pending >= 0 && dq_part == 0) {
-        wait_lds_loads_but_16();
-      } else {
-        wait_lds_loads();
+      if (qi0 + BQ < q_last) {   // the next block's loads must have landed
+        if (pending >= 0 && dq_part == 0) {
+          wait_lds_loads_but_16();
+        } else {
+          wait_lds_loads();
+        }
       }
       __syncthreads();
       pending = qi0;
@@ -489,12 +491,15 @@ struct BwdKernel {
 
   // Issues the loads of a tile's K (direct to LDS; rows past the end read as zeros
   // and are masked) and of this wave's V fragment (to registers, zeros past the end).
-  // The caller ensures that nobody reads the K region or vf meanwhile.
-  __device__ __forceinline__ void issue_kv(const Geo& g) {
+  // The caller ensures that nobody reads the K region, or vf, meanwhile.
+  __device__ __forceinline__ void issue_k(const Geo& g) {
     const int nv = min(g.n - g.j0, BN);
     lds_load_tile<D, NW>(smem + OFF_K, BN, wave, lane,
                          make_rsrc_sgpr(a.k + (g.kv0 + g.j0) * rs + (int64_t)g.h * D, (uint32_t)(nv * rs * 2)),
                          (uint32_t)(rs * 2));
+  }
+  __device__ __forceinline__ void issue_v(const Geo& g) {
+    const int nv = min(g.n - g.j0, BN);
     const int nw = min(max(nv - 32 * wave, 0), 32);   // this wave's keys inside the sequence
     const rsrc_t vr = make_rsrc(a.v + (g.kv0 + g.j0 + 32 * wave) * rs + (int64_t)g.h * D,
                                 (uint32_t)(nw * rs * 2));
@@ -504,11 +509,15 @@ struct BwdKernel {
     for (int ks = 0; ks < KS; ++ks)
       vf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vr, vo + 32u * ks, 0, 0));
   }
+  __device__ __forceinline__ void issue_kv(const Geo& g) {
+    issue_k(g);
+    issue_v(g);
+  }
 
-  // One tile whose K/V loads have been issued.  `pre` runs after the first barrier;
-  // after the last dQ product and a barrier, `next(ng)` names the following tile (or
-  // returns false) and that tile's K/V loads are issued before this tile's dK / dV
-  // leave, so their latency overlaps the epilogue.
+  // One tile whose K/V loads have been issued.  `pre` runs after the first barrier.
+  // After the query loop `next(ng)` names the following tile (or returns false); its
+  // V fragment (vf is no longer read) is loaded during the last dQ product and its K
+  // tile once every wave is past that product, before this tile's dK / dV leave.
   template <class Pre, class Next>
   __device__ __forceinline__ bool process(const Geo& g, Pre&& pre, Next&& next, Geo& ng) {
     h = g.h;
@@ -555,6 +564,8 @@ struct BwdKernel {
     run<true>(qs, qm, q_last, pending);
     run<false>(qm, qfull, q_last, pending);
     run<true>(qfull, q_last, q_last, pending);
+    const bool more = next(ng);
+    if (more) issue_v(ng);
     if (pending >= 0) {
       if constexpr (KP == 1) {
         dq_atomics(dq_compute(), pending);
@@ -565,9 +576,7 @@ struct BwdKernel {
       }
     }
     __syncthreads();   // every wave is past its last read of the K tile and dQ partials
-
-    const bool more = next(ng);
-    if (more) issue_kv(ng);
+    if (more) issue_k(ng);
 
     // dK = c dS^T Q and dV -> bf16 rows, staged through this wave's slot of the
     // (idle) query-block region

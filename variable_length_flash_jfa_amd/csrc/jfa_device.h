@@ -168,9 +168,21 @@ __device__ __forceinline__ bf16x8 lds_operand_tr(const char* tile, uint32_t tr_b
 
 // Raw buffer resource over `bytes` bytes from `base` (gfx9-family descriptor word 3).
 // Buffer loads past `bytes` return zeros, which zero-fills rows past a sequence end.
+// Both arguments must be wave-uniform; they are taken from the first lane so that
+// the descriptor lives in SGPRs (a descriptor the compiler believes divergent is
+// wrapped in a loop over its distinct values).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// 64-bit value from two 32-bit words; the words are unsigned so that a low word with
+// bit 31 set does not sign-extend into the high word (readfirstlane returns int).
+__host__ __device__ __forceinline__ uint64_t join_u32(uint32_t hi, uint32_t lo) {
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  const uint64_t a = (uint64_t)base;
+  const uint64_t u = join_u32((uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)),
+                              (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
 // One 16-byte (or 4-byte) chunk per lane from the buffer straight into LDS (gfx950
