@@ -147,7 +147,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gem_broadcast", choices=workloads.ORDER)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--schedule", type=int, default=0, help="0 sorted+zigzag, 1 identity, 2 dynamic")
+    ap.add_argument("--schedule", type=int, default=2, help="0 sorted+zigzag, 1 identity, 2 dynamic (default)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",

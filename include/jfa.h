@@ -65,10 +65,12 @@ typedef enum {
  *   JFA_SCHED_SORTED_ZIGZAG  forward tiles sorted by KV work (descending) and dealt
  *                            boustrophedon across persistent workgroups; backward
  *                            valid (b, h, KV-block) tiles dealt round-robin (JFA news
- *                            page, "Five changes unlocked the gains", item 1).  Default.
+ *                            page, "Five changes unlocked the gains", item 1).
  *   JFA_SCHED_IDENTITY       tiles in natural (b, block, h) order, dealt round-robin.
  *   JFA_SCHED_DYNAMIC        sorted tiles claimed through a device atomic counter by
  *                            whichever workgroup is free (the same section, item 2).
+ *                            Default: on MI355X it was the fastest of the three on
+ *                            every measured workload.
  * Results are independent of the schedule: O, LSE, dK and dV bit for bit, dQ up to
  * the order of its fp32 additions. */
 typedef enum {

@@ -20,7 +20,7 @@
 namespace {
 
 thread_local char g_error[512] = "";
-std::atomic<int> g_schedule{JFA_SCHED_SORTED_ZIGZAG};
+std::atomic<int> g_schedule{JFA_SCHED_DYNAMIC};
 
 jfa_status_t fail(jfa_status_t st, const char* fmt, ...) {
   va_list ap;
