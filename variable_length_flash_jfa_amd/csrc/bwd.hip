@@ -387,11 +387,13 @@ struct BwdKernel {
     }
   }
 
-  // Reduce-add of a block's dQ slice into the fp32 accumulator with buffer atomics.
-  // Register r holds query row 8 (r / 4) + 4 (lane / 32) + r % 4; one descriptor per
-  // group of four rows bounds the group, so rows past the query end fall outside
-  // the buffer range and are dropped by the hardware.
-  __device__ __forceinline__ void dq_atomics(const f32x16& dq, int qi0) {
+  // Reduce-add of rows 8 g .. 8 g + 7 (g = g0 .. g0 + NG - 1) of a block's dQ slice
+  // into the fp32 accumulator with buffer atomics; vals[k] holds registers 4 (g0 + k)
+  // .. + 3, i.e. rows 8 g + 4 (lane / 32) + e.  One descriptor per group bounds the
+  // group, so rows past the query end fall outside the buffer range and are dropped
+  // by the hardware.
+  template <int NG>
+  __device__ __forceinline__ void dq_atomics(const f32x4 (&vals)[NG], int g0, int qi0) {
     const int rows = min(q_rows - qi0, BQ);
     const int64_t qrow0 = BCAST ? (int64_t)(blockIdx.x & (kDqStripes - 1)) * a.q_len + qi0 : kv0 + qi0;
     const uint32_t row_bytes = (uint32_t)(a.heads * D * 4);
@@ -399,62 +401,65 @@ struct BwdKernel {
     const uint32_t o0 = launder(dq_lane_off);
     const uint32_t o[4] = {o0, o0 + row_bytes, o0 + 2 * row_bytes, o0 + 3 * row_bytes};
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int k = 0; k < NG; ++k) {
+      const int g = g0 + k;
       const int grow = max(rows - 8 * g, 0);
       const rsrc_t acc = make_rsrc(base + (int64_t)(8 * g) * a.heads * D, (uint32_t)grow * row_bytes);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dq[4 * g + e], acc, o[e], 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(vals[k][e], acc, o[e], 0, 0);
     }
   }
+  __device__ __forceinline__ void dq_atomics_all(const f32x16& dq, int qi0) {
+    const f32x4 v[4] = {{dq[0], dq[1], dq[2], dq[3]},
+                        {dq[4], dq[5], dq[6], dq[7]},
+                        {dq[8], dq[9], dq[10], dq[11]},
+                        {dq[12], dq[13], dq[14], dq[15]}};
+    dq_atomics<4>(v, 0, qi0);
+  }
 
-  // After a barrier: part-0 waves sum the parts' partials and reduce-add them.
+  // Rows handled by each key part in the flush: 32 / KP rows, 16 / KP reduce-adds.
+  static constexpr int FLUSH_GROUPS = 4 / KP;
+
+  // After a barrier: every wave sums the parts' partials of its d tile over the rows
+  // of its own key part (groups dq_part FLUSH_GROUPS ..) and reduce-adds them, so
+  // the flush work is spread evenly over the parts.
   __device__ __forceinline__ void dq_flush(int qi0) {
-    if (dq_part != 0) return;
-    f32x16 dq;
-    {
-      const float* srcp = dq_partial(0, dq_dt);
+    const int g0 = dq_part * FLUSH_GROUPS;
+    f32x4 v[FLUSH_GROUPS];
 #pragma unroll
-      for (int r = 0; r < 16; r += 4) {
-        const f32x4 v4 = *reinterpret_cast<const f32x4*>(srcp + (r / 4) * 256 + lane * 4);
-        dq[r] = v4[0];
-        dq[r + 1] = v4[1];
-        dq[r + 2] = v4[2];
-        dq[r + 3] = v4[3];
-      }
-    }
+    for (int k = 0; k < FLUSH_GROUPS; ++k)
+      v[k] = *reinterpret_cast<const f32x4*>(dq_partial(0, dq_dt) + (g0 + k) * 256 + lane * 4);
 #pragma unroll
     for (int p = 1; p < KP; ++p) {
       if (p < nparts) {
-        const float* srcp = dq_partial(p, dq_dt);
 #pragma unroll
-        for (int r = 0; r < 16; r += 4) {
-          const f32x4 v4 = *reinterpret_cast<const f32x4*>(srcp + (r / 4) * 256 + lane * 4);
-          dq[r] += v4[0];
-          dq[r + 1] += v4[1];
-          dq[r + 2] += v4[2];
-          dq[r + 3] += v4[3];
+        for (int k = 0; k < FLUSH_GROUPS; ++k) {
+          const f32x4 w = *reinterpret_cast<const f32x4*>(dq_partial(p, dq_dt) + (g0 + k) * 256 + lane * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[k][e] += w[e];
         }
       }
     }
-    dq_atomics(dq, qi0);
+    dq_atomics<FLUSH_GROUPS>(v, g0, qi0);
   }
 
   // Query-block loop.  Iteration t issues the LDS loads of block t + 1, computes the
   // dQ partial of block t - 1 (its dS^T is still in LDS), then block t.  With one key
   // part a wave reduce-adds its partial at once and the barrier that retires the
   // readers of dS^T(t - 1) sits inside block t, before its dS^T write; with
-  // several, the partials are published to LDS, a barrier follows, and part 0 sums
-  // and reduce-adds them before block t.  Vector memory operations retire in issue
-  // order, so the wait before the closing barrier (for the loads) leaves the 16
-  // reduce-adds issued after them in flight.
+  // several, the partials are published to LDS, a barrier follows, and every part
+  // sums and reduce-adds its share of the rows before block t.  Vector memory
+  // operations retire in issue order, so the wait before the closing barrier (for
+  // the loads) leaves the reduce-adds issued after them in flight; the last block
+  // loads nothing and does not wait.
   template <bool MASKED>
   __device__ __forceinline__ void run(int qs, int qe, int q_last, int& pending) {
     for (int qi0 = qs; qi0 < qe; qi0 += BQ) {
       const int buf = (qi0 / BQ) & 1;
       if (qi0 + BQ < q_last) load_qblock(qi0 + BQ, buf ^ 1);   // one block ahead
       if constexpr (KP == 1) {
-        if (pending >= 0) dq_atomics(dq_compute(), pending);
+        if (pending >= 0) dq_atomics_all(dq_compute(), pending);
         qblock<MASKED, true>(buf, qi0);
       } else {
         if (pending >= 0 && dq_part < nparts) dq_publish(dq_compute());
@@ -463,8 +468,8 @@ struct BwdKernel {
         qblock<MASKED, false>(buf, qi0);
       }
       if (qi0 + BQ < q_last) {   // the next block's loads must have landed
-        if (pending >= 0 && dq_part == 0) {
-          wait_lds_loads_but_16();
+        if (pending >= 0) {
+          wait_vmcnt<4 * FLUSH_GROUPS>();   // the reduce-adds issued after them stay in flight
         } else {
           wait_lds_loads();
         }
@@ -568,7 +573,7 @@ struct BwdKernel {
     if (more) issue_v(ng);
     if (pending >= 0) {
       if constexpr (KP == 1) {
-        dq_atomics(dq_compute(), pending);
+        dq_atomics_all(dq_compute(), pending);
       } else {
         if (dq_part < nparts) dq_publish(dq_compute());
         __syncthreads();

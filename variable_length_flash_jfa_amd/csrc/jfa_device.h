@@ -227,9 +227,14 @@ __device__ __forceinline__ void lds_load4(u32x4 r, uint32_t voff, char* lds) {
 }
 // s_waitcnt vmcnt(0): all of this wave's vector memory operations are complete.
 __device__ __forceinline__ void wait_lds_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-// s_waitcnt vmcnt(16): all but the 16 most recently issued vector memory operations
-// are complete (they retire in issue order).
-__device__ __forceinline__ void wait_lds_loads_but_16() { __builtin_amdgcn_s_waitcnt(0x4F70); }
+// s_waitcnt vmcnt(N): all but the N most recently issued vector memory operations are
+// complete (they retire in issue order).  gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt (7) and lgkmcnt (15) left unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // Copies rows [0, nrows) of a [rows][D] bf16 tile (row r at byte r * row_bytes of
 // the buffer, row_bytes a multiple of 2 D) into a swizzled LDS tile.  Each wave
