@@ -105,6 +105,9 @@ SMALL_CASES = {
     "self_d64": ([2, 33, 190, 257], 3, 64, False, False, 0),
     "self_empty_seq_causal": ([20, 0, 45], 2, 128, False, True, 0),
     "block64": ([64] * 40, 4, 128, False, False, 0),
+    # every sequence within one backward tile: dQ is written by the tiles directly
+    "self_d64_short_causal": ([3, 64, 100, 128, 1], 2, 64, False, True, 0),
+    "self_d128_short": ([128, 1, 77, 100], 3, 128, False, False, 0),
 }
 
 

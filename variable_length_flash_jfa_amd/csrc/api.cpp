@@ -286,19 +286,20 @@ jfa_status_t jfa_bwd(const void* q, const void* k, const void* v, const void* of
   float* dq_acc = reinterpret_cast<float*>(carve(cur, (size_t)acc_elems * sizeof(float)));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int sched = g_schedule.load();
-  hipError_t e = timed_launch("bwd_pre", s, [&] {
-    return jfa::launch_bwd_pre(p, o, d_o, lse, rowstat, dq_acc, acc_elems, s);
+  hipError_t e = timed_launch("plan_bwd", s, [&] { return jfa::launch_plan_bwd(p, plan, sched, s); });
+  if (e != hipSuccess) return hip_fail(e, "jfa_bwd: plan launch");
+  e = timed_launch("bwd_pre", s, [&] {
+    return jfa::launch_bwd_pre(p, o, d_o, lse, rowstat, dq_acc, acc_elems, plan.meta, s);
   });
   if (e != hipSuccess) return hip_fail(e, "jfa_bwd: delta launch");
   if (p.total_kv > 0) {
-    e = timed_launch("plan_bwd", s, [&] { return jfa::launch_plan_bwd(p, plan, sched, s); });
-    if (e != hipSuccess) return hip_fail(e, "jfa_bwd: plan launch");
     e = timed_launch("bwd", s, [&] {
-      return jfa::launch_bwd(p, plan, sched, rowstat, d_o, dq_acc, dk, dv, s);
+      return jfa::launch_bwd(p, plan, sched, rowstat, d_o, dq_acc, dq, dk, dv, s);
     });
     if (e != hipSuccess) return hip_fail(e, "jfa_bwd: kernel launch");
   }
-  e = timed_launch("dq_finalize", s, [&] { return jfa::launch_dq_finalize(p, dq_acc, dq, s); });
+  e = timed_launch("dq_finalize", s,
+                   [&] { return jfa::launch_dq_finalize(p, dq_acc, dq, plan.meta, s); });
   if (e != hipSuccess) return hip_fail(e, "jfa_bwd: dq finalize launch");
   return JFA_OK;
 }

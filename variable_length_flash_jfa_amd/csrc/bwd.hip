@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o
                                                        const float* __restrict__ lse,
                                                        float2* __restrict__ rowstat, int64_t rows,
                                                        int heads, float* __restrict__ dq_acc,
-                                                       int64_t acc_vec4) {
+                                                       int64_t acc_vec4, const int* __restrict__ meta) {
   constexpr int TPR = D / 8;                 // threads per (row, head)
   const int64_t pair = ((int64_t)blockIdx.x * 256 + threadIdx.x) / TPR;   // row * heads + h
   const int part = threadIdx.x % TPR;
@@ -65,7 +65,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o
     const int64_t i = (pair - row * heads) * rows + row;   // [head][row]
     rowstat[i] = make_float2(lse[i] * kLog2e, s);
   }
-  // grid-stride zero fill of the dQ accumulator
+  // grid-stride zero fill of the dQ accumulator (unless the tiles write dQ directly)
+  if (meta[3] != 0) return;
   const int64_t nthreads = (int64_t)gridDim.x * 256;
   float4* acc = reinterpret_cast<float4*>(dq_acc);
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < acc_vec4; i += nthreads)
@@ -89,6 +90,7 @@ struct BwdArgs {
   float scale_log2;
   float scale;
   float* dq_acc;
+  bf16* dq;        // written directly when every tile holds a whole sequence
   bf16* dk;
   bf16* dv;
   const int4* items;
@@ -137,6 +139,7 @@ struct BwdKernel {
   int lane, wave, c32, hf;
   int64_t rs;
   int dq_dt, dq_part;    // this wave's d tile and key part in the dQ product
+  bool direct;           // self mode, every sequence in one tile: dQ stored, not reduce-added
 
   // per tile
   int64_t kv0;           // first K/V row of the sequence
@@ -164,6 +167,7 @@ struct BwdKernel {
     rs = (int64_t)a.heads * D;
     dq_dt = wave % DT;
     dq_part = wave / DT;
+    direct = !BCAST && __builtin_amdgcn_readfirstlane(a.meta[3]) != 0;
     row_base = row_read_base<D>(lane);
     k_row_base = row_base + (uint32_t)(OFF_K + 32 * wave * 2 * D);
     tr4_base = tr_read_base<D>(lane, 4 * hf);
@@ -395,6 +399,26 @@ struct BwdKernel {
   template <int NG>
   __device__ __forceinline__ void dq_atomics(const f32x4 (&vals)[NG], int g0, int qi0) {
     const int rows = min(q_rows - qi0, BQ);
+    if (direct) {
+      // the tile holds every key of these queries: dQ = c dS K is final, one bf16 per
+      // (row, column) with the same row grouping and bounds
+      const uint32_t row_bytes = (uint32_t)(a.heads * D * 2);
+      bf16* base = a.dq + ((kv0 + qi0) * a.heads + h) * D;
+      const uint32_t o0 = launder(dq_lane_off) >> 1;   // fp32 lane offset -> bf16
+      const uint32_t o[4] = {o0, o0 + row_bytes, o0 + 2 * row_bytes, o0 + 3 * row_bytes};
+#pragma unroll
+      for (int k = 0; k < NG; ++k) {
+        const int g = g0 + k;
+        const int grow = max(rows - 8 * g, 0);
+        const rsrc_t out = make_rsrc(base + (int64_t)(8 * g) * a.heads * D, (uint32_t)grow * row_bytes);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16 v = (bf16)(vals[k][e] * a.scale);
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), out, o[e], 0, 0);
+        }
+      }
+      return;
+    }
     const int64_t qrow0 = BCAST ? (int64_t)(blockIdx.x & (kDqStripes - 1)) * a.q_len + qi0 : kv0 + qi0;
     const uint32_t row_bytes = (uint32_t)(a.heads * D * 4);
     float* base = a.dq_acc + (qrow0 * a.heads + h) * D;
@@ -649,7 +673,8 @@ void bwd_kernel(BwdArgs a) {
 __global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restrict__ acc,
                                                           bf16* __restrict__ dq, int64_t n_vec4,
                                                           int64_t stripe_vec4, int stripes,
-                                                          float scale) {
+                                                          float scale, const int* __restrict__ meta) {
+  if (meta[3] != 0) return;   // the tiles wrote dQ
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n_vec4) return;
   const float4* a4 = reinterpret_cast<const float4*>(acc);
@@ -708,7 +733,8 @@ int64_t bwd_max_items(const Problem& p) {
 }
 
 hipError_t launch_bwd_pre(const Problem& p, const void* o, const void* d_o, const float* lse,
-                          float* rowstat, float* dq_acc, int64_t dq_acc_elems, hipStream_t s) {
+                          float* rowstat, float* dq_acc, int64_t dq_acc_elems, const int* meta,
+                          hipStream_t s) {
   const int64_t pairs = p.rows * p.heads;
   const int tpr = p.head_dim / 8;
   int64_t blocks = (pairs * tpr + 255) / 256;
@@ -718,16 +744,16 @@ hipError_t launch_bwd_pre(const Problem& p, const void* o, const void* d_o, cons
   if (p.head_dim == 128)
     hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s,
                        static_cast<const bf16*>(o), static_cast<const bf16*>(d_o), lse, rs2, p.rows,
-                       p.heads, dq_acc, vec4);
+                       p.heads, dq_acc, vec4, meta);
   else
     hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s,
                        static_cast<const bf16*>(o), static_cast<const bf16*>(d_o), lse, rs2, p.rows,
-                       p.heads, dq_acc, vec4);
+                       p.heads, dq_acc, vec4, meta);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd(const Problem& p, const Plan& plan, int sched, const float* rowstat,
-                      const void* d_o, float* dq_acc, void* dk, void* dv, hipStream_t s) {
+                      const void* d_o, float* dq_acc, void* dq, void* dk, void* dv, hipStream_t s) {
   BwdArgs a;
   a.q = static_cast<const bf16*>(p.q);
   a.k = static_cast<const bf16*>(p.k);
@@ -742,6 +768,7 @@ hipError_t launch_bwd(const Problem& p, const Plan& plan, int sched, const float
   a.scale_log2 = p.scale * kLog2e;
   a.scale = p.scale;
   a.dq_acc = dq_acc;
+  a.dq = static_cast<bf16*>(dq);
   a.dk = static_cast<bf16*>(dk);
   a.dv = static_cast<bf16*>(dv);
   a.items = plan.items;
@@ -750,14 +777,15 @@ hipError_t launch_bwd(const Problem& p, const Plan& plan, int sched, const float
   return p.head_dim == 128 ? launch_bwd_d<128>(p, a, s) : launch_bwd_d<64>(p, a, s);
 }
 
-hipError_t launch_dq_finalize(const Problem& p, const float* dq_acc, void* dq, hipStream_t s) {
+hipError_t launch_dq_finalize(const Problem& p, const float* dq_acc, void* dq, const int* meta,
+                              hipStream_t s) {
   const int64_t q_rows = p.broadcast ? p.q_len : p.total_kv;
   const int64_t n = q_rows * p.heads * p.head_dim;
   const int64_t vec4 = n / 4;
   const int64_t blocks = (vec4 + 255) / 256;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(dq_finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, s, dq_acc,
-                     static_cast<bf16*>(dq), vec4, vec4, p.broadcast ? kDqStripes : 1, p.scale);
+                     static_cast<bf16*>(dq), vec4, vec4, p.broadcast ? kDqStripes : 1, p.scale, meta);
   return hipGetLastError();
 }
 

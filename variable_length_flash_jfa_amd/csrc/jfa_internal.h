@@ -34,8 +34,9 @@ struct Problem {
 };
 
 // Plan written on the device: meta[0] = number of items, meta[1] = dynamic-schedule
-// counter, meta[2] = number of tiles.  items[i] = (sequence b, block, offsets[b],
-// offsets[b + 1] - offsets[b]).
+// counter, meta[2] = number of tiles, meta[3] (backward) = 1 when every tile holds a
+// whole self-mode sequence and writes its dQ directly.  items[i] = (sequence b,
+// block, offsets[b], offsets[b + 1] - offsets[b]).
 struct Plan {
   int* meta;
   int4* items;
@@ -52,12 +53,16 @@ hipError_t launch_fwd(const Problem& p, const Plan& plan, int sched, void* o, fl
                       hipStream_t s);
 
 // rowstat: [heads][rows] pairs (LSE log2 e, delta = rowsum(dO * O)), 2 floats each.
+// Runs after the backward plan: the dQ accumulator is zeroed unless meta[3] is set.
 hipError_t launch_bwd_pre(const Problem& p, const void* o, const void* d_o, const float* lse,
-                          float* rowstat, float* dq_acc, int64_t dq_acc_elems, hipStream_t s);
+                          float* rowstat, float* dq_acc, int64_t dq_acc_elems, const int* meta,
+                          hipStream_t s);
 hipError_t launch_plan_bwd(const Problem& p, const Plan& plan, int sched, hipStream_t s);
 hipError_t launch_bwd(const Problem& p, const Plan& plan, int sched, const float* rowstat,
-                      const void* d_o, float* dq_acc, void* dk, void* dv, hipStream_t s);
-hipError_t launch_dq_finalize(const Problem& p, const float* dq_acc, void* dq, hipStream_t s);
+                      const void* d_o, float* dq_acc, void* dq, void* dk, void* dv, hipStream_t s);
+// Does nothing when meta[3] is set (the tiles wrote dQ).
+hipError_t launch_dq_finalize(const Problem& p, const float* dq_acc, void* dq, const int* meta,
+                              hipStream_t s);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

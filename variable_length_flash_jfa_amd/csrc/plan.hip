@@ -197,16 +197,22 @@ struct PlanBwdArgs {
   int batch;
   int heads;
   int bn;          // keys per backward tile
+  int self_mode;   // queries are the packed sequences themselves
   int4* items;
   int* meta;
 };
 
 // Valid (sequence, K/V block) pairs in natural order; tile t = (items[t / H], t % H).
+// meta[3] = 1 when, in self mode, every sequence fits one tile: each tile then sees
+// all keys of its queries, so its dQ is final and is written directly.
 // Each item also carries the sequence's first row and length (int32: the library
 // rejects T >= 2^30), so a tile's geometry is one 16-byte load.
 __global__ __launch_bounds__(kPlanThreads) void plan_bwd_kernel(PlanBwdArgs a) {
   __shared__ int wave_sums[kPlanThreads / 64 + 1];
+  __shared__ int all_single;
   const int tid = threadIdx.x;
+  if (tid == 0) all_single = 1;
+  __syncthreads();
   const int per = (a.batch + kPlanThreads - 1) / kPlanThreads;
   const int b_begin = min(a.batch, tid * per);
   const int b_end = min(a.batch, b_begin + per);
@@ -214,6 +220,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_bwd_kernel(PlanBwdArgs a) {
   for (int b = b_begin; b < b_end; ++b) {
     const int64_t n = load_offset(a.offsets, a.off64, b + 1) - load_offset(a.offsets, a.off64, b);
     count += (int)((n + a.bn - 1) / a.bn);
+    if (n > a.bn) all_single = 0;   // every writer stores the same value
   }
   int total = 0;
   int pos = block_exclusive_scan(count, wave_sums, &total);
@@ -227,6 +234,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_bwd_kernel(PlanBwdArgs a) {
     a.meta[0] = total;
     a.meta[1] = 0;
     a.meta[2] = total * a.heads;
+    a.meta[3] = a.self_mode && all_single;   // read after the scan's barriers
   }
 }
 
@@ -256,6 +264,7 @@ hipError_t launch_plan_bwd(const Problem& p, const Plan& plan, int /*sched*/, hi
   a.batch = p.batch;
   a.heads = p.heads;
   a.bn = 32 * bwd_waves(p);
+  a.self_mode = !p.broadcast;
   a.items = plan.items;
   a.meta = plan.meta;
   hipLaunchKernelGGL(plan_bwd_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
