@@ -111,7 +111,8 @@ struct BwdKernel {
   static constexpr int NT = 64 * NW;
   static constexpr int DT = D / 32;          // 32-wide d tiles
   static constexpr int KS = D / 16;          // 16-deep k steps over d
-  static constexpr int KP = NW / DT;         // key parts of the dQ product
+  static constexpr int DTW = DT > NW ? DT / NW : 1;   // d tiles of the dQ product per wave
+  static constexpr int KP = DT > NW ? 1 : NW / DT;    // key parts of the dQ product
   static constexpr int KPART = BN / KP;      // keys per part
   static constexpr int KT_BYTES = BN * D * 2;
   static constexpr int QT_BYTES = BQ * D * 2;
@@ -128,7 +129,7 @@ struct BwdKernel {
   static constexpr int SMEM = OFF_ROW + 2 * ROW_BYTES;
   static constexpr uint32_t GQ = OFF_DO - OFF_Q;              // dO tile minus Q tile, same buffer
   static constexpr int XB = D == 128 ? 256 : 128;             // the XOR-free granule
-  static_assert(BN == 32 * NW && KP * DT == NW && KPART % 16 == 0, "tile shape");
+  static_assert(BN == 32 * NW && KP * DT == NW * DTW && DTW <= 2 && KPART % 16 == 0, "tile shape");
   static_assert(OFF_Q + NW * 32 * 2 * D <= SMEM, "epilogue slots must fit behind the K tile region");
   static_assert(OFF_Q % XB == 0 && QT_BYTES % XB == 0 && GQ % XB == 0 && (KPART * 2 * D) % XB == 0 &&
                     (32 * 2 * D) % XB == 0 && OFF_DS % 64 == 0 && (KPART * BQ * 2) % 64 == 0,
@@ -138,7 +139,7 @@ struct BwdKernel {
   char* smem;
   int lane, wave, c32, hf;
   int64_t rs;
-  int dq_dt, dq_part;    // this wave's d tile and key part in the dQ product
+  int dq_dt, dq_part;    // this wave's (first) d tile and key part in the dQ product
   bool direct;           // self mode, every sequence in one tile: dQ stored, not reduce-added
 
   // per tile
@@ -165,8 +166,8 @@ struct BwdKernel {
     c32 = lane & 31;
     hf = lane >> 5;
     rs = (int64_t)a.heads * D;
-    dq_dt = wave % DT;
-    dq_part = wave / DT;
+    dq_dt = (wave % (DT / DTW)) * DTW;   // even when a wave takes two d tiles
+    dq_part = wave / (DT / DTW);
     direct = !BCAST && __builtin_amdgcn_readfirstlane(a.meta[3]) != 0;
     row_base = row_read_base<D>(lane);
     k_row_base = row_base + (uint32_t)(OFF_K + 32 * wave * 2 * D);
@@ -347,37 +348,67 @@ struct BwdKernel {
   // (d tile dq_dt) over all keys of its part.  The rows of keys past the sequence
   // end hold zeros (zero probability, or zeroed at the start of the tile for waves
   // with no key inside), so the loop needs no bounds.
-  __device__ __forceinline__ f32x16 dq_compute() {
+  __device__ __forceinline__ void dq_compute(f32x16 (&out)[DTW]) {
     const uint32_t dsb = launder(dsq_base);
     const uint32_t kb8 = launder(kq_base);
-    f32x16 acc0 = zero16(), acc1 = zero16();
     auto ds_op = [&](int jj) {   // dS[query l % 32][keys jj + 8 (l / 32) + e] of the part
       const uint32_t x = (uint32_t)(((jj >> 2) & 4) << 3);
       return cat(lds_read_tr(smem + ((dsb ^ x) + jj * (BQ * 2))),
                  lds_read_tr(smem + ((dsb ^ x ^ 8u) + (jj + 4) * (BQ * 2))));
     };
-    bf16x8 sa = ds_op(0);
-    bf16x8 kb = lds_operand_tr<D>(smem, kb8, 0, 4, 0);
+    if constexpr (DTW == 1) {
+      f32x16 acc0 = zero16(), acc1 = zero16();
+      bf16x8 sa = ds_op(0);
+      bf16x8 kb = lds_operand_tr<D>(smem, kb8, 0, 4, 0);
 #pragma unroll
-    for (int jj = 0; jj < KPART; jj += 16) {
-      bf16x8 sa_n = sa, kb_n = kb;
-      if (jj + 16 < KPART) {
-        sa_n = ds_op(jj + 16);
-        kb_n = lds_operand_tr<D>(smem, kb8, jj + 16, jj + 20, 0);
+      for (int jj = 0; jj < KPART; jj += 16) {
+        bf16x8 sa_n = sa, kb_n = kb;
+        if (jj + 16 < KPART) {
+          sa_n = ds_op(jj + 16);
+          kb_n = lds_operand_tr<D>(smem, kb8, jj + 16, jj + 20, 0);
+        }
+        // two independent accumulators halve the dependent-MFMA chain
+        if ((jj / 16) & 1) {
+          acc1 = mfma32(sa, kb, acc1);
+        } else {
+          acc0 = mfma32(sa, kb, acc0);
+        }
+        sa = sa_n;
+        kb = kb_n;
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // two independent accumulators halve the dependent-MFMA chain
-      if ((jj / 16) & 1) {
-        acc1 = mfma32(sa, kb, acc1);
-      } else {
-        acc0 = mfma32(sa, kb, acc0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc0[r] += acc1[r];
+      out[0] = acc0;
+    } else {
+      // two d tiles (the second one's chunk index is the first's plus one, an XOR
+      // since the first is even): two independent chains sharing the dS operand
+      out[0] = zero16();
+      out[DTW - 1] = zero16();
+      bf16x8 sa = ds_op(0);
+      bf16x8 k0 = lds_operand_tr<D>(smem, kb8, 0, 4, 0);
+      bf16x8 k1 = lds_operand_tr<D>(smem, kb8, 0, 4, 1);
+#pragma unroll
+      for (int jj = 0; jj < KPART; jj += 16) {
+        bf16x8 sa_n = sa, k0_n = k0, k1_n = k1;
+        if (jj + 16 < KPART) {
+          sa_n = ds_op(jj + 16);
+          k0_n = lds_operand_tr<D>(smem, kb8, jj + 16, jj + 20, 0);
+          k1_n = lds_operand_tr<D>(smem, kb8, jj + 16, jj + 20, 1);
+        }
+        out[0] = mfma32(sa, k0, out[0]);
+        out[DTW - 1] = mfma32(sa, k1, out[DTW - 1]);
+        sa = sa_n;
+        k0 = k0_n;
+        k1 = k1_n;
+        __builtin_amdgcn_sched_barrier(0);
       }
-      sa = sa_n;
-      kb = kb_n;
-      __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc0[r] += acc1[r];
-    return acc0;
+  }
+  __device__ __forceinline__ f32x16 dq_compute1() {
+    f32x16 o[DTW];
+    dq_compute(o);
+    return o[0];
   }
 
   // Several key parts: every part with keys publishes its partial to LDS (summed by
@@ -397,14 +428,14 @@ struct BwdKernel {
   // group, so rows past the query end fall outside the buffer range and are dropped
   // by the hardware.
   template <int NG>
-  __device__ __forceinline__ void dq_atomics(const f32x4 (&vals)[NG], int g0, int qi0) {
+  __device__ __forceinline__ void dq_atomics(const f32x4 (&vals)[NG], int g0, int qi0, int dtk = 0) {
     const int rows = min(q_rows - qi0, BQ);
     if (direct) {
       // the tile holds every key of these queries: dQ = c dS K is final, one bf16 per
       // (row, column) with the same row grouping and bounds
       const uint32_t row_bytes = (uint32_t)(a.heads * D * 2);
       bf16* base = a.dq + ((kv0 + qi0) * a.heads + h) * D;
-      const uint32_t o0 = launder(dq_lane_off) >> 1;   // fp32 lane offset -> bf16
+      const uint32_t o0 = (launder(dq_lane_off) >> 1) + 64u * dtk;   // fp32 lane offset -> bf16
       const uint32_t o[4] = {o0, o0 + row_bytes, o0 + 2 * row_bytes, o0 + 3 * row_bytes};
 #pragma unroll
       for (int k = 0; k < NG; ++k) {
@@ -422,7 +453,7 @@ struct BwdKernel {
     const int64_t qrow0 = BCAST ? (int64_t)(blockIdx.x & (kDqStripes - 1)) * a.q_len + qi0 : kv0 + qi0;
     const uint32_t row_bytes = (uint32_t)(a.heads * D * 4);
     float* base = a.dq_acc + (qrow0 * a.heads + h) * D;
-    const uint32_t o0 = launder(dq_lane_off);
+    const uint32_t o0 = launder(dq_lane_off) + 128u * dtk;
     const uint32_t o[4] = {o0, o0 + row_bytes, o0 + 2 * row_bytes, o0 + 3 * row_bytes};
 #pragma unroll
     for (int k = 0; k < NG; ++k) {
@@ -434,12 +465,18 @@ struct BwdKernel {
         __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(vals[k][e], acc, o[e], 0, 0);
     }
   }
-  __device__ __forceinline__ void dq_atomics_all(const f32x16& dq, int qi0) {
-    const f32x4 v[4] = {{dq[0], dq[1], dq[2], dq[3]},
-                        {dq[4], dq[5], dq[6], dq[7]},
-                        {dq[8], dq[9], dq[10], dq[11]},
-                        {dq[12], dq[13], dq[14], dq[15]}};
-    dq_atomics<4>(v, 0, qi0);
+  // One key part: reduce-add (or store) every row of this wave's d tile(s).
+  __device__ __forceinline__ void dq_atomics_all(int qi0) {
+    f32x16 dq[DTW];
+    dq_compute(dq);
+#pragma unroll
+    for (int k = 0; k < DTW; ++k) {
+      const f32x4 v[4] = {{dq[k][0], dq[k][1], dq[k][2], dq[k][3]},
+                          {dq[k][4], dq[k][5], dq[k][6], dq[k][7]},
+                          {dq[k][8], dq[k][9], dq[k][10], dq[k][11]},
+                          {dq[k][12], dq[k][13], dq[k][14], dq[k][15]}};
+      dq_atomics<4>(v, 0, qi0, k);
+    }
   }
 
   // Rows handled by each key part in the flush: 32 / KP rows, 16 / KP reduce-adds.
@@ -483,17 +520,17 @@ struct BwdKernel {
       const int buf = (qi0 / BQ) & 1;
       if (qi0 + BQ < q_last) load_qblock(qi0 + BQ, buf ^ 1);   // one block ahead
       if constexpr (KP == 1) {
-        if (pending >= 0) dq_atomics_all(dq_compute(), pending);
+        if (pending >= 0) dq_atomics_all(pending);
         qblock<MASKED, true>(buf, qi0);
       } else {
-        if (pending >= 0 && dq_part < nparts) dq_publish(dq_compute());
+        if (pending >= 0 && dq_part < nparts) dq_publish(dq_compute1());
         __syncthreads();
         if (pending >= 0) dq_flush(pending);
         qblock<MASKED, false>(buf, qi0);
       }
       if (qi0 + BQ < q_last) {   // the next block's loads must have landed
         if (pending >= 0) {
-          wait_vmcnt<4 * FLUSH_GROUPS>();   // the reduce-adds issued after them stay in flight
+          wait_vmcnt<4 * FLUSH_GROUPS * DTW>();   // the reduce-adds issued after them stay in flight
         } else {
           wait_lds_loads();
         }
@@ -597,9 +634,9 @@ struct BwdKernel {
     if (more) issue_v(ng);
     if (pending >= 0) {
       if constexpr (KP == 1) {
-        dq_atomics_all(dq_compute(), pending);
+        dq_atomics_all(pending);
       } else {
-        if (dq_part < nparts) dq_publish(dq_compute());
+        if (dq_part < nparts) dq_publish(dq_compute1());
         __syncthreads();
         dq_flush(pending);
       }
@@ -712,7 +749,10 @@ hipError_t launch_bwd_dw(const Problem& p, const BwdArgs& a, hipStream_t s) {
 
 template <int D>
 hipError_t launch_bwd_d(const Problem& p, const BwdArgs& a, hipStream_t s) {
-  return bwd_waves(p) == 8 ? launch_bwd_dw<D, 8>(p, a, s) : launch_bwd_dw<D, 4>(p, a, s);
+  const int nw = bwd_waves(p);
+  if (nw == 8) return launch_bwd_dw<D, 8>(p, a, s);
+  if (nw == 4) return launch_bwd_dw<D, 4>(p, a, s);
+  return launch_bwd_dw<D, 2>(p, a, s);
 }
 
 }  // namespace
@@ -720,10 +760,12 @@ hipError_t launch_bwd_d(const Problem& p, const BwdArgs& a, hipStream_t s) {
 // Eight waves (256-key tiles) halve the dQ reduce-adds per key.  In broadcast mode
 // every tile adds into the one shared dQ, so that always pays; in self mode it pays
 // when a tile's query loop is long, and four waves (128-key tiles) waste less on
-// short sequences.
+// short sequences.  Sequences of about 64 keys take two waves (64-key tiles, each
+// wave computing two d tiles of dQ), so that no wave of a tile sits idle.
 int bwd_waves(const Problem& p) {
   if (p.broadcast) return 8;
   const int64_t mean_len = p.batch > 0 ? p.total_kv / p.batch : 0;
+  if (mean_len <= 96) return 2;   // 64-key tiles for short sequences
   return mean_len >= 512 ? 8 : 4;
 }
 

@@ -46,7 +46,7 @@ struct Plan {
 int fwd_waves(const Problem& p);                 // waves per forward workgroup
 int64_t fwd_max_items(const Problem& p);         // capacity of the forward item list
 int64_t bwd_max_items(const Problem& p);         // capacity of the backward item list
-int bwd_waves(const Problem& p);                 // waves per backward workgroup (4 or 8)
+int bwd_waves(const Problem& p);                 // waves per backward workgroup (2, 4 or 8)
 
 hipError_t launch_plan_fwd(const Problem& p, const Plan& plan, int sched, hipStream_t s);
 hipError_t launch_fwd(const Problem& p, const Plan& plan, int sched, void* o, float* lse,
