@@ -14,7 +14,9 @@
 //    S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16, so that the
 //    fp32 score accumulator is already laid out as the bf16 P operand;
 //  * K/V blocks of 64 keys stream straight from HBM into swizzled LDS (gfx950
-//    direct global->LDS loads, double buffered) one block ahead of the MFMA work;
+//    direct global->LDS loads, double buffered) one block ahead of the MFMA work,
+//    across tile boundaries too: the next tile's first block and Q fragment load
+//    during the current tile's last block and epilogue;
 //    V^T operands come from the gfx950 transposing LDS read;
 //  * online softmax in the exp2 domain with a running max and a lane-local running
 //    sum (the two halves of a wave hold the two halves of a row's keys and are
@@ -57,8 +59,14 @@ struct FwdKernel {
   static constexpr int TILE_BYTES = BN * D * 2;
   static constexpr int DT = D / 32;              // 32-wide d tiles of O
   static constexpr int KS = D / 16;              // 16-deep k steps of Q K^T
+  static constexpr int PF_S = 2;                 // operand reads in flight ahead of the S MFMAs
+  static constexpr int PF_V = 3;                 // ... and of the O MFMAs
   static_assert((BN * D * 2 / 1024) % NW == 0, "a K/V block must split evenly over the waves");
-  static_assert(NW * 32 * 2 * D <= 4 * TILE_BYTES, "epilogue slots must fit in the K/V buffers");
+  // The epilogue stages O through one K/V buffer (K and V tiles) while the next
+  // tile's first block lands in the other; with eight waves it takes two passes.
+  static constexpr int EPI_PASSES = NW * 32 * 2 * D > 2 * TILE_BYTES ? 2 : 1;
+  static constexpr int SLOT_BYTES = 32 * 2 * D / EPI_PASSES;
+  static_assert(NW * SLOT_BYTES <= 2 * TILE_BYTES, "epilogue slots must fit in one K/V buffer");
 
   // Tile-invariant per-wave state.
   FwdArgs a;
@@ -66,9 +74,15 @@ struct FwdKernel {
   int lane, wave, c32, hf;
   int64_t rs;          // row stride (elements) of q, k, v, o
 
+  // Tile geometry: sequence b with K/V rows [kv0, kv0 + n), query block m, head h.
+  struct Geo {
+    int64_t kv0;
+    int n, b, m, h;
+  };
+
   // Per-tile state.
-  int64_t kv0, n;
-  int h, q_rows, m0, i0;
+  Geo g;               // the current tile
+  int q_rows, m0, i0;
   int64_t out_row0;    // first output row of the sequence
   bf16x8 qf[KS];
   f32x16 acc[DT];
@@ -89,13 +103,48 @@ struct FwdKernel {
   __device__ __forceinline__ char* kbuf(int buf) { return smem + (buf * 2 + 0) * TILE_BYTES; }
   __device__ __forceinline__ char* vbuf(int buf) { return smem + (buf * 2 + 1) * TILE_BYTES; }
 
-  // Issues the direct LDS loads of K/V block `blk` into buffer `buf`; rows past the
-  // sequence end read as zeros (and the masked tail gives them zero weight).
-  __device__ __forceinline__ void load_block(int blk, int buf) {
+  // Tile idx of the list: item `it` = (sequence, query block, first row, length).
+  __device__ __forceinline__ Geo geometry(int idx, int4 it, int per_item) const {
+    Geo t;
+    const int item = idx / per_item;
+    const int rem = idx - item * per_item;
+    t.b = __builtin_amdgcn_readfirstlane(it.x);
+    t.kv0 = __builtin_amdgcn_readfirstlane(it.z);
+    t.n = __builtin_amdgcn_readfirstlane(it.w);
+    if (BCAST) {
+      t.m = rem / a.heads;
+      t.h = rem % a.heads;
+    } else {
+      t.m = __builtin_amdgcn_readfirstlane(it.y);
+      t.h = rem;
+    }
+    return t;
+  }
+
+  // K/V blocks the tile visits.
+  __device__ __forceinline__ int num_blocks(const Geo& t) const {
+    const int64_t kv_end = CAUSAL ? min((int64_t)t.n, (int64_t)(t.m + 1) * BM) : (int64_t)t.n;
+    return (int)((kv_end + BN - 1) / BN);
+  }
+
+  // This wave's Q fragment of tile t (rows past the query end read as zeros).
+  __device__ __forceinline__ void load_q(const Geo& t) {
+    const int qr = BCAST ? a.q_len : t.n;
+    const int qi = t.m * BM + 32 * wave + c32;
+    const bool qvalid = qi < qr;
+    const bf16* qp = a.q + ((BCAST ? (int64_t)qi : t.kv0 + qi) * rs + (int64_t)t.h * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = qvalid ? *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * hf) : zero_bf16x8();
+  }
+
+  // Issues the direct LDS loads of K/V block `blk` of tile t into buffer `buf`; rows
+  // past the sequence end read as zeros (and the masked tail gives them zero weight).
+  __device__ __forceinline__ void load_block(const Geo& t, int blk, int buf) {
     const int64_t jb = (int64_t)blk * BN;
-    const int64_t rows = min(n - jb, (int64_t)BN);
+    const int64_t rows = max(min((int64_t)t.n - jb, (int64_t)BN), (int64_t)0);
     const uint32_t bytes = (uint32_t)(rows * rs * 2);
-    const int64_t base = (kv0 + jb) * rs + (int64_t)h * D;
+    const int64_t base = (t.kv0 + jb) * rs + (int64_t)t.h * D;
     const uint32_t row_bytes = (uint32_t)(rs * 2);
     lds_load_tile<D, NW>(kbuf(buf), BN, wave, lane, make_rsrc_sgpr(a.k + base, bytes), row_bytes);
     lds_load_tile<D, NW>(vbuf(buf), BN, wave, lane, make_rsrc_sgpr(a.v + base, bytes), row_bytes);
@@ -108,16 +157,29 @@ struct FwdKernel {
     const char* vb = vbuf(buf);
     const uint32_t krb = launder(k_row_base);
     const uint32_t vtb = launder(v_tr_base);
-    f32x16 s[2];
+    // S^T = K Q^T for the block's two 32-key halves as two interleaved MFMA chains
+    // (step i: k step i / 2, half i % 2).  Operands are read PF_S steps ahead of their
+    // MFMAs; the scheduling fences keep that pipeline as written.
+    auto kop = [&](int i) { return lds_read8(kb, row_read_addr(krb, i / 2) + 32 * (i % 2) * 2 * D); };
+    f32x16 s[2] = {zero16(), zero16()};
+    {
+      bf16x8 kr[PF_S + 1];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      s[c] = zero16();
+      for (int i = 0; i < PF_S; ++i) kr[i] = kop(i);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kf = lds_read8(kb, row_read_addr(krb, ks) + 32 * c * 2 * D);
-        s[c] = mfma32(kf, qf[ks], s[c]);
+      for (int i = 0; i < 2 * KS; ++i) {
+        if (i + PF_S < 2 * KS) kr[(i + PF_S) % (PF_S + 1)] = kop(i + PF_S);
+        s[i % 2] = mfma32(kr[i % (PF_S + 1)], qf[i / 2], s[i % 2]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // the first V^T operands of O^T += V^T P^T (step i: keys 16 (i / DT), d tile
+    // i % DT) are read before the softmax
+    auto vop = [&](int i) { return lds_operand_tr<D>(vb, vtb, 16 * (i / DT), 16 * (i / DT) + 8, i % DT); };
+    bf16x8 vr[PF_V + 1];
+#pragma unroll
+    for (int i = 0; i < PF_V; ++i) vr[i] = vop(i);
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (MASKED) {
       const int64_t i = i0 + c32;
 #pragma unroll
@@ -125,7 +187,7 @@ struct FwdKernel {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t j = (int64_t)blk * BN + 32 * c + 8 * (r >> 2) + 4 * hf + (r & 3);
-          bool vis = j < n;
+          bool vis = j < g.n;
           if constexpr (CAUSAL) vis = vis && (j <= i);
           s[c][r] = vis ? s[c][r] : -INFINITY;
         }
@@ -159,17 +221,14 @@ struct FwdKernel {
         }
       }
     }
+    // keys 16 ckc + 4 (lane / 32) + e, and + 8, with ckc = 2 c + kc
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const int jb = 32 * c + 16 * kc;   // keys jb + 4 (lane / 32) + e, and + 8
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const bf16x8 vt = lds_operand_tr<D>(vb, vtb, jb, jb + 8, dt);
-          acc[dt] = mfma32(vt, p[c][kc], acc[dt]);
-        }
-      }
+    for (int i = 0; i < 4 * DT; ++i) {
+      if (i + PF_V < 4 * DT) vr[(i + PF_V) % (PF_V + 1)] = vop(i + PF_V);
+      const int ckc = i / DT;
+      acc[i % DT] = mfma32(vr[i % (PF_V + 1)], p[ckc / 2][ckc % 2], acc[i % DT]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -179,95 +238,153 @@ struct FwdKernel {
     return true;
   }
 
+  // Blocks [t_begin, t_end) of the current tile; block t sits in buffer (pb + t) & 1.
+  // Each iteration first issues the loads of the block after it: the tile's own, or,
+  // after the last one, the first block of the next tile, which stays in flight
+  // through the epilogue (the last iteration does not wait).
   template <bool MASKED>
-  __device__ __forceinline__ void run_blocks(int t_begin, int t_end, int nblk) {
+  __device__ __forceinline__ void run_blocks(int t_begin, int t_end, int nblk, int pb, const Geo& nxt,
+                                             bool has_next) {
     for (int t = t_begin; t < t_end; ++t) {
-      if (t + 1 < nblk) load_block(t + 1, (t + 1) & 1);   // one block ahead
-      if (wave_needs(t)) compute_block<MASKED>(t & 1, t);
-      wait_lds_loads();
+      const int buf = (pb + t) & 1;
+      if (t + 1 < nblk) {
+        load_block(g, t + 1, buf ^ 1);
+      } else if (has_next) {
+        load_block(nxt, 0, buf ^ 1);
+      }
+      if (wave_needs(t)) compute_block<MASKED>(buf, t);
+      if (t + 1 < nblk) wait_lds_loads();
       __syncthreads();
     }
   }
 
-  // Tile (sequence b with rows [kv0, kv0 + len), query block m, head).
-  __device__ __forceinline__ void tile(int b, int m, int head, int seq_kv0, int seq_len) {
-    __syncthreads();   // the previous tile's epilogue is done with the K/V buffers
-    h = head;
-    kv0 = seq_kv0;
-    n = seq_len;
-    q_rows = BCAST ? a.q_len : (int)n;
-    m0 = m * BM;
+  // Runs tile g, whose first K/V block is in buffer pb and whose Q fragment is in
+  // qf (both loaded or in flight, the block published by a barrier).  After the last
+  // barrier over the K/V buffers it issues the next tile's Q fragment, runs
+  // `between`, and writes O and LSE, staging O through the buffer of the last block
+  // (the next tile's first block goes to the other).  Returns the next tile's pb.
+  template <class Between>
+  __device__ __forceinline__ int tile(int pb, const Geo& nxt, bool has_next, Between&& between) {
+    q_rows = BCAST ? a.q_len : g.n;
+    m0 = g.m * BM;
     i0 = m0 + 32 * wave;
-    out_row0 = BCAST ? (int64_t)b * a.q_len : kv0;
-
+    out_row0 = BCAST ? (int64_t)g.b * a.q_len : g.kv0;
     const int qi = i0 + c32;
     const bool qvalid = qi < q_rows;
-    const bf16* qp = a.q + ((BCAST ? (int64_t)qi : kv0 + qi) * rs + (int64_t)h * D);
+    // The Q fragment was loaded during the previous tile: consume it here so that the
+    // compiler's wait for it lands before the block loop, not inside it (where it
+    // would also wait for the next block's loads).
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = qvalid ? *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * hf) : zero_bf16x8();
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[ks]));
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
     mrun = kNegBig;
     lsum = 0.f;
 
-    const int64_t kv_end = CAUSAL ? min(n, (int64_t)m0 + BM) : n;
-    const int nblk = (int)((kv_end + BN - 1) / BN);
-    int nfull = (int)(n / BN);
+    const int nblk = num_blocks(g);
+    int nfull = (int)(g.n / BN);
     if constexpr (CAUSAL) nfull = min(nfull, (m0 + 1) / BN);
     nfull = min(nfull, nblk);
-
-    if (nblk > 0) load_block(0, 0);
-    wait_lds_loads();
-    __syncthreads();
-    run_blocks<false>(0, nfull, nblk);
-    run_blocks<true>(nfull, nblk, nblk);
+    run_blocks<false>(0, nfull, nblk, pb, nxt, has_next);
+    run_blocks<true>(nfull, nblk, nblk, pb, nxt, has_next);
+    if (nblk == 0) {   // an empty sequence (broadcast mode): no block barrier ran
+      __syncthreads();
+      if (has_next) load_block(nxt, 0, pb);
+    }
+    if (has_next) load_q(nxt);   // this tile is done with its Q fragment
+    between();
 
     // epilogue
     const float lt = sum_across_halves(lsum);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    // O rows staged through this wave's slot of the (now idle) K/V buffers
-    store_acc_rows<D>(acc, inv, smem + wave * (32 * 2 * D), a.o + ((out_row0 + i0) * rs + (int64_t)h * D), rs,
-                      min(max(q_rows - i0, 0), 32), lane);
+    char* slot = smem + ((pb + nblk + 1) & 1) * (2 * TILE_BYTES) + wave * SLOT_BYTES;
+    store_acc_rows<D, EPI_PASSES>(acc, inv, slot, a.o + ((out_row0 + i0) * rs + (int64_t)g.h * D), rs,
+                                  min(max(q_rows - i0, 0), 32), lane);
     if (qvalid && hf == 0)
-      a.lse[(int64_t)h * a.rows + out_row0 + qi] = lt > 0.f ? (mrun + __log2f(lt)) * kLn2 : -INFINITY;
+      a.lse[(int64_t)g.h * a.rows + out_row0 + qi] = lt > 0.f ? (mrun + __log2f(lt)) * kLn2 : -INFINITY;
+    return (pb + nblk) & 1;
   }
 };
 
+// Persistent tile loop.  A workgroup knows two tiles ahead: while tile r runs, the
+// index of tile r + 2 is claimed (or computed, for the static schedules) and, after
+// tile r's last block, its plan item is copied into LDS by a direct load, so that
+// tile r + 1's first K/V block and Q fragment can be issued during tile r.
 template <int D, int NW, bool BCAST, bool CAUSAL>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_kernel(FwdArgs a) {
   using K = FwdKernel<D, NW, BCAST, CAUSAL>;
+  using Geo = typename K::Geo;
   __shared__ __attribute__((aligned(16))) char smem[4 * K::TILE_BYTES];
-  __shared__ int claimed;
+  __shared__ __attribute__((aligned(16))) int next_item[64];   // one dword per lane of the copy
+  __shared__ int next_idx;
+  __shared__ int first_idx[2];
   K kern(a, smem);
   const int num_wg = gridDim.x;
   const int lwg = xcd_logical_wg(blockIdx.x, num_wg);
   const int ntiles = a.meta[2];
   const int per_item = BCAST ? ((a.q_len + K::BM - 1) / K::BM) * a.heads : a.heads;
+  const bool dyn = a.sched == kDynamic;
+  auto sched_idx = [&](int r) {
+    if (a.sched == kIdentity) return r * num_wg + lwg;
+    return r * num_wg + ((r & 1) ? (num_wg - 1 - lwg) : lwg);
+  };
+  auto fetch_item = [&](int idx) {   // plan item of tile idx -> next_item[0 .. 3]
+    lds_load4(make_rsrc_sgpr(a.items + idx / per_item, 16u), (uint32_t)kern.lane * 4u,
+              reinterpret_cast<char*>(next_item));
+  };
+
+  int idx0, idx1;
+  if (dyn) {
+    if (threadIdx.x == 0) {
+      first_idx[0] = atomicAdd(a.meta + 1, 1);
+      first_idx[1] = atomicAdd(a.meta + 1, 1);
+    }
+    __syncthreads();
+    idx0 = __builtin_amdgcn_readfirstlane(first_idx[0]);
+    idx1 = __builtin_amdgcn_readfirstlane(first_idx[1]);
+  } else {
+    idx0 = sched_idx(0);
+    idx1 = sched_idx(1);
+  }
+  if (idx0 >= ntiles) return;
+  kern.g = kern.geometry(idx0, a.items[idx0 / per_item], per_item);
+  if (kern.wave == 0) {
+    if (idx1 < ntiles) fetch_item(idx1);
+    if (threadIdx.x == 0) next_idx = idx1;
+  }
+  kern.load_q(kern.g);
+  if (kern.num_blocks(kern.g) > 0) kern.load_block(kern.g, 0, 0);
+
+  int pb = 0;
   for (int r = 0;; ++r) {
-    int idx;
-    if (a.sched == kDynamic) {
-      if (threadIdx.x == 0) claimed = atomicAdd(a.meta + 1, 1);
-      __syncthreads();
-      idx = claimed;
-      __syncthreads();
-    } else if (a.sched == kIdentity) {
-      idx = r * num_wg + lwg;
+    // Everything but the previous epilogue's D / 16 stores has landed: this tile's
+    // first block, its Q fragment and the next tile's item.
+    if (r == 0) {
+      wait_lds_loads();
     } else {
-      idx = r * num_wg + ((r & 1) ? (num_wg - 1 - lwg) : lwg);
+      wait_vmcnt<D / 16>();
     }
-    if (idx >= ntiles) break;
-    const int item = idx / per_item;
-    const int rem = idx - item * per_item;
-    const int4 it = a.items[item];
-    const int b = __builtin_amdgcn_readfirstlane(it.x), blk = __builtin_amdgcn_readfirstlane(it.y);
-    const int s0 = __builtin_amdgcn_readfirstlane(it.z), len = __builtin_amdgcn_readfirstlane(it.w);
-    if (BCAST) {
-      kern.tile(b, rem / a.heads, rem % a.heads, s0, len);
+    __syncthreads();
+    const int nidx = __builtin_amdgcn_readfirstlane(next_idx);
+    const bool has_next = nidx < ntiles;
+    Geo nxt = kern.g;
+    if (has_next) nxt = kern.geometry(nidx, *reinterpret_cast<const int4*>(next_item), per_item);
+    int pend = ntiles;   // index of tile r + 2 (lane 0 of wave 0 under the dynamic schedule)
+    if (dyn) {
+      if (threadIdx.x == 0) pend = atomicAdd(a.meta + 1, 1);
     } else {
-      kern.tile(b, blk, rem, s0, len);
+      pend = sched_idx(r + 2);
     }
+    pb = kern.tile(pb, nxt, has_next, [&]() {
+      if (has_next && kern.wave == 0) {
+        const int i2 = __builtin_amdgcn_readfirstlane(pend);
+        if (i2 < ntiles) fetch_item(i2);
+        if (threadIdx.x == 0) next_idx = i2;
+      }
+    });
+    if (!has_next) break;
+    kern.g = nxt;
   }
 }
 

@@ -288,31 +288,19 @@ __device__ __forceinline__ int xcd_logical_wg(int wg, int num_wg) {
 // and d = 32 dt + 8 (r / 4) + 4 (l / 32) + r % 4), to 32 consecutive rows of a bf16
 // array with a row pitch of `ld` elements, times the lane's `scale`.  Straight from
 // registers every store would cover 8 bytes of 32 different rows; instead the tile
-// is staged through a private LDS slot of 64 D bytes (16-byte chunks XOR-swizzled
-// by row) and read back so that each store instruction writes whole rows in
-// 16-byte pieces.  The stores go through a buffer descriptor spanning `nrows` rows,
-// so rows past the end are dropped by the hardware range check.
-template <int D>
+// is staged through a private LDS slot of 64 D / PASSES bytes (16-byte chunks
+// XOR-swizzled by row), 32 / PASSES rows per pass, and read back so that each store
+// instruction writes whole rows in 16-byte pieces.  The stores go through a buffer
+// descriptor spanning `nrows` rows, so rows past the end are dropped by the
+// hardware range check; every call issues exactly D / 16 store instructions.
+template <int D, int PASSES = 1>
 __device__ __forceinline__ void store_acc_rows(const f32x16 (&acc)[D / 32], float scale, char* slot,
                                                bf16* dst, int64_t ld, int nrows, int lane) {
-  constexpr int CH = D / 8;       // 16-byte chunks per row
-  constexpr int RPI = 64 / CH;    // rows per read instruction
+  constexpr int CH = D / 8;            // 16-byte chunks per row
+  constexpr int RPI = 64 / CH;         // rows per read instruction
+  constexpr int RPP = 32 / PASSES;     // rows per pass (the slot holds RPP rows)
+  static_assert(RPP % RPI == 0, "a pass must cover whole read instructions");
   const int r = lane & 31, hf = lane >> 5;
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      bf16x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[dt][4 * q4 + e] * scale);
-      const int c = 4 * dt + q4;   // chunk of d = 32 dt + 8 q4 + 4 hf + e
-      *reinterpret_cast<bf16x4*>(slot + r * (2 * D) + ((c ^ (r & (CH - 1))) << 4) + 8 * hf) = w;
-    }
-  }
-  // LDS operations of a wave execute in order; the fences only keep the compiler
-  // from moving the reads above the other lanes' writes.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const uint32_t pitch = (uint32_t)(ld * 2);
   const rsrc_t out = make_rsrc(dst, (uint32_t)max(nrows, 0) * pitch);
   // lane-derived offsets are recomputed here rather than hoisted across tiles
@@ -321,15 +309,37 @@ __device__ __forceinline__ void store_acc_rows(const f32x16 (&acc)[D / 32], floa
   const uint32_t voff = r0 * pitch + 16u * c;
   const uint32_t loff = r0 * (2 * D) + ((c ^ r0) << 4);
 #pragma unroll
-  for (int i = 0; i < 32 / RPI; ++i) {
-    // row RPI i + r0 with r0 < RPI: its swizzle mask is r0 ^ (RPI i mod CH)
-    const uint32_t la = (loff ^ (uint32_t)(((RPI * i) & (CH - 1)) << 4)) + (uint32_t)(RPI * i * 2 * D);
-    const bf16x8 v = *reinterpret_cast<const bf16x8*>(slot + la);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), out,
-                                           voff + (uint32_t)(RPI * i) * pitch, 0, 0);
+  for (int p = 0; p < PASSES; ++p) {
+    if (PASSES == 1 || r / RPP == p) {
+      const int sr = r % RPP;   // slot row
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[dt][4 * q4 + e] * scale);
+          const int ci = 4 * dt + q4;   // chunk of d = 32 dt + 8 q4 + 4 hf + e
+          *reinterpret_cast<bf16x4*>(slot + sr * (2 * D) + ((ci ^ (sr & (CH - 1))) << 4) + 8 * hf) = w;
+        }
+      }
+    }
+    // LDS operations of a wave execute in order; the fences only keep the compiler
+    // from moving the reads above the other lanes' writes (or a pass's writes above
+    // the previous pass's reads).
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < RPP / RPI; ++i) {
+      // slot row RPI i + r0 with r0 < RPI: its swizzle mask is r0 ^ (RPI i mod CH)
+      const uint32_t la = (loff ^ (uint32_t)(((RPI * i) & (CH - 1)) << 4)) + (uint32_t)(RPI * i * 2 * D);
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(slot + la);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), out,
+                                             voff + (uint32_t)(RPP * p + RPI * i) * pitch, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 }  // namespace jfa
