@@ -105,9 +105,16 @@ SMALL_CASES = {
     "self_d64": ([2, 33, 190, 257], 3, 64, False, False, 0),
     "self_empty_seq_causal": ([20, 0, 45], 2, 128, False, True, 0),
     "block64": ([64] * 40, 4, 128, False, False, 0),
-    # every sequence within one backward tile: dQ is written by the tiles directly
+    # short sequences (64-key backward tiles), not all within one tile
     "self_d64_short_causal": ([3, 64, 100, 128, 1], 2, 64, False, True, 0),
     "self_d128_short": ([128, 1, 77, 100], 3, 128, False, False, 0),
+    # every sequence within one backward tile: delta is formed inline and dQ is
+    # written by the tiles directly (64-key tiles of two waves, 128-key tiles of four;
+    # D = 64 with four waves splits the dQ product into two key parts)
+    "single_tile_d128_nw2_causal": ([64, 1, 37, 64, 50, 64, 13], 3, 128, False, True, 0),
+    "single_tile_d128_nw4": ([128, 100, 110, 128, 90, 97], 2, 128, False, False, 0),
+    "single_tile_d64_nw4_causal": ([128, 120, 99, 128, 70], 2, 64, False, True, 0),
+    "single_tile_d64_nw2": ([64, 3, 64, 50, 17], 2, 64, False, False, 0),
 }
 
 
@@ -117,6 +124,26 @@ def test_small_cases_match_oracle(name):
     case = workloads.make_case(lengths, heads=h, head_dim=d, broadcast_q=bq, causal=causal,
                                q_len=lq, seed=zlib.crc32(name.encode()) % 1000)
     out = _run(case)
+    _compare_full(case, out)
+
+
+def test_single_tile_backward_does_not_read_o():
+    """With every self-mode sequence inside one backward tile, delta comes from the
+    tile's own P and dP, so O is not read: an O of NaNs gives the same gradients."""
+    jfa = _jfa()
+    case = workloads.make_case([64, 17, 64, 40], heads=2, head_dim=128, broadcast_q=False,
+                               causal=False, q_len=0, seed=11)
+    q, k, v, g = (case[x].cuda() for x in ("q", "k", "v", "g"))
+    off = case["offsets"].cuda()
+    kw = dict(broadcast_q=False, causal=False, scale=case["scale"])
+    o, lse = jfa.fwd(q, k, v, off, **kw)
+    ref = jfa.bwd(q, k, v, off, o, lse, g, **kw)
+    nan_o = torch.full_like(o, float("nan"))
+    got = jfa.bwd(q, k, v, off, nan_o, lse, g, **kw)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), ref, got):
+        assert torch.equal(a.cpu(), b.cpu()), name
+    out = {"o": o.cpu(), "lse": lse.cpu(), "dq": got[0].cpu(), "dk": got[1].cpu(), "dv": got[2].cpu()}
     _compare_full(case, out)
 
 

@@ -294,7 +294,7 @@ jfa_status_t jfa_bwd(const void* q, const void* k, const void* v, const void* of
   if (e != hipSuccess) return hip_fail(e, "jfa_bwd: delta launch");
   if (p.total_kv > 0) {
     e = timed_launch("bwd", s, [&] {
-      return jfa::launch_bwd(p, plan, sched, rowstat, d_o, dq_acc, dq, dk, dv, s);
+      return jfa::launch_bwd(p, plan, sched, rowstat, lse, d_o, dq_acc, dq, dk, dv, s);
     });
     if (e != hipSuccess) return hip_fail(e, "jfa_bwd: kernel launch");
   }

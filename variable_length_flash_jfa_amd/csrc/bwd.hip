@@ -40,33 +40,53 @@ namespace {
 // rowstat[(h rows + row) 2 + 0] = LSE[h][row] log2(e) (so that P = exp2(S c log2 e -
 // that) needs no multiply per score), rowstat[... + 1] = delta[h][row]; one 8-byte
 // pair per row lets a single direct load bring both values of 32 rows into LDS.
-template <int D>
+// CHECK: the call may have every sequence within one tile (known on the device only,
+// meta[3]); the kernel then returns at once, and takes four pairs per group of
+// threads so that there are fewer blocks to retire.  Otherwise there is no check (its
+// load would stand in front of every block's work) and one pair per group.
+template <int D, bool CHECK>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o,
                                                        const bf16* __restrict__ d_o,
                                                        const float* __restrict__ lse,
                                                        float2* __restrict__ rowstat, int64_t rows,
                                                        int heads, float* __restrict__ dq_acc,
                                                        int64_t acc_vec4, const int* __restrict__ meta) {
+  // every sequence within one tile: the tiles read LSE themselves, form delta
+  // inline and write dQ directly, so there is nothing to do
+  if (CHECK && meta[3] != 0) return;
   constexpr int TPR = D / 8;                 // threads per (row, head)
-  const int64_t pair = ((int64_t)blockIdx.x * 256 + threadIdx.x) / TPR;   // row * heads + h
+  constexpr int PPG = CHECK ? 4 : 1;         // pairs per group of TPR threads
   const int part = threadIdx.x % TPR;
   const int64_t npairs = rows * heads;
-  float s = 0.f;
-  if (pair < npairs) {
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(o + pair * D + part * 8);
-    const bf16x8 y = *reinterpret_cast<const bf16x8*>(d_o + pair * D + part * 8);
+  const int64_t groups = (int64_t)gridDim.x * (256 / TPR);
+  const int64_t g0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) / TPR;
+  // group g takes pairs g, g + groups, ... (consecutive groups, consecutive pairs);
+  // all loads are issued before the sums.  A pair's TPR lanes share every branch.
+  bf16x8 x[PPG], y[PPG];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s += (float)x[e] * (float)y[e];
+  for (int u = 0; u < PPG; ++u) {
+    const int64_t pair = g0 + u * groups;
+    if (pair < npairs) {
+      x[u] = *reinterpret_cast<const bf16x8*>(o + pair * D + part * 8);
+      y[u] = *reinterpret_cast<const bf16x8*>(d_o + pair * D + part * 8);
+    }
   }
 #pragma unroll
-  for (int m = TPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
-  if (pair < npairs && part == 0) {
-    const int64_t row = pair / heads;
-    const int64_t i = (pair - row * heads) * rows + row;   // [head][row]
-    rowstat[i] = make_float2(lse[i] * kLog2e, s);
+  for (int u = 0; u < PPG; ++u) {
+    const int64_t pair = g0 + u * groups;
+    if (pair >= npairs) break;
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += (float)x[u][e] * (float)y[u][e];
+#pragma unroll
+    for (int m = TPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+    if (part == 0) {
+      const int64_t row = pair / heads;
+      const int64_t i = (pair - row * heads) * rows + row;   // [head][row]
+      rowstat[i] = make_float2(lse[i] * kLog2e, s);
+    }
   }
-  // grid-stride zero fill of the dQ accumulator (unless the tiles write dQ directly)
-  if (meta[3] != 0) return;
+  // grid-stride zero fill of the dQ accumulator
   const int64_t nthreads = (int64_t)gridDim.x * 256;
   float4* acc = reinterpret_cast<float4*>(dq_acc);
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < acc_vec4; i += nthreads)
@@ -82,6 +102,7 @@ struct BwdArgs {
   const bf16* v;
   const bf16* d_o;
   const float2* rowstat;
+  const float* lse;   // [heads][rows], read directly when every tile holds a whole sequence
   const void* offsets;
   int off64;
   int heads;
@@ -104,7 +125,9 @@ struct BwdArgs {
 // added to that VGPR once, which commutes with the per-read XOR of the swizzle
 // (the XOR only touches the low 8 (7) bits).  Each read then costs at most one
 // XOR and its constant part rides in the instruction's offset field.
-template <int D, int NW, bool BCAST, bool CAUSAL>
+// DIRECT: self mode with every sequence in one tile (the plan flags such a call in
+// meta[3]); delta is formed inline and dQ is stored, not reduce-added.
+template <int D, int NW, bool BCAST, bool CAUSAL, bool DIRECT>
 struct BwdKernel {
   static constexpr int BN = 32 * NW;         // keys per tile (NW waves x 32)
   static constexpr int BQ = kBwdBQ;          // query rows per block
@@ -126,11 +149,12 @@ struct BwdKernel {
   static constexpr int OFF_DS = OFF_DO + 2 * QT_BYTES;
   static constexpr int OFF_DQP = OFF_DS + DS_BYTES;           // dQ partials of the key parts
   static constexpr int OFF_ROW = OFF_DQP + DQP_BYTES;         // 2 buffers
-  static constexpr int SMEM = OFF_ROW + 2 * ROW_BYTES;
+  static constexpr int OFF_DEL = OFF_ROW + 2 * ROW_BYTES;     // per-wave partial deltas (self mode)
+  static constexpr int DEL_BYTES = DIRECT ? NW * BQ * 4 : 0;
+  static constexpr int SMEM = OFF_DEL + DEL_BYTES;
   static constexpr uint32_t GQ = OFF_DO - OFF_Q;              // dO tile minus Q tile, same buffer
   static constexpr int XB = D == 128 ? 256 : 128;             // the XOR-free granule
   static_assert(BN == 32 * NW && KP * DT == NW * DTW && DTW <= 2 && KPART % 16 == 0, "tile shape");
-  static_assert(OFF_Q + NW * 32 * 2 * D <= SMEM, "epilogue slots must fit behind the K tile region");
   static_assert(OFF_Q % XB == 0 && QT_BYTES % XB == 0 && GQ % XB == 0 && (KPART * 2 * D) % XB == 0 &&
                     (32 * 2 * D) % XB == 0 && OFF_DS % 64 == 0 && (KPART * BQ * 2) % 64 == 0,
                 "tile offsets must commute with the swizzle XOR");
@@ -140,7 +164,6 @@ struct BwdKernel {
   int lane, wave, c32, hf;
   int64_t rs;
   int dq_dt, dq_part;    // this wave's (first) d tile and key part in the dQ product
-  bool direct;           // self mode, every sequence in one tile: dQ stored, not reduce-added
 
   // per tile
   int64_t kv0;           // first K/V row of the sequence
@@ -155,10 +178,6 @@ struct BwdKernel {
   uint32_t row_base;     // Q / dO row reads (add the tile offset)
   uint32_t k_row_base;   // this wave's K rows
   uint32_t tr4_base;     // Q^T / dO^T transposing reads (add the tile offset)
-  uint32_t kq_base;      // K transposing reads of this wave's dQ slice and key part
-  uint32_t dsq_base;     // dS^T transposing reads of this wave's key part
-  uint32_t dsw_base;     // dS^T writes of this lane's key row
-  uint32_t dq_lane_off;  // byte offset of this lane's dQ element within a query block
 
   __device__ BwdKernel(const BwdArgs& args, char* sm) : a(args), smem(sm) {
     lane = threadIdx.x & 63;
@@ -168,22 +187,41 @@ struct BwdKernel {
     rs = (int64_t)a.heads * D;
     dq_dt = (wave % (DT / DTW)) * DTW;   // even when a wave takes two d tiles
     dq_part = wave / (DT / DTW);
-    direct = !BCAST && __builtin_amdgcn_readfirstlane(a.meta[3]) != 0;
     row_base = row_read_base<D>(lane);
     k_row_base = row_base + (uint32_t)(OFF_K + 32 * wave * 2 * D);
     tr4_base = tr_read_base<D>(lane, 4 * hf);
-    kq_base = (tr_read_base<D>(lane, 8 * hf) ^ (uint32_t)((4 * dq_dt) << 4)) +
-              (uint32_t)(OFF_K + dq_part * KPART * 2 * D);
-    // dS^T tile [BN keys][BQ queries] bf16, 64-byte rows of eight 8-byte units; unit u
-    // of row j is stored at u ^ ((j >> 2) & 7), which keeps both the 32-row writes
-    // and the 4-row transposing reads free of bank conflicts.
-    const int t = lane & 15;
-    const int unit = 4 * ((lane >> 4) & 1) + (t & 3);
-    dsq_base = (uint32_t)(OFF_DS + dq_part * KPART * (BQ * 2) + (8 * hf + (t >> 2)) * (BQ * 2) +
-                          ((unit ^ (2 * hf)) << 3));
-    const int j = 32 * wave + c32;
-    dsw_base = (uint32_t)(OFF_DS + j * (BQ * 2) + ((hf ^ ((j >> 2) & 7)) << 3));
-    dq_lane_off = (uint32_t)(((4 * hf) * a.heads * D + 32 * dq_dt + c32) * 4);
+  }
+
+  // Lane parts of the dQ-product, dS^T and reduce-add addresses.  They are formed
+  // where they are used, from a laundered lane index, instead of being held in
+  // VGPRs for the whole kernel.
+  // K transposing reads of this wave's dQ slice and key part:
+  __device__ __forceinline__ uint32_t kq_base() const {
+    const int l = (int)launder((uint32_t)lane);
+    return (tr_read_base<D>(l, 8 * (l >> 5)) ^ (uint32_t)((4 * dq_dt) << 4)) +
+           (uint32_t)(OFF_K + dq_part * KPART * 2 * D);
+  }
+  // dS^T tile [BN keys][BQ queries] bf16, 64-byte rows of eight 8-byte units; unit u
+  // of row j is stored at u ^ ((j >> 2) & 7), which keeps both the 32-row writes
+  // and the 4-row transposing reads free of bank conflicts.
+  // dS^T transposing reads of this wave's key part:
+  __device__ __forceinline__ uint32_t dsq_base() const {
+    const int l = (int)launder((uint32_t)lane);
+    const int t = l & 15, h2 = l >> 5;
+    const int unit = 4 * ((l >> 4) & 1) + (t & 3);
+    return (uint32_t)(OFF_DS + dq_part * KPART * (BQ * 2) + (8 * h2 + (t >> 2)) * (BQ * 2) +
+                      ((unit ^ (2 * h2)) << 3));
+  }
+  // dS^T writes of this lane's key row:
+  __device__ __forceinline__ uint32_t dsw_base() const {
+    const int l = (int)launder((uint32_t)lane);
+    const int j = 32 * wave + (l & 31);
+    return (uint32_t)(OFF_DS + j * (BQ * 2) + (((l >> 5) ^ ((j >> 2) & 7)) << 3));
+  }
+  // byte offset of this lane's fp32 dQ element within a query block:
+  __device__ __forceinline__ uint32_t dq_lane_off() const {
+    const int l = (int)launder((uint32_t)lane);
+    return (uint32_t)(((4 * (l >> 5)) * a.heads * D + 32 * dq_dt + (l & 31)) * 4);
   }
 
   __device__ __forceinline__ char* rowbuf(int b) { return smem + OFF_ROW + b * ROW_BYTES; }
@@ -195,19 +233,25 @@ struct BwdKernel {
   // Issues the direct LDS loads of query block [qi0, qi0 + BQ): Q and dO rows, and
   // the (LSE, delta) pairs of those rows.  Rows past the end read as zeros; the
   // masked path gives them zero weight.
-  __device__ __forceinline__ void load_qblock(int qi0, int buf) {
-    const int rows = min(q_rows - qi0, BQ);
+  __device__ __forceinline__ void load_qblock(int qi0, int buf) { load_qblock(qi0, buf, kv0, grow0, h, q_rows); }
+  __device__ __forceinline__ void load_qblock(int qi0, int buf, int64_t kv0_, int64_t grow0_, int h_, int q_rows_) {
+    const int rows = min(q_rows_ - qi0, BQ);
     const uint32_t row_bytes = (uint32_t)(rs * 2);
     const uint32_t bytes = (uint32_t)rows * row_bytes;
-    const bf16* qsrc = a.q + ((BCAST ? 0 : kv0) + qi0) * rs + (int64_t)h * D;
-    const bf16* gsrc = a.d_o + (grow0 + qi0) * rs + (int64_t)h * D;
+    const bf16* qsrc = a.q + ((BCAST ? 0 : kv0_) + qi0) * rs + (int64_t)h_ * D;
+    const bf16* gsrc = a.d_o + (grow0_ + qi0) * rs + (int64_t)h_ * D;
     lds_load_tile<D, NW>(smem + OFF_Q + buf * QT_BYTES, BQ, wave, lane, make_rsrc_sgpr(qsrc, bytes),
                          row_bytes);
     lds_load_tile<D, NW>(smem + OFF_DO + buf * QT_BYTES, BQ, wave, lane, make_rsrc_sgpr(gsrc, bytes),
                          row_bytes);
     if (wave == NW - 1) {
-      const float2* src = a.rowstat + (int64_t)h * a.rows + grow0 + qi0;
-      lds_load4(make_rsrc_sgpr(src, (uint32_t)rows * 8u), (uint32_t)lane * 4u, rowbuf(buf));
+      if constexpr (DIRECT) {   // the forward's LSE, one float per row
+        const float* src = a.lse + (int64_t)h_ * a.rows + grow0_ + qi0;
+        lds_load4(make_rsrc_sgpr(src, (uint32_t)rows * 4u), (uint32_t)lane * 4u, rowbuf(buf));
+      } else {                  // (LSE log2 e, delta) pairs
+        const float2* src = a.rowstat + (int64_t)h_ * a.rows + grow0_ + qi0;
+        lds_load4(make_rsrc_sgpr(src, (uint32_t)rows * 8u), (uint32_t)lane * 4u, rowbuf(buf));
+      }
     }
   }
 
@@ -215,10 +259,17 @@ struct BwdKernel {
   // With MID_BAR the barrier that retires the previous block's dS^T readers comes
   // last, right before the dS^T write (every wave reaches it, active or not);
   // otherwise the caller has passed it.
+  //
+  // DIRECT (every key of the sequence is in this tile): P comes from the forward's
+  // LSE and delta_i = sum_j P_ij dP_ij is formed here, without a pass over O
+  // ("Meta's TLX Block Attention Beats Flash Attention v2 by 2.3x on Blackwell
+  // GPUs", section "One Constraint, Five Eliminations").  Each wave sums its 32 keys
+  // (half_lane_sums16), the partial sums meet in LDS at a barrier (the MID_BAR one
+  // when there is one), and every wave adds the NW partials of its rows.
   template <bool MASKED, bool MID_BAR>
   __device__ __forceinline__ void qblock(int buf, int qi0) {
     if (!active) {
-      if constexpr (MID_BAR) __syncthreads();
+      if constexpr (MID_BAR || DIRECT) __syncthreads();
       return;
     }
     const uint32_t boff = (uint32_t)(buf * QT_BYTES);
@@ -250,6 +301,51 @@ struct BwdKernel {
         ga = ga_n;
         __builtin_amdgcn_sched_barrier(0);
       }
+      // rows past the query end, keys past the sequence end, and (causal) keys after
+      // the query get zero probability
+      auto visible = [&](int q4, int e) {
+        const int ipos = qi0 + 8 * q4 + 4 * hf + e;
+        const int jpos = j0 + 32 * wave + c32;
+        bool vis = jpos < n && ipos < q_rows;
+        if constexpr (CAUSAL) vis = vis && jpos <= ipos;
+        return vis;
+      };
+      if constexpr (DIRECT) {
+        const float* lsep = reinterpret_cast<const float*>(rowbuf(buf)) + 4 * hf;
+        float pv[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lsep + 8 * q4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * q4 + e;
+            float p = fast_exp2(fmaf(s[r], a.scale_log2, -(l4[e] * kLog2e)));
+            if constexpr (MASKED) {
+              if (!visible(q4, e)) p = 0.f;
+            }
+            pv[r] = p;
+          }
+        }
+        const float part = half_lane_dots16(pv, dp, lane);
+        float* del = reinterpret_cast<float*>(smem + OFF_DEL);
+        if ((lane & 1) == 0) {
+          const int r = (lane >> 1) & 15;
+          del[wave * BQ + 8 * (r >> 2) + 4 * hf + (r & 3)] = part;
+        }
+        __syncthreads();   // partial deltas visible; the previous block's dS^T readers are done
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4 d4 = *reinterpret_cast<const f32x4*>(del + 8 * q4 + 4 * hf);
+#pragma unroll
+          for (int w = 1; w < NW; ++w) d4 += *reinterpret_cast<const f32x4*>(del + w * BQ + 8 * q4 + 4 * hf);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * q4 + e;
+            pb[r >> 3][r & 7] = (bf16)pv[r];
+            sb[r >> 3][r & 7] = (bf16)(pv[r] * (dp[r] - d4[e]));
+          }
+        }
+      }
       // P = exp2(S c log2 e - LSE log2 e); dS = P (dP - delta) for query rows
       // 8 q4 + 4 hf + e (register r = 4 q4 + e); (rs01, rs23) hold the (LSE log2 e,
       // delta) pairs of rows e = 0, 1 and e = 2, 3
@@ -259,34 +355,31 @@ struct BwdKernel {
         const float dl = e < 2 ? rs01[2 * e + 1] : rs23[2 * (e - 2) + 1];
         float p = fast_exp2(fmaf(s[r], a.scale_log2, -l2));
         if constexpr (MASKED) {
-          // rows past the query end, keys past the sequence end, and (causal) keys
-          // after the query get zero probability
-          const int ipos = qi0 + 8 * q4 + 4 * hf + e;
-          const int jpos = j0 + 32 * wave + c32;
-          bool vis = jpos < n && ipos < q_rows;
-          if constexpr (CAUSAL) vis = vis && jpos <= ipos;
-          if (!vis) p = 0.f;
+          if (!visible(q4, e)) p = 0.f;
         }
         const float ds = p * (dp[r] - dl);
         pb[r >> 3][r & 7] = (bf16)p;
         sb[r >> 3][r & 7] = (bf16)ds;
       };
       const char* rowp = rowbuf(buf) + 32 * hf;
-      // rows of query block half 0 (registers 0..7) now; those of half 1 are formed
-      // between the dV / dK products of half 0, which do not depend on them
+      f32x4 h01 = {}, h23 = {};
+      if constexpr (!DIRECT) {
+        // rows of query block half 0 (registers 0..7) now; those of half 1 are formed
+        // between the dV / dK products of half 0, which do not depend on them
 #pragma unroll
-      for (int q4 = 0; q4 < 2; ++q4) {
-        const f32x4 rs01 = *reinterpret_cast<const f32x4*>(rowp + 64 * q4);
-        const f32x4 rs23 = *reinterpret_cast<const f32x4*>(rowp + 64 * q4 + 16);
+        for (int q4 = 0; q4 < 2; ++q4) {
+          const f32x4 rs01 = *reinterpret_cast<const f32x4*>(rowp + 64 * q4);
+          const f32x4 rs23 = *reinterpret_cast<const f32x4*>(rowp + 64 * q4 + 16);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) softmax(q4, e, rs01, rs23);
+          for (int e = 0; e < 4; ++e) softmax(q4, e, rs01, rs23);
+        }
+        // (LSE, delta) of q4 = 2 now, of q4 = 3 once q4 = 2 is done
+        h01 = *reinterpret_cast<const f32x4*>(rowp + 128);
+        h23 = *reinterpret_cast<const f32x4*>(rowp + 128 + 16);
       }
-      // (LSE, delta) of q4 = 2 now, of q4 = 3 once q4 = 2 is done
-      f32x4 h01 = *reinterpret_cast<const f32x4*>(rowp + 128);
-      f32x4 h23 = *reinterpret_cast<const f32x4*>(rowp + 128 + 16);
       // publish dS^T [key][query] (bf16)
       auto publish_ds = [&]() {
-        const uint32_t wb = launder(dsw_base);
+        const uint32_t wb = dsw_base();
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           bf16x4 w;
@@ -311,7 +404,7 @@ struct BwdKernel {
           q_n = lds_operand_tr<D>(smem, tb, 16 * kc1, 16 * kc1 + 8, dt1);
         }
         dvt[dt] = mfma32(g_op, pb[kc], dvt[dt]);
-        if (kc == 0) {
+        if (!DIRECT && kc == 0) {
 #pragma unroll
           for (int k = 0; k < EPS / 2; ++k) {
             const int el = EPS * step + k;   // 0..7 -> (q4 2 + el / 4, e el % 4)
@@ -319,7 +412,7 @@ struct BwdKernel {
           }
         }
         dkt[dt] = mfma32(q_op, sb[kc], dkt[dt]);
-        if (kc == 0) {
+        if (!DIRECT && kc == 0) {
 #pragma unroll
           for (int k = EPS / 2; k < EPS; ++k) {
             const int el = EPS * step + k;
@@ -332,12 +425,12 @@ struct BwdKernel {
         }
         g_op = g_n;
         q_op = q_n;
-        if constexpr (!MID_BAR) {
+        if constexpr (!MID_BAR || DIRECT) {   // (DIRECT: the barrier came with the deltas)
           if (step == DT - 1) publish_ds();
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (MID_BAR) {
+      if constexpr (MID_BAR && !DIRECT) {
         __syncthreads();   // the previous block's dS^T readers are done
         publish_ds();
       }
@@ -349,8 +442,8 @@ struct BwdKernel {
   // end hold zeros (zero probability, or zeroed at the start of the tile for waves
   // with no key inside), so the loop needs no bounds.
   __device__ __forceinline__ void dq_compute(f32x16 (&out)[DTW]) {
-    const uint32_t dsb = launder(dsq_base);
-    const uint32_t kb8 = launder(kq_base);
+    const uint32_t dsb = dsq_base();
+    const uint32_t kb8 = kq_base();
     auto ds_op = [&](int jj) {   // dS[query l % 32][keys jj + 8 (l / 32) + e] of the part
       const uint32_t x = (uint32_t)(((jj >> 2) & 4) << 3);
       return cat(lds_read_tr(smem + ((dsb ^ x) + jj * (BQ * 2))),
@@ -430,12 +523,12 @@ struct BwdKernel {
   template <int NG>
   __device__ __forceinline__ void dq_atomics(const f32x4 (&vals)[NG], int g0, int qi0, int dtk = 0) {
     const int rows = min(q_rows - qi0, BQ);
-    if (direct) {
+    if constexpr (DIRECT) {
       // the tile holds every key of these queries: dQ = c dS K is final, one bf16 per
       // (row, column) with the same row grouping and bounds
       const uint32_t row_bytes = (uint32_t)(a.heads * D * 2);
       bf16* base = a.dq + ((kv0 + qi0) * a.heads + h) * D;
-      const uint32_t o0 = (launder(dq_lane_off) >> 1) + 64u * dtk;   // fp32 lane offset -> bf16
+      const uint32_t o0 = (dq_lane_off() >> 1) + 64u * dtk;   // fp32 lane offset -> bf16
       const uint32_t o[4] = {o0, o0 + row_bytes, o0 + 2 * row_bytes, o0 + 3 * row_bytes};
 #pragma unroll
       for (int k = 0; k < NG; ++k) {
@@ -453,7 +546,7 @@ struct BwdKernel {
     const int64_t qrow0 = BCAST ? (int64_t)(blockIdx.x & (kDqStripes - 1)) * a.q_len + qi0 : kv0 + qi0;
     const uint32_t row_bytes = (uint32_t)(a.heads * D * 4);
     float* base = a.dq_acc + (qrow0 * a.heads + h) * D;
-    const uint32_t o0 = launder(dq_lane_off) + 128u * dtk;
+    const uint32_t o0 = dq_lane_off() + 128u * dtk;
     const uint32_t o[4] = {o0, o0 + row_bytes, o0 + 2 * row_bytes, o0 + 3 * row_bytes};
 #pragma unroll
     for (int k = 0; k < NG; ++k) {
@@ -579,13 +672,43 @@ struct BwdKernel {
     issue_k(g);
     issue_v(g);
   }
+  // First query block that sees a tile's keys, and its buffer.
+  __device__ __forceinline__ static int first_qblock(const Geo& g) {
+    if constexpr (CAUSAL) return (g.j0 / BQ) * BQ;
+    return 0;
+  }
+  __device__ __forceinline__ static int first_qbuf(const Geo& g) { return (first_qblock(g) / BQ) & 1; }
+  // Issues the loads of a tile's first query block.
+  __device__ __forceinline__ void issue_q0(const Geo& g) {
+    const int qr = BCAST ? a.q_len : g.n;
+    const int qs = first_qblock(g);
+    if (qs < qr) load_qblock(qs, first_qbuf(g), g.kv0, BCAST ? (int64_t)g.b * a.q_len : g.kv0, g.h, qr);
+  }
 
-  // One tile whose K/V loads have been issued.  `pre` runs after the first barrier.
-  // After the query loop `next(ng)` names the following tile (or returns false); its
-  // V fragment (vf is no longer read) is loaded during the last dQ product and its K
-  // tile once every wave is past that product, before this tile's dK / dV leave.
+  // Epilogue slots: wave 0 stages through the query buffer that the next tile's
+  // first block leaves free, wave 1 through the matching dO buffer, the others
+  // through the dS^T / dQ-partial region; EPI_PASSES splits a slot's 32 rows so that
+  // they fit.
+  static constexpr int EPI_PASSES =
+      (NW - 2) * 32 * 2 * D <= DS_BYTES + DQP_BYTES ? 1 : ((NW - 2) * 16 * 2 * D <= DS_BYTES + DQP_BYTES ? 2 : 4);
+  static constexpr int SLOT_BYTES = 32 * 2 * D / EPI_PASSES;
+  static_assert((NW - 2) * SLOT_BYTES <= DS_BYTES + DQP_BYTES && SLOT_BYTES <= QT_BYTES,
+                "epilogue slots must fit in the free query buffers and the dS^T / dQ regions");
+  static constexpr int EPI_STORES = 2 * (D / 16);   // store instructions of one epilogue
+  __device__ __forceinline__ char* epilogue_slot(int free_buf) const {
+    if (wave == 0) return smem + OFF_Q + free_buf * QT_BYTES;
+    if (wave == 1) return smem + OFF_DO + free_buf * QT_BYTES;
+    return smem + OFF_DS + (wave - 2) * SLOT_BYTES;
+  }
+
+  // One tile whose K/V and first query block loads have been issued (`first`: by
+  // the kernel prologue, so nothing else is in flight).  `pre` runs after the first
+  // barrier.  After the query loop `next(ng)` names the following tile (or returns
+  // false); its V fragment (vf is no longer read) is loaded during the last dQ
+  // product, and its K tile and first query block once every wave is past that
+  // product, before this tile's dK / dV leave.
   template <class Pre, class Next>
-  __device__ __forceinline__ bool process(const Geo& g, Pre&& pre, Next&& next, Geo& ng) {
+  __device__ __forceinline__ bool process(const Geo& g, bool first, Pre&& pre, Next&& next, Geo& ng) {
     h = g.h;
     kv0 = g.kv0;
     n = g.n;
@@ -601,22 +724,28 @@ struct BwdKernel {
     // a wave with no key inside the sequence never writes its dS^T rows in this
     // tile: zero them once for the dQ products
     if (!active) {
-      const uint32_t wb = dsw_base;
+      const uint32_t wb = dsw_base();
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
         *reinterpret_cast<bf16x4*>(smem + (wb ^ (uint32_t)(q4 << 4))) = bf16x4{};
+      // nor its partial deltas
+      if (DIRECT && lane < BQ) reinterpret_cast<float*>(smem + OFF_DEL)[wave * BQ + lane] = 0.f;
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       dvt[dt] = zero16();
       dkt[dt] = zero16();
     }
-    // query rows that can see this tile's keys
-    int qs = 0;
-    if constexpr (CAUSAL) qs = (j0 / BQ) * BQ;
+    // query rows that can see this tile's keys; their first block was issued with
+    // the tile's K/V, before the previous tile's epilogue, whose row stores may stay
+    // in flight
+    const int qs = first_qblock(g);
     const int q_last = q_rows;
-    if (qs < q_last) load_qblock(qs, (qs / BQ) & 1);
-    wait_lds_loads();
+    if (first) {
+      wait_lds_loads();
+    } else {
+      wait_vmcnt<EPI_STORES>();
+    }
     __syncthreads();
     // Peeled loops: query blocks that need a mask (causal diagonal, a partial K/V
     // block at the sequence end, or a partial last query block) run apart from the
@@ -641,26 +770,30 @@ struct BwdKernel {
         dq_flush(pending);
       }
     }
-    __syncthreads();   // every wave is past its last read of the K tile and dQ partials
-    if (more) issue_k(ng);
+    __syncthreads();   // every wave is past its last read of the K tile, dQ partials and query blocks
+    if (more) {
+      issue_k(ng);
+      issue_q0(ng);
+    }
 
-    // dK = c dS^T Q and dV -> bf16 rows, staged through this wave's slot of the
-    // (idle) query-block region
+    // dK = c dS^T Q and dV -> bf16 rows, staged through this wave's epilogue slot
     {
       const int nrows = min(max(n - (j0 + 32 * wave), 0), 32);
-      char* slot = smem + OFF_Q + wave * (32 * 2 * D);
+      char* slot = epilogue_slot(more ? first_qbuf(ng) ^ 1 : 0);
       const int64_t off = (kv0 + j0 + 32 * wave) * rs + (int64_t)h * D;
-      store_acc_rows<D>(dkt, a.scale, slot, a.dk + off, rs, nrows, lane);
-      store_acc_rows<D>(dvt, 1.f, slot, a.dv + off, rs, nrows, lane);
+      store_acc_rows<D, EPI_PASSES>(dkt, a.scale, slot, a.dk + off, rs, nrows, lane);
+      store_acc_rows<D, EPI_PASSES>(dvt, 1.f, slot, a.dv + off, rs, nrows, lane);
     }
     return more;
   }
 };
 
-template <int D, int NW, bool BCAST, bool CAUSAL>
+template <int D, int NW, bool BCAST, bool CAUSAL, bool DIRECT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_kernel(BwdArgs a) {
-  using K = BwdKernel<D, NW, BCAST, CAUSAL>;
+  // self mode launches both variants; the plan's meta[3] picks the one that runs
+  if ((__builtin_amdgcn_readfirstlane(a.meta[3]) != 0) != DIRECT) return;
+  using K = BwdKernel<D, NW, BCAST, CAUSAL, DIRECT>;
   using Geo = typename K::Geo;
   __shared__ __attribute__((aligned(16))) char smem[K::SMEM];
   __shared__ __attribute__((aligned(16))) int next_item[64];   // DMA target, 16 bytes used
@@ -681,7 +814,8 @@ void bwd_kernel(BwdArgs a) {
   if (idx >= ntiles) return;
   Geo g = kern.geometry(a.items[idx / a.heads], idx % a.heads);
   kern.issue_kv(g);
-  for (;;) {
+  kern.issue_q0(g);
+  for (bool first = true;; first = false) {
     // static schedules know the next tile now: its item is copied into LDS while
     // this tile runs (the copy completes at this tile's first load wait)
     int nidx = dyn ? -1 : idx + num_wg;
@@ -698,7 +832,7 @@ void bwd_kernel(BwdArgs a) {
       return true;
     };
     Geo ng;
-    if (!kern.process(g, pre, next, ng)) break;
+    if (!kern.process(g, first, pre, next, ng)) break;
     g = ng;
     idx = nidx;
   }
@@ -707,11 +841,14 @@ void bwd_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // 5. dQ finalize
 // ---------------------------------------------------------------------------
+// CHECK: the call may have every sequence within one tile, whose tiles then wrote dQ
+// (meta[3]); without it the flag is not read.
+template <bool CHECK>
 __global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restrict__ acc,
                                                           bf16* __restrict__ dq, int64_t n_vec4,
                                                           int64_t stripe_vec4, int stripes,
                                                           float scale, const int* __restrict__ meta) {
-  if (meta[3] != 0) return;   // the tiles wrote dQ
+  if (CHECK && meta[3] != 0) return;   // the tiles wrote dQ
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n_vec4) return;
   const float4* a4 = reinterpret_cast<const float4*>(acc);
@@ -731,20 +868,36 @@ __global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restric
   reinterpret_cast<bf16x4*>(dq)[i] = o;
 }
 
-template <int D, int NW, bool BCAST, bool CAUSAL>
-hipError_t launch_bwd_inst(const BwdArgs& a, hipStream_t s, int64_t max_tiles) {
-  const void* fn = reinterpret_cast<const void*>(&bwd_kernel<D, NW, BCAST, CAUSAL>);
+template <int D, int NW, bool BCAST, bool CAUSAL, bool DIRECT>
+hipError_t launch_bwd_one(const BwdArgs& a, hipStream_t s, int64_t max_tiles) {
+  const void* fn = reinterpret_cast<const void*>(&bwd_kernel<D, NW, BCAST, CAUSAL, DIRECT>);
   const int grid = persistent_grid(fn, 64 * NW, max_tiles);
-  hipLaunchKernelGGL((bwd_kernel<D, NW, BCAST, CAUSAL>), dim3(grid), dim3(64 * NW), 0, s, a);
+  hipLaunchKernelGGL((bwd_kernel<D, NW, BCAST, CAUSAL, DIRECT>), dim3(grid), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
+}
+// Broadcast mode has one variant.  In self mode whether every sequence fits one
+// tile is known on the device only (meta[3], from the plan), so both variants are
+// launched and the one that does not match returns at once.
+template <int D, int NW, bool BCAST, bool CAUSAL>
+hipError_t launch_bwd_inst(const BwdArgs& a, hipStream_t s, int64_t max_tiles, bool maybe_single) {
+  if constexpr (BCAST) {
+    return launch_bwd_one<D, NW, true, false, false>(a, s, max_tiles);
+  } else {
+    if (maybe_single) {
+      const hipError_t e = launch_bwd_one<D, NW, false, CAUSAL, true>(a, s, max_tiles);
+      if (e != hipSuccess) return e;
+    }
+    return launch_bwd_one<D, NW, false, CAUSAL, false>(a, s, max_tiles);
+  }
 }
 
 template <int D, int NW>
 hipError_t launch_bwd_dw(const Problem& p, const BwdArgs& a, hipStream_t s) {
   const int64_t max_tiles = bwd_max_items(p) * p.heads;
-  if (p.broadcast) return launch_bwd_inst<D, NW, true, false>(a, s, max_tiles);
-  if (p.causal) return launch_bwd_inst<D, NW, false, true>(a, s, max_tiles);
-  return launch_bwd_inst<D, NW, false, false>(a, s, max_tiles);
+  const bool ms = maybe_single_tile(p);
+  if (p.broadcast) return launch_bwd_inst<D, NW, true, false>(a, s, max_tiles, ms);
+  if (p.causal) return launch_bwd_inst<D, NW, false, true>(a, s, max_tiles, ms);
+  return launch_bwd_inst<D, NW, false, false>(a, s, max_tiles, ms);
 }
 
 template <int D>
@@ -769,6 +922,12 @@ int bwd_waves(const Problem& p) {
   return mean_len >= 512 ? 8 : 4;
 }
 
+// Whether every sequence may lie within one backward tile (self mode, and the mean
+// length at most the tile's keys); the plan decides on the device (meta[3]).
+bool maybe_single_tile(const Problem& p) {
+  return !p.broadcast && p.total_kv <= (int64_t)p.batch * 32 * bwd_waves(p);
+}
+
 int64_t bwd_max_items(const Problem& p) {
   const int bn = 32 * bwd_waves(p);
   return (p.total_kv + bn - 1) / bn + p.batch;
@@ -779,29 +938,34 @@ hipError_t launch_bwd_pre(const Problem& p, const void* o, const void* d_o, cons
                           hipStream_t s) {
   const int64_t pairs = p.rows * p.heads;
   const int tpr = p.head_dim / 8;
-  int64_t blocks = (pairs * tpr + 255) / 256;
+  const bool check = maybe_single_tile(p);
+  const int ppg = check ? 4 : 1;
+  int64_t blocks = (pairs * tpr + ppg * 256 - 1) / (ppg * 256);
   if (blocks < 1) blocks = 1;
   const int64_t vec4 = dq_acc_elems / 4;
   float2* rs2 = reinterpret_cast<float2*>(rowstat);
-  if (p.head_dim == 128)
-    hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s,
-                       static_cast<const bf16*>(o), static_cast<const bf16*>(d_o), lse, rs2, p.rows,
-                       p.heads, dq_acc, vec4, meta);
-  else
-    hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s,
-                       static_cast<const bf16*>(o), static_cast<const bf16*>(d_o), lse, rs2, p.rows,
-                       p.heads, dq_acc, vec4, meta);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const bf16*>(o),
+                       static_cast<const bf16*>(d_o), lse, rs2, p.rows, p.heads, dq_acc, vec4, meta);
+  };
+  if (p.head_dim == 128) {
+    check ? go(bwd_pre_kernel<128, true>) : go(bwd_pre_kernel<128, false>);
+  } else {
+    check ? go(bwd_pre_kernel<64, true>) : go(bwd_pre_kernel<64, false>);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd(const Problem& p, const Plan& plan, int sched, const float* rowstat,
-                      const void* d_o, float* dq_acc, void* dq, void* dk, void* dv, hipStream_t s) {
+                      const float* lse, const void* d_o, float* dq_acc, void* dq, void* dk, void* dv,
+                      hipStream_t s) {
   BwdArgs a;
   a.q = static_cast<const bf16*>(p.q);
   a.k = static_cast<const bf16*>(p.k);
   a.v = static_cast<const bf16*>(p.v);
   a.d_o = static_cast<const bf16*>(d_o);
   a.rowstat = reinterpret_cast<const float2*>(rowstat);
+  a.lse = lse;
   a.offsets = p.offsets;
   a.off64 = p.off64;
   a.heads = p.heads;
@@ -826,8 +990,11 @@ hipError_t launch_dq_finalize(const Problem& p, const float* dq_acc, void* dq, c
   const int64_t vec4 = n / 4;
   const int64_t blocks = (vec4 + 255) / 256;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(dq_finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, s, dq_acc,
-                     static_cast<bf16*>(dq), vec4, vec4, p.broadcast ? kDqStripes : 1, p.scale, meta);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, s, dq_acc, static_cast<bf16*>(dq),
+                       vec4, vec4, p.broadcast ? kDqStripes : 1, p.scale, meta);
+  };
+  maybe_single_tile(p) ? go(dq_finalize_kernel<true>) : go(dq_finalize_kernel<false>);
   return hipGetLastError();
 }
 

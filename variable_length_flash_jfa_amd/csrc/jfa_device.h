@@ -64,6 +64,30 @@ __device__ __forceinline__ float sum_across_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Sixteen dot products at once over the 32 lanes of each wave half: x[r] y[r] of
+// every lane of a half is added up for each r.  Transpose-reduce: at each step a
+// lane keeps half of its values and adds its partner's copy of them (partners
+// differ in lane bit 4, then 3, 2, 1), so 16 shuffles do what 16 butterflies of 5
+// steps would; the products are formed in the first step.  Lane l returns the sum
+// for r = (l >> 1) & 15 (lanes l and l ^ 1 agree).
+__device__ __forceinline__ float half_lane_dots16(const float (&x)[16], const f32x16& y, int lane) {
+  float a[8], c[4], d[2];
+  const bool b4 = (lane >> 4) & 1, b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1, b1 = (lane >> 1) & 1;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {   // a[k]: r = k + 8 b4
+    const float lo = x[k] * y[k], hi = x[k + 8] * y[k + 8];
+    a[k] = (b4 ? hi : lo) + __shfl_xor(b4 ? lo : hi, 16);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k)   // c[k]: r = k + 4 b3 + 8 b4
+    c[k] = (b3 ? a[k + 4] : a[k]) + __shfl_xor(b3 ? a[k] : a[k + 4], 8);
+#pragma unroll
+  for (int k = 0; k < 2; ++k)   // d[k]: r = k + 2 b2 + 4 b3 + 8 b4
+    d[k] = (b2 ? c[k + 2] : c[k]) + __shfl_xor(b2 ? c[k] : c[k + 2], 4);
+  float e = (b1 ? d[1] : d[0]) + __shfl_xor(b1 ? d[0] : d[1], 2);
+  return e + __shfl_xor(e, 1);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---- swizzled LDS tiles -----------------------------------------------------

@@ -47,19 +47,24 @@ int fwd_waves(const Problem& p);                 // waves per forward workgroup
 int64_t fwd_max_items(const Problem& p);         // capacity of the forward item list
 int64_t bwd_max_items(const Problem& p);         // capacity of the backward item list
 int bwd_waves(const Problem& p);                 // waves per backward workgroup (2, 4 or 8)
+bool maybe_single_tile(const Problem& p);        // every sequence may fit one backward tile
 
 hipError_t launch_plan_fwd(const Problem& p, const Plan& plan, int sched, hipStream_t s);
 hipError_t launch_fwd(const Problem& p, const Plan& plan, int sched, void* o, float* lse,
                       hipStream_t s);
 
-// rowstat: [heads][rows] pairs (LSE log2 e, delta = rowsum(dO * O)), 2 floats each.
-// Runs after the backward plan: the dQ accumulator is zeroed unless meta[3] is set.
+// rowstat: [heads][rows] pairs (LSE log2 e, delta = rowsum(dO * O)), 2 floats each,
+// and the zeroed dQ accumulator.  Runs after the backward plan and does nothing when
+// meta[3] is set (the tiles then form delta themselves and write dQ directly).
 hipError_t launch_bwd_pre(const Problem& p, const void* o, const void* d_o, const float* lse,
                           float* rowstat, float* dq_acc, int64_t dq_acc_elems, const int* meta,
                           hipStream_t s);
 hipError_t launch_plan_bwd(const Problem& p, const Plan& plan, int sched, hipStream_t s);
+// lse: the forward's [heads][rows] LSE, read instead of rowstat when every tile
+// holds a whole self-mode sequence (meta[3]).
 hipError_t launch_bwd(const Problem& p, const Plan& plan, int sched, const float* rowstat,
-                      const void* d_o, float* dq_acc, void* dq, void* dk, void* dv, hipStream_t s);
+                      const float* lse, const void* d_o, float* dq_acc, void* dq, void* dk, void* dv,
+                      hipStream_t s);
 // Does nothing when meta[3] is set (the tiles wrote dQ).
 hipError_t launch_dq_finalize(const Problem& p, const float* dq_acc, void* dq, const int* meta,
                               hipStream_t s);
