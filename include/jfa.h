@@ -108,7 +108,11 @@ jfa_status_t jfa_fwd(const void* q, const void* k, const void* v,
 /* Backward pass: gradients of sum(O * dO) with respect to q, k and v, given the
  * o and lse that jfa_fwd returned for the same inputs.  In broadcast mode dq is
  * the sum over all sequences (JFA news page, "GEM's sequences do not fit a fixed
- * grid").  Same size rules as jfa_fwd. */
+ * grid").  In self mode, when every sequence fits one backward tile (block-diagonal
+ * attention in 64-token blocks, for instance), the row sums dO . O are formed from
+ * the tile's own probabilities and o is not read (Block Attention page, "One
+ * Constraint, Five Eliminations"); it must still be a valid pointer.  Same size
+ * rules as jfa_fwd. */
 jfa_status_t jfa_bwd(const void* q, const void* k, const void* v,
                      const void* offsets, int offsets_is_int64,
                      int64_t batch, int64_t num_heads, int64_t head_dim,
