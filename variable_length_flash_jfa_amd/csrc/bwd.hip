@@ -842,30 +842,33 @@ void bwd_kernel(BwdArgs a) {
 // 5. dQ finalize
 // ---------------------------------------------------------------------------
 // CHECK: the call may have every sequence within one tile, whose tiles then wrote dQ
-// (meta[3]); without it the flag is not read.
+// (meta[3]); the kernel then returns at once, from a bounded grid that strides over
+// the elements.  Without CHECK the flag is not read and every thread takes one
+// element group.
 template <bool CHECK>
 __global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restrict__ acc,
                                                           bf16* __restrict__ dq, int64_t n_vec4,
                                                           int64_t stripe_vec4, int stripes,
                                                           float scale, const int* __restrict__ meta) {
   if (CHECK && meta[3] != 0) return;   // the tiles wrote dQ
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n_vec4) return;
   const float4* a4 = reinterpret_cast<const float4*>(acc);
-  float4 s = a4[i];
-  for (int k = 1; k < stripes; ++k) {
-    const float4 t = a4[i + k * stripe_vec4];
-    s.x += t.x;
-    s.y += t.y;
-    s.z += t.z;
-    s.w += t.w;
+  const int64_t step = CHECK ? (int64_t)gridDim.x * 256 : n_vec4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_vec4; i += step) {
+    float4 s = a4[i];
+    for (int k = 1; k < stripes; ++k) {
+      const float4 t = a4[i + k * stripe_vec4];
+      s.x += t.x;
+      s.y += t.y;
+      s.z += t.z;
+      s.w += t.w;
+    }
+    bf16x4 o;
+    o[0] = (bf16)(s.x * scale);
+    o[1] = (bf16)(s.y * scale);
+    o[2] = (bf16)(s.z * scale);
+    o[3] = (bf16)(s.w * scale);
+    reinterpret_cast<bf16x4*>(dq)[i] = o;
   }
-  bf16x4 o;
-  o[0] = (bf16)(s.x * scale);
-  o[1] = (bf16)(s.y * scale);
-  o[2] = (bf16)(s.z * scale);
-  o[3] = (bf16)(s.w * scale);
-  reinterpret_cast<bf16x4*>(dq)[i] = o;
 }
 
 template <int D, int NW, bool BCAST, bool CAUSAL, bool DIRECT>
@@ -988,13 +991,15 @@ hipError_t launch_dq_finalize(const Problem& p, const float* dq_acc, void* dq, c
   const int64_t q_rows = p.broadcast ? p.q_len : p.total_kv;
   const int64_t n = q_rows * p.heads * p.head_dim;
   const int64_t vec4 = n / 4;
-  const int64_t blocks = (vec4 + 255) / 256;
+  int64_t blocks = (vec4 + 255) / 256;
   if (blocks == 0) return hipSuccess;
+  const bool check = maybe_single_tile(p);
+  if (check) blocks = std::min<int64_t>(blocks, (int64_t)device_cu_count() * 32);
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, s, dq_acc, static_cast<bf16*>(dq),
                        vec4, vec4, p.broadcast ? kDqStripes : 1, p.scale, meta);
   };
-  maybe_single_tile(p) ? go(dq_finalize_kernel<true>) : go(dq_finalize_kernel<false>);
+  check ? go(dq_finalize_kernel<true>) : go(dq_finalize_kernel<false>);
   return hipGetLastError();
 }
 
