@@ -11,3 +11,4 @@ from .attention import (  # noqa: F401
     backward,
     row_count,
 )
+from .rope import rope_rotate, rope_conjugate, backward_rope  # noqa: F401

@@ -352,3 +352,99 @@ def test_dq_rows_match_full_backward(causal):
     rows = [0, 3, 22, 11]
     np.testing.assert_allclose(oracle.sequence_dq_rows(qb, kb, vb, gb, rows, c, causal), dq[rows],
                                atol=1e-13)
+
+
+# ---- rotary-embedding conjugate (oracle/rope.py) ---------------------------------
+
+def _angle_tables(rng, max_pos, d):
+    ang = rng.uniform(-np.pi, np.pi, (max_pos, d // 2))
+    return np.cos(ang), np.sin(ang)
+
+
+def test_rope_conjugate_is_the_transpose_of_the_rotation():
+    """<R x, y> = <x, R^T y> for random angles and positions, and with
+    cos^2 + sin^2 = 1 the conjugate undoes the rotation."""
+    rng = np.random.default_rng(21)
+    d, rows, h, max_pos = 8, 7, 2, 5
+    cos, sin = _angle_tables(rng, max_pos, d)
+    pos = rng.integers(0, max_pos, rows)
+    x = rng.standard_normal((rows, h, d))
+    y = rng.standard_normal((rows, h, d))
+    lhs = float((oracle.rope_rotate(x, cos, sin, pos) * y).sum())
+    rhs = float((x * oracle.rope_conjugate(y, cos, sin, pos)).sum())
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+    back = oracle.rope_conjugate(oracle.rope_rotate(x, cos, sin, pos), cos, sin, pos)
+    np.testing.assert_allclose(back, x, atol=1e-12)
+
+
+def test_rope_quarter_turn_closed_form():
+    """At a quarter turn (cos 0, sin 1) each pair (a, b) = (x[d], x[d + D/2])
+    becomes (-b, a), and the conjugate turns it back: (a, b) -> (b, -a)."""
+    d = 4
+    x = np.arange(1.0, 1.0 + 2 * d).reshape(2, 1, d)
+    cos, sin, pos = np.zeros((1, d // 2)), np.ones((1, d // 2)), np.zeros(2, dtype=np.int64)
+    a, b = x[..., : d // 2], x[..., d // 2:]
+    np.testing.assert_array_equal(oracle.rope_rotate(x, cos, sin, pos), np.concatenate([-b, a], axis=2))
+    np.testing.assert_array_equal(oracle.rope_conjugate(x, cos, sin, pos), np.concatenate([b, -a], axis=2))
+
+
+def test_rope_zero_angle_is_the_plain_backward():
+    rng = np.random.default_rng(4)
+    lengths, h, d = [2, 5], 2, 8
+    q, k, v, g, off = _rand_case(rng, lengths, h, d, False, 0)
+    cos, sin = np.ones((6, d // 2)), np.zeros((6, d // 2))
+    pos = np.concatenate([np.arange(n) for n in lengths])
+    kw = dict(broadcast_q=False, causal=True, scale=0.5)
+    got = oracle.backward_rope(q, k, v, off, g, cos, sin, pos, pos, **kw)
+    ref = oracle.backward(q, k, v, off, g, **kw)
+    for a, b in zip(got, ref):
+        np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("broadcast_q,causal", MODES)
+def test_rope_backward_finite_differences(broadcast_q, causal):
+    """Central differences of L(q0, k0) = sum(O(R q0, R k0, V) * G), where attention
+    runs on the rotated vectors, for every element of q0 and k0."""
+    rng = np.random.default_rng(9)
+    lengths, h, d, lq, scale = [1, 3, 4], 2, 4, 3, 0.7
+    q0, k0, v, g, off = _rand_case(rng, lengths, h, d, broadcast_q, lq)
+    cos, sin = _angle_tables(rng, 5, d)
+    pos_k = np.concatenate([np.arange(n) for n in lengths])
+    pos_q = np.arange(lq) if broadcast_q else pos_k
+    kw = dict(broadcast_q=broadcast_q, causal=causal, scale=scale)
+
+    def rot(x, pos):
+        return oracle.rope_rotate(x, cos, sin, pos)
+
+    dq, dk, dv = oracle.backward_rope(rot(q0, pos_q), rot(k0, pos_k), v, off, g, cos, sin, pos_q, pos_k, **kw)
+    np.testing.assert_array_equal(dv, oracle.backward(rot(q0, pos_q), rot(k0, pos_k), v, off, g, **kw)[2])
+
+    def loss(q_, k_):
+        return float((oracle.forward(rot(q_, pos_q), rot(k_, pos_k), v, off, **kw)[0] * g).sum())
+
+    eps = 1e-6
+    for name, x, grad in [("q0", q0, dq), ("k0", k0, dk)]:
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            if name == "q0":
+                num[idx] = (loss(xp, k0) - loss(xm, k0)) / (2 * eps)
+            else:
+                num[idx] = (loss(q0, xp) - loss(q0, xm)) / (2 * eps)
+        err = np.abs(num - grad).max() / max(np.abs(grad).max(), 1e-30)
+        assert err <= 1e-6, (name, err)
+
+
+def test_rope_inputs_recipe():
+    """The generated tables hold cos / sin of p * 10000^(-2d/D) rounded to fp32, and
+    positions count from each sequence's start (broadcast queries: 0 .. Lq - 1)."""
+    case = workloads.make_case([3, 1, 4], heads=1, head_dim=8, broadcast_q=True, q_len=5, seed=0)
+    r = workloads.rope_inputs(case)
+    assert r["cos"].shape == (5, 4) and r["cos"].dtype == torch.float32
+    assert r["pos_k"].tolist() == [0, 1, 2, 0, 0, 1, 2, 3]
+    assert r["pos_q"].tolist() == [0, 1, 2, 3, 4]
+    ang = 3 * 10000.0 ** (-2 * 2 / 8)
+    assert r["cos"][3, 2].item() == np.float32(math.cos(ang))
+    assert r["sin"][3, 2].item() == np.float32(math.sin(ang))

@@ -7,6 +7,8 @@ attention arithmetic.  Values are drawn as float32 N(0, 1) with numpy's PCG64
 
 The five named workloads stand in for the pages' production shapes (batch 1152,
 4 heads, head dim 128, sequences up to about 4k tokens), which are not public.
+``rope_inputs`` lays out the rotary-embedding tables and positions that the fused
+rotary backward takes as inputs.
 """
 from __future__ import annotations
 
@@ -147,6 +149,26 @@ def make_workload(name: str, seed: int = 0, with_grad: bool = True, offsets_dtyp
                      with_grad=with_grad, rng=rng, seed=seed, device=device)
     case["workload"] = w
     return case
+
+
+def rope_inputs(case, base: float = 10000.0):
+    """Rotary-embedding inputs for a case: fp32 tables cos / sin of shape
+    [max_pos, D/2] with angle p * base ** (-2 d / D) (the common frequency recipe,
+    computed in fp64 and rounded to fp32), and int32 positions: every key row's
+    index within its sequence, and every query row's (broadcast: 0 .. Lq - 1;
+    self: the key positions).  CPU tensors."""
+    lengths = np.asarray(case["lengths"], dtype=np.int64)
+    d = case["k"].shape[2]
+    pos_k = np.concatenate([np.arange(n, dtype=np.int64) for n in lengths]) if len(lengths) else \
+        np.zeros(0, dtype=np.int64)
+    pos_q = np.arange(case["q_len"], dtype=np.int64) if case["broadcast_q"] else pos_k
+    max_pos = max(int(lengths.max()) if len(lengths) else 0, int(case["q_len"]), 1)
+    inv = base ** (-2.0 * np.arange(d // 2, dtype=np.float64) / d)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return dict(cos=torch.from_numpy(np.cos(ang).astype(np.float32)),
+                sin=torch.from_numpy(np.sin(ang).astype(np.float32)),
+                pos_q=torch.from_numpy(pos_q.astype(np.int32)),
+                pos_k=torch.from_numpy(pos_k.astype(np.int32)))
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:
