@@ -140,6 +140,51 @@ def cpu_baseline(case, w, budget_s: float):
     }
 
 
+def rope_comparison(args, jfa, w, case, o, lse, dq, dk, dv, ws_f, ws_b):
+    """Fused rotary backward vs plain backward vs plain backward + separate rotary
+    backward, as in the Block Attention page's rotary-fusion table.  The separate
+    rotary backward reads the bf16 gradients, rotates them in fp32 and writes bf16."""
+    q, k, v, g, off = case["q"], case["k"], case["v"], case["g"], case["offsets"]
+    bq, causal, scale = w.broadcast_q, w.causal, case["scale"]
+    r = {x: t.cuda() for x, t in workloads.rope_inputs(case).items()}
+    rope = (r["cos"], r["sin"], r["pos_q"], r["pos_k"])
+    half = w.head_dim // 2
+    jfa.fwd(q, k, v, off, broadcast_q=bq, causal=causal, scale=scale, out=o, lse=lse, workspace=ws_f)
+    kw = dict(broadcast_q=bq, causal=causal, scale=scale, dq=dq, dk=dk, dv=dv, workspace=ws_b)
+
+    def conj(x, pos):
+        c, s_ = r["cos"][pos].unsqueeze(1), r["sin"][pos].unsqueeze(1)
+        xf = x.float()
+        a, b = xf[..., :half], xf[..., half:]
+        return torch.cat([a * c + b * s_, b * c - a * s_], dim=-1).to(torch.bfloat16)
+
+    variants = {
+        "bwd": lambda: jfa.bwd(q, k, v, off, o, lse, g, **kw),
+        "bwd_rope_fused": lambda: jfa.bwd(q, k, v, off, o, lse, g, rope=rope, **kw),
+        "bwd_then_rotary": lambda: (jfa.bwd(q, k, v, off, o, lse, g, **kw),
+                                    conj(dq, r["pos_q"]), conj(dk, r["pos_k"])),
+        "rotary_only": lambda: (conj(dq, r["pos_q"]), conj(dk, r["pos_k"])),
+    }
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, fn in variants.items():
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(args.steps):
+            fn()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        res[name] = round(start.elapsed_time(stop) / args.steps, 4)
+        log(f"{name}: {res[name]:.4f} ms")
+    print(json.dumps({"mode": "rope", "workload": w.name, "steps": args.steps, "ms": res,
+                      "fused_over_plain": round(res["bwd_rope_fused"] / res["bwd"], 4),
+                      "unfused_over_fused": round(res["bwd_then_rotary"] / res["bwd_rope_fused"], 4)}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +195,10 @@ def main():
     ap.add_argument("--schedule", type=int, default=2, help="0 sorted+zigzag, 1 identity, 2 dynamic (default)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rope", action="store_true",
+                    help="instead of the step: time the backward with the fused rotary conjugate "
+                         "(jfa_bwd_rope) against the plain backward, and against the plain backward "
+                         "followed by a separate rotary backward (torch elementwise ops)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (3 times); used to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -194,6 +243,10 @@ def main():
         jfa.fwd(q, k, v, off, broadcast_q=bq, causal=causal, scale=scale, out=o, lse=lse, workspace=ws_f)
         jfa.bwd(q, k, v, off, o, lse, g, broadcast_q=bq, causal=causal, scale=scale,
                 dq=dq, dk=dk, dv=dv, workspace=ws_b)
+
+    if args.rope:
+        rope_comparison(args, jfa, w, case, o, lse, dq, dk, dv, ws_f, ws_b)
+        return
 
     log(f"workload {w.name}: B={len(lengths)} H={w.heads} D={w.head_dim} Lq={w.q_len} "
         f"T={int(lengths.sum())} lengths min/median/mean/max = {lengths.min()}/{np.median(lengths):.0f}/"

@@ -122,6 +122,37 @@ jfa_status_t jfa_bwd(const void* q, const void* k, const void* v,
                      void* dq, void* dk, void* dv,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Backward pass with the rotary-embedding conjugate fused into its epilogues
+ * ("Meta's TLX Block Attention Beats Flash Attention v2 by 2.3x on Blackwell GPUs",
+ * section "The Rotary Fusion Bonus").  q and k are the rotated vectors the forward
+ * attended with, q = R(pos_q) q0 and k = R(pos_k) k0, where R(p) rotates each pair
+ * of elements (d, d + D/2), d < D/2, by the angle whose cosine and sine are
+ * rope_cos[p * D/2 + d] and rope_sin[p * D/2 + d]:
+ *   x'[d] = x[d] cos - x[d + D/2] sin,  x'[d + D/2] = x[d + D/2] cos + x[d] sin.
+ * dq and dk receive the gradients with respect to q0 and k0: the conjugate
+ * rotation R(p)^T applied in fp32 to the attention gradients before their bf16
+ * rounding (dq after the batch sum in broadcast mode).  dv is as in jfa_bwd.
+ *   rope_cos, rope_sin: fp32 device arrays [max_pos][D/2], 16-byte aligned;
+ *   pos_q: int32 device array, one position per query row ([Lq] in broadcast mode,
+ *          [T] in self mode); pos_k: int32 device array [T], one per key row;
+ *   positions outside [0, max_pos) are clamped into it.
+ * dq is rotated either in the fp32 dQ finalize or, on the single-tile path of
+ * jfa_bwd (every self-mode sequence within one 64-key tile, D = 128), by the tiles
+ * before they store it; other single-tile calls take the finalize route.  Same workspace
+ * (jfa_bwd_workspace_size), ownership and error rules as jfa_bwd; null tables or
+ * positions, max_pos outside [1, 2^30] or misaligned tables give
+ * JFA_ERR_INVALID_ARGUMENT. */
+jfa_status_t jfa_bwd_rope(const void* q, const void* k, const void* v,
+                          const void* offsets, int offsets_is_int64,
+                          int64_t batch, int64_t num_heads, int64_t head_dim,
+                          int64_t q_len, int64_t total_kv,
+                          int broadcast_q, int causal, float softmax_scale,
+                          const void* o, const float* lse, const void* d_o,
+                          const float* rope_cos, const float* rope_sin,
+                          const int32_t* pos_q, const int32_t* pos_k, int64_t max_pos,
+                          void* dq, void* dk, void* dv,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Measurement support.  While enabled on a thread, every kernel this library
  * launches from that thread is bracketed by two HIP events recorded on the
  * launch stream (events are created on first use and reused).  Kernel names:

@@ -110,3 +110,26 @@ def test_schedule_selector(lib):
             _binding.set_schedule(7)
     finally:
         _binding.set_schedule(old)
+
+
+def bwd_rope(lib, *, batch=4, heads=2, head_dim=128, q_len=64, total_kv=100, bq=1, causal=0, scale=0.1,
+             cos=FAKE, sin=FAKE, pos_q=FAKE, pos_k=FAKE, max_pos=300, ws=FAKE, ws_bytes=1 << 30):
+    return lib.jfa_bwd_rope(FAKE, FAKE, FAKE, FAKE, 0, batch, heads, head_dim, q_len, total_kv, bq, causal,
+                            scale, FAKE, FAKE, FAKE, cos, sin, pos_q, pos_k, max_pos, FAKE, FAKE, FAKE,
+                            ws, ws_bytes, None)
+
+
+def test_rope_rejections(lib):
+    assert bwd_rope(lib, cos=None) == INVALID
+    assert bwd_rope(lib, sin=None) == INVALID
+    assert bwd_rope(lib, pos_q=None) == INVALID
+    assert bwd_rope(lib, pos_k=None) == INVALID
+    assert b"rotary" in lib.jfa_last_error()
+    assert bwd_rope(lib, max_pos=0) == INVALID
+    assert bwd_rope(lib, cos=ctypes.c_void_p((1 << 20) + 4)) == INVALID    # tables 16-byte aligned
+    assert bwd_rope(lib, pos_k=ctypes.c_void_p((1 << 20) + 2)) == INVALID  # positions 4-byte aligned
+    # the plain backward's checks apply too, under this entry point's name
+    assert bwd_rope(lib, head_dim=96) == UNSUPPORTED
+    assert b"jfa_bwd_rope" in lib.jfa_last_error()
+    assert bwd_rope(lib, ws_bytes=16) == WS_SMALL
+    assert bwd_rope(lib, batch=0, ws=None) == OK                            # empty: a no-op

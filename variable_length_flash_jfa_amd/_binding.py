@@ -65,6 +65,9 @@ def library() -> ctypes.CDLL:
             lib.jfa_bwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, i64, i32, i32, f32,
                                     vp, vp, vp, vp, vp, vp, vp, sz, vp]
             lib.jfa_bwd.restype = i32
+            lib.jfa_bwd_rope.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, i64, i32, i32, f32,
+                                         vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
+            lib.jfa_bwd_rope.restype = i32
             lib.jfa_last_error.argtypes = []
             lib.jfa_last_error.restype = ctypes.c_char_p
             lib.jfa_version.argtypes = []
@@ -187,8 +190,13 @@ def fwd(q, k, v, offsets, *, broadcast_q: bool, causal: bool = False, scale=None
 
 
 def bwd(q, k, v, offsets, o, lse, d_o, *, broadcast_q: bool, causal: bool = False, scale=None,
-        dq=None, dk=None, dv=None, workspace=None):
-    """dQ, dK, dV = jfa_bwd(...) (bf16, shapes of q, k, v)."""
+        dq=None, dk=None, dv=None, workspace=None, rope=None):
+    """dQ, dK, dV = jfa_bwd(...) (bf16, shapes of q, k, v).
+
+    rope: optional (cos, sin, pos_q, pos_k) for jfa_bwd_rope: fp32 tables
+    [max_pos, D/2] and int32 positions of the query rows and key rows, all on the
+    GPU; q and k are then the rotated inputs and dQ, dK are returned with respect
+    to the unrotated ones."""
     _validate(q, k, v, offsets)
     batch, heads, head_dim, q_len, total_kv, rows = _sizes(q, k, offsets, broadcast_q)
     for name, t, dt in (("o", o, torch.bfloat16), ("d_o", d_o, torch.bfloat16), ("lse", lse, torch.float32)):
@@ -204,10 +212,27 @@ def bwd(q, k, v, offsets, o, lse, d_o, *, broadcast_q: bool, causal: bool = Fals
     need = bwd_workspace_size(batch, heads, head_dim, q_len, total_kv, broadcast_q, causal)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    st = library().jfa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(offsets),
-                           int(offsets.dtype == torch.int64), batch, heads, head_dim, q_len,
-                           total_kv, int(broadcast_q), int(causal), scale, _ptr(o), _ptr(lse),
-                           _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
-                           workspace.numel(), _stream(dev))
+    if rope is None:
+        st = library().jfa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(offsets),
+                               int(offsets.dtype == torch.int64), batch, heads, head_dim, q_len,
+                               total_kv, int(broadcast_q), int(causal), scale, _ptr(o), _ptr(lse),
+                               _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                               workspace.numel(), _stream(dev))
+    else:
+        cos, sin, pos_q, pos_k = rope
+        for name, t, dt in (("cos", cos, torch.float32), ("sin", sin, torch.float32),
+                            ("pos_q", pos_q, torch.int32), ("pos_k", pos_k, torch.int32)):
+            if t.dtype != dt or not t.is_contiguous() or not t.is_cuda:
+                raise ValueError(f"rope {name} must be a contiguous {dt} GPU tensor")
+        if cos.dim() != 2 or cos.shape != sin.shape or cos.shape[1] * 2 != head_dim:
+            raise ValueError("rope cos / sin must both be [max_pos, head_dim / 2]")
+        if pos_q.shape != (q.shape[0],) or pos_k.shape != (k.shape[0],):
+            raise ValueError("rope positions must be [q rows] and [k rows]")
+        st = library().jfa_bwd_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(offsets),
+                                    int(offsets.dtype == torch.int64), batch, heads, head_dim, q_len,
+                                    total_kv, int(broadcast_q), int(causal), scale, _ptr(o), _ptr(lse),
+                                    _ptr(d_o), _ptr(cos), _ptr(sin), _ptr(pos_q), _ptr(pos_k),
+                                    cos.shape[0], _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                    workspace.numel(), _stream(dev))
     _check(st)
     return dq, dk, dv

@@ -250,30 +250,34 @@ jfa_status_t jfa_fwd(const void* q, const void* k, const void* v, const void* of
   return JFA_OK;
 }
 
-jfa_status_t jfa_bwd(const void* q, const void* k, const void* v, const void* offsets,
-                     int offsets_is_int64, int64_t batch, int64_t num_heads, int64_t head_dim,
-                     int64_t q_len, int64_t total_kv, int broadcast_q, int causal, float softmax_scale,
-                     const void* o, const float* lse, const void* d_o, void* dq, void* dk, void* dv,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// jfa_bwd and jfa_bwd_rope; `fn` names the entry point in error messages.
+jfa_status_t bwd_impl(const char* fn, const void* q, const void* k, const void* v, const void* offsets,
+                      int offsets_is_int64, int64_t batch, int64_t num_heads, int64_t head_dim,
+                      int64_t q_len, int64_t total_kv, int broadcast_q, int causal, float softmax_scale,
+                      const void* o, const float* lse, const void* d_o, void* dq, void* dk, void* dv,
+                      const jfa::Rope& rope, void* workspace, size_t workspace_bytes, void* stream) {
   g_error[0] = '\0';
   const Sizes sz = check_sizes(batch, num_heads, head_dim, q_len, total_kv, broadcast_q, causal);
-  if (!sz.ok) return fail(sz.st, "jfa_bwd: %s", sz.why);
+  if (!sz.ok) return fail(sz.st, "%s: %s", fn, sz.why);
   if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
-    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_bwd: softmax_scale must be finite and > 0");
-  const jfa::Problem p = make_problem(q, k, v, offsets, offsets_is_int64, batch, num_heads, head_dim,
-                                      q_len, total_kv, broadcast_q, causal, softmax_scale);
+    return fail(JFA_ERR_INVALID_ARGUMENT, "%s: softmax_scale must be finite and > 0", fn);
+  jfa::Problem p = make_problem(q, k, v, offsets, offsets_is_int64, batch, num_heads, head_dim,
+                                q_len, total_kv, broadcast_q, causal, softmax_scale);
+  p.rope = rope.cos != nullptr ? 1 : 0;
   if (p.batch == 0 || p.rows == 0) return JFA_OK;
   if (!q || !offsets || !o || !lse || !d_o || !dq || !workspace ||
       (p.total_kv > 0 && (!k || !v || !dk || !dv)))
-    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_bwd: null pointer argument");
+    return fail(JFA_ERR_INVALID_ARGUMENT, "%s: null pointer argument", fn);
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(d_o) ||
       misaligned(dq) || misaligned(dk) || misaligned(dv) || misaligned(workspace) ||
       (reinterpret_cast<uintptr_t>(lse) & 3) ||
       (reinterpret_cast<uintptr_t>(offsets) & (offsets_is_int64 ? 7 : 3)))
-    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_bwd: tensors must be 16-byte aligned");
+    return fail(JFA_ERR_INVALID_ARGUMENT, "%s: tensors must be 16-byte aligned", fn);
   const size_t need = bwd_ws_bytes(p);
   if (workspace_bytes < need)
-    return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "jfa_bwd: workspace of %zu bytes, need %zu",
+    return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, need %zu", fn,
                 workspace_bytes, need);
   char* cur = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(workspace)));
   jfa::Plan plan;
@@ -294,14 +298,53 @@ jfa_status_t jfa_bwd(const void* q, const void* k, const void* v, const void* of
   if (e != hipSuccess) return hip_fail(e, "jfa_bwd: delta launch");
   if (p.total_kv > 0) {
     e = timed_launch("bwd", s, [&] {
-      return jfa::launch_bwd(p, plan, sched, rowstat, lse, d_o, dq_acc, dq, dk, dv, s);
+      return jfa::launch_bwd(p, plan, sched, rowstat, lse, d_o, dq_acc, dq, dk, dv, rope, s);
     });
     if (e != hipSuccess) return hip_fail(e, "jfa_bwd: kernel launch");
   }
   e = timed_launch("dq_finalize", s,
-                   [&] { return jfa::launch_dq_finalize(p, dq_acc, dq, plan.meta, s); });
+                   [&] { return jfa::launch_dq_finalize(p, dq_acc, dq, plan.meta, rope, s); });
   if (e != hipSuccess) return hip_fail(e, "jfa_bwd: dq finalize launch");
   return JFA_OK;
+}
+
+}  // namespace
+
+jfa_status_t jfa_bwd(const void* q, const void* k, const void* v, const void* offsets,
+                     int offsets_is_int64, int64_t batch, int64_t num_heads, int64_t head_dim,
+                     int64_t q_len, int64_t total_kv, int broadcast_q, int causal, float softmax_scale,
+                     const void* o, const float* lse, const void* d_o, void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl("jfa_bwd", q, k, v, offsets, offsets_is_int64, batch, num_heads, head_dim, q_len,
+                  total_kv, broadcast_q, causal, softmax_scale, o, lse, d_o, dq, dk, dv, jfa::Rope{},
+                  workspace, workspace_bytes, stream);
+}
+
+jfa_status_t jfa_bwd_rope(const void* q, const void* k, const void* v, const void* offsets,
+                          int offsets_is_int64, int64_t batch, int64_t num_heads, int64_t head_dim,
+                          int64_t q_len, int64_t total_kv, int broadcast_q, int causal,
+                          float softmax_scale, const void* o, const float* lse, const void* d_o,
+                          const float* rope_cos, const float* rope_sin, const int32_t* pos_q,
+                          const int32_t* pos_k, int64_t max_pos, void* dq, void* dk, void* dv,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  g_error[0] = '\0';
+  if (!rope_cos || !rope_sin || !pos_q || (total_kv > 0 && !pos_k))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_bwd_rope: null rotary table or position pointer");
+  if (max_pos < 1 || max_pos > (int64_t)1 << 30)
+    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_bwd_rope: max_pos must be in [1, 2^30]");
+  if (misaligned(rope_cos) || misaligned(rope_sin) || (reinterpret_cast<uintptr_t>(pos_q) & 3) ||
+      (reinterpret_cast<uintptr_t>(pos_k) & 3))
+    return fail(JFA_ERR_INVALID_ARGUMENT,
+                "jfa_bwd_rope: rotary tables must be 16-byte aligned, positions 4-byte aligned");
+  jfa::Rope rope;
+  rope.cos = rope_cos;
+  rope.sin = rope_sin;
+  rope.pos_q = pos_q;
+  rope.pos_k = pos_k;
+  rope.max_pos = (int)max_pos;
+  return bwd_impl("jfa_bwd_rope", q, k, v, offsets, offsets_is_int64, batch, num_heads, head_dim, q_len,
+                  total_kv, broadcast_q, causal, softmax_scale, o, lse, d_o, dq, dk, dv, rope, workspace,
+                  workspace_bytes, stream);
 }
 
 jfa_status_t jfa_profile_enable(int enable) {

@@ -117,6 +117,12 @@ struct BwdArgs {
   const int4* items;
   int* meta;
   int sched;
+  // rotary conjugate of dK (null cos: none); tables [max_pos][D/2], key positions [T]
+  const float* rope_cos;
+  const float* rope_sin;
+  const int* rope_pos_k;
+  const int* rope_pos_q;   // query positions (the single-tile path rotates dQ itself)
+  int rope_max_pos;
 };
 
 // LDS offsets below are byte offsets from the start of the kernel's LDS block.  A
@@ -127,7 +133,9 @@ struct BwdArgs {
 // XOR and its constant part rides in the instruction's offset field.
 // DIRECT: self mode with every sequence in one tile (the plan flags such a call in
 // meta[3]); delta is formed inline and dQ is stored, not reduce-added.
-template <int D, int NW, bool BCAST, bool CAUSAL, bool DIRECT>
+// ROPE: the rotary conjugate is applied to dK in the epilogue (and to dQ where the
+// tiles store it); without it none of that code is compiled in.
+template <int D, int NW, bool BCAST, bool CAUSAL, bool DIRECT, bool ROPE>
 struct BwdKernel {
   static constexpr int BN = 32 * NW;         // keys per tile (NW waves x 32)
   static constexpr int BQ = kBwdBQ;          // query rows per block
@@ -155,6 +163,8 @@ struct BwdKernel {
   static constexpr uint32_t GQ = OFF_DO - OFF_Q;              // dO tile minus Q tile, same buffer
   static constexpr int XB = D == 128 ? 256 : 128;             // the XOR-free granule
   static_assert(BN == 32 * NW && KP * DT == NW * DTW && DTW <= 2 && KPART % 16 == 0, "tile shape");
+  static_assert(!(DIRECT && ROPE) || (KP == 1 && DTW == 2),
+                "the single-tile rotary path needs both halves of a dQ column pair in one wave");
   static_assert(OFF_Q % XB == 0 && QT_BYTES % XB == 0 && GQ % XB == 0 && (KPART * 2 * D) % XB == 0 &&
                     (32 * 2 * D) % XB == 0 && OFF_DS % 64 == 0 && (KPART * BQ * 2) % 64 == 0,
                 "tile offsets must commute with the swizzle XOR");
@@ -185,7 +195,7 @@ struct BwdKernel {
     c32 = lane & 31;
     hf = lane >> 5;
     rs = (int64_t)a.heads * D;
-    dq_dt = (wave % (DT / DTW)) * DTW;   // even when a wave takes two d tiles
+    dq_dt = wave % (DT / DTW);   // with two d tiles a wave takes dq_dt and dq_dt + DT / 2
     dq_part = wave / (DT / DTW);
     row_base = row_read_base<D>(lane);
     k_row_base = row_base + (uint32_t)(OFF_K + 32 * wave * 2 * D);
@@ -474,20 +484,22 @@ struct BwdKernel {
       for (int r = 0; r < 16; ++r) acc0[r] += acc1[r];
       out[0] = acc0;
     } else {
-      // two d tiles (the second one's chunk index is the first's plus one, an XOR
-      // since the first is even): two independent chains sharing the dS operand
+      // two d tiles, dq_dt and dq_dt + DT / 2 = dq_dt + 2 (an XOR of the chunk index
+      // with 8, since dq_dt < 2), so that a lane holds columns d and d + D / 2 of its
+      // rows (the pairs of the rotary conjugate): two independent chains sharing the
+      // dS operand
       out[0] = zero16();
       out[DTW - 1] = zero16();
       bf16x8 sa = ds_op(0);
       bf16x8 k0 = lds_operand_tr<D>(smem, kb8, 0, 4, 0);
-      bf16x8 k1 = lds_operand_tr<D>(smem, kb8, 0, 4, 1);
+      bf16x8 k1 = lds_operand_tr<D>(smem, kb8, 0, 4, DT / 2);
 #pragma unroll
       for (int jj = 0; jj < KPART; jj += 16) {
         bf16x8 sa_n = sa, k0_n = k0, k1_n = k1;
         if (jj + 16 < KPART) {
           sa_n = ds_op(jj + 16);
           k0_n = lds_operand_tr<D>(smem, kb8, jj + 16, jj + 20, 0);
-          k1_n = lds_operand_tr<D>(smem, kb8, jj + 16, jj + 20, 1);
+          k1_n = lds_operand_tr<D>(smem, kb8, jj + 16, jj + 20, DT / 2);
         }
         out[0] = mfma32(sa, k0, out[0]);
         out[DTW - 1] = mfma32(sa, k1, out[DTW - 1]);
@@ -528,7 +540,7 @@ struct BwdKernel {
       // (row, column) with the same row grouping and bounds
       const uint32_t row_bytes = (uint32_t)(a.heads * D * 2);
       bf16* base = a.dq + ((kv0 + qi0) * a.heads + h) * D;
-      const uint32_t o0 = (dq_lane_off() >> 1) + 64u * dtk;   // fp32 lane offset -> bf16
+      const uint32_t o0 = (dq_lane_off() >> 1) + (uint32_t)(D / 2 * 2) * dtk;   // fp32 -> bf16 offset
       const uint32_t o[4] = {o0, o0 + row_bytes, o0 + 2 * row_bytes, o0 + 3 * row_bytes};
 #pragma unroll
       for (int k = 0; k < NG; ++k) {
@@ -546,7 +558,7 @@ struct BwdKernel {
     const int64_t qrow0 = BCAST ? (int64_t)(blockIdx.x & (kDqStripes - 1)) * a.q_len + qi0 : kv0 + qi0;
     const uint32_t row_bytes = (uint32_t)(a.heads * D * 4);
     float* base = a.dq_acc + (qrow0 * a.heads + h) * D;
-    const uint32_t o0 = dq_lane_off() + 128u * dtk;
+    const uint32_t o0 = dq_lane_off() + (uint32_t)(D / 2 * 4) * dtk;   // second d tile: + D / 2 columns
     const uint32_t o[4] = {o0, o0 + row_bytes, o0 + 2 * row_bytes, o0 + 3 * row_bytes};
 #pragma unroll
     for (int k = 0; k < NG; ++k) {
@@ -562,6 +574,7 @@ struct BwdKernel {
   __device__ __forceinline__ void dq_atomics_all(int qi0) {
     f32x16 dq[DTW];
     dq_compute(dq);
+    if constexpr (DIRECT && ROPE) rope_conjugate_dq(dq, qi0);
 #pragma unroll
     for (int k = 0; k < DTW; ++k) {
       const f32x4 v[4] = {{dq[k][0], dq[k][1], dq[k][2], dq[k][3]},
@@ -611,9 +624,17 @@ struct BwdKernel {
   __device__ __forceinline__ void run(int qs, int qe, int q_last, int& pending) {
     for (int qi0 = qs; qi0 < qe; qi0 += BQ) {
       const int buf = (qi0 / BQ) & 1;
+      // With the rotary conjugate in the single-tile path the dQ of the pending block
+      // reads table entries: done before the next block's loads are issued, so that
+      // waiting for those entries does not wait for the loads (vector memory
+      // operations complete in order).
+      constexpr bool kDqFirst = DIRECT && ROPE;
+      if constexpr (kDqFirst) {
+        if (pending >= 0) dq_atomics_all(pending);
+      }
       if (qi0 + BQ < q_last) load_qblock(qi0 + BQ, buf ^ 1);   // one block ahead
       if constexpr (KP == 1) {
-        if (pending >= 0) dq_atomics_all(pending);
+        if (!kDqFirst && pending >= 0) dq_atomics_all(pending);
         qblock<MASKED, true>(buf, qi0);
       } else {
         if (pending >= 0 && dq_part < nparts) dq_publish(dq_compute1());
@@ -622,7 +643,7 @@ struct BwdKernel {
         qblock<MASKED, false>(buf, qi0);
       }
       if (qi0 + BQ < q_last) {   // the next block's loads must have landed
-        if (pending >= 0) {
+        if (!kDqFirst && pending >= 0) {
           wait_vmcnt<4 * FLUSH_GROUPS * DTW>();   // the reduce-adds issued after them stay in flight
         } else {
           wait_lds_loads();
@@ -701,6 +722,73 @@ struct BwdKernel {
     return smem + OFF_DS + (wave - 2) * SLOT_BYTES;
   }
 
+  // Rotary conjugate of a query block's dQ in the single-tile path, where the tile
+  // stores dQ itself: with two d tiles per wave, register r of dq[0] and dq[1] holds
+  // columns d = 32 dq_dt + lane % 32 and d + D / 2 of row
+  // 8 (r / 4) + 4 (lane / 32) + r % 4 (the MFMA C layout), the rotated pair.
+  __device__ __forceinline__ void rope_conjugate_dq(f32x16 (&dq)[DTW], int qi0) {
+    const int d = 32 * dq_dt + c32;
+    // eight rows at a time (their 16 table values live together; the kernel has
+    // little register room here)
+#pragma unroll
+    for (int r0 = 0; r0 < 16; r0 += 8) {
+      float c[8], sn[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = r0 + i;
+        const int row = qi0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        int pos = row < q_rows ? a.rope_pos_q[kv0 + row] : 0;
+        pos = min(max(pos, 0), a.rope_max_pos - 1);
+        c[i] = a.rope_cos[(int64_t)pos * (D / 2) + d];
+        sn[i] = a.rope_sin[(int64_t)pos * (D / 2) + d];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = r0 + i;
+        const float lo = dq[0][r], hi = dq[DTW - 1][r];
+        dq[0][r] = lo * c[i] + hi * sn[i];
+        dq[DTW - 1][r] = hi * c[i] - lo * sn[i];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Rotary conjugate of this wave's dK^T accumulators, in fp32 before the bf16
+  // rounding ("Meta's TLX Block Attention Beats Flash Attention v2 by 2.3x on
+  // Blackwell GPUs", section "The Rotary Fusion Bonus").  The pair (d, d + D/2) of
+  // the lane's key row sits in the same register of d tiles dt and dt + DT/2:
+  //   dk[d] = g[d] cos + g[d + D/2] sin,  dk[d + D/2] = g[d + D/2] cos - g[d] sin
+  // with (cos, sin) of the key's position; register r of d tile dt holds
+  // d = 32 dt + 8 (r / 4) + 4 (lane / 32) + r % 4, so four consecutive table entries
+  // serve four registers.
+  __device__ __forceinline__ void rope_conjugate_dk() {
+    const int j = j0 + 32 * wave + c32;
+    int pos = j < n ? a.rope_pos_k[kv0 + j] : 0;
+    pos = min(max(pos, 0), a.rope_max_pos - 1);
+    const float* cr = a.rope_cos + (int64_t)pos * (D / 2);
+    const float* sr = a.rope_sin + (int64_t)pos * (D / 2);
+    // one d-tile pair at a time: its 32 table values are loaded together, then used
+    // (the epilogue holds little register room)
+#pragma unroll
+    for (int dt = 0; dt < DT / 2; ++dt) {
+      f32x4 c4[4], s4[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * dt + 8 * q4 + 4 * hf;
+        c4[q4] = *reinterpret_cast<const f32x4*>(cr + d0);
+        s4[q4] = *reinterpret_cast<const f32x4*>(sr + d0);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float c = c4[r / 4][r % 4], sn = s4[r / 4][r % 4];
+        const float lo = dkt[dt][r], hi = dkt[dt + DT / 2][r];
+        dkt[dt][r] = lo * c + hi * sn;
+        dkt[dt + DT / 2][r] = hi * c - lo * sn;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
   // One tile whose K/V and first query block loads have been issued (`first`: by
   // the kernel prologue, so nothing else is in flight).  `pre` runs after the first
   // barrier.  After the query loop `next(ng)` names the following tile (or returns
@@ -760,7 +848,8 @@ struct BwdKernel {
     run<false>(qm, qfull, q_last, pending);
     run<true>(qfull, q_last, q_last, pending);
     const bool more = next(ng);
-    if (more) issue_v(ng);
+    constexpr bool kDqFirst = DIRECT && ROPE;   // as in run(): the table reads go first
+    if (more && !kDqFirst) issue_v(ng);
     if (pending >= 0) {
       if constexpr (KP == 1) {
         dq_atomics_all(pending);
@@ -770,6 +859,7 @@ struct BwdKernel {
         dq_flush(pending);
       }
     }
+    if (more && kDqFirst) issue_v(ng);
     __syncthreads();   // every wave is past its last read of the K tile, dQ partials and query blocks
     if (more) {
       issue_k(ng);
@@ -781,6 +871,7 @@ struct BwdKernel {
       const int nrows = min(max(n - (j0 + 32 * wave), 0), 32);
       char* slot = epilogue_slot(more ? first_qbuf(ng) ^ 1 : 0);
       const int64_t off = (kv0 + j0 + 32 * wave) * rs + (int64_t)h * D;
+      if constexpr (ROPE) rope_conjugate_dk();
       store_acc_rows<D, EPI_PASSES>(dkt, a.scale, slot, a.dk + off, rs, nrows, lane);
       store_acc_rows<D, EPI_PASSES>(dvt, 1.f, slot, a.dv + off, rs, nrows, lane);
     }
@@ -788,12 +879,12 @@ struct BwdKernel {
   }
 };
 
-template <int D, int NW, bool BCAST, bool CAUSAL, bool DIRECT>
+template <int D, int NW, bool BCAST, bool CAUSAL, bool DIRECT, bool ROPE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_kernel(BwdArgs a) {
   // self mode launches both variants; the plan's meta[3] picks the one that runs
   if ((__builtin_amdgcn_readfirstlane(a.meta[3]) != 0) != DIRECT) return;
-  using K = BwdKernel<D, NW, BCAST, CAUSAL, DIRECT>;
+  using K = BwdKernel<D, NW, BCAST, CAUSAL, DIRECT, ROPE>;
   using Geo = typename K::Geo;
   __shared__ __attribute__((aligned(16))) char smem[K::SMEM];
   __shared__ __attribute__((aligned(16))) int next_item[64];   // DMA target, 16 bytes used
@@ -871,36 +962,93 @@ __global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restric
   }
 }
 
-template <int D, int NW, bool BCAST, bool CAUSAL, bool DIRECT>
+// dQ finalize with the rotary conjugate: sum of the stripes, times the softmax
+// scale, rotated by the opposite angle of the query row's position, -> bf16.  One
+// thread takes four columns d .. d + 3 (d < D/2) of a (row, head) and their partners
+// d + D/2 .. d + D/2 + 3.  CHECK as for dq_finalize_kernel (the tiles may have
+// stored dQ, rotated, themselves).
+template <int D, bool CHECK>
+__global__ __launch_bounds__(256) void dq_finalize_rope_kernel(const float* __restrict__ acc,
+                                                               bf16* __restrict__ dq, int64_t rows,
+                                                               int heads, int64_t stripe_elems,
+                                                               int stripes, float scale,
+                                                               const float* __restrict__ rcos,
+                                                               const float* __restrict__ rsin,
+                                                               const int* __restrict__ pos_q,
+                                                               int max_pos, const int* __restrict__ meta) {
+  if (CHECK && meta[3] != 0) return;   // the tiles wrote dQ
+  constexpr int G = D / 8;   // four-column groups in each half
+  const int64_t total = rows * heads * G;
+  const int64_t step = CHECK ? (int64_t)gridDim.x * 256 : total;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += step) {
+    const int64_t rh = t / G;   // row * heads + head
+    const int g = (int)(t - rh * G);
+    const int64_t row = rh / heads;
+    const int64_t e0 = rh * D + 4 * g;
+    f32x4 lo = *reinterpret_cast<const f32x4*>(acc + e0);
+    f32x4 hi = *reinterpret_cast<const f32x4*>(acc + e0 + D / 2);
+    for (int k = 1; k < stripes; ++k) {
+      lo += *reinterpret_cast<const f32x4*>(acc + e0 + k * stripe_elems);
+      hi += *reinterpret_cast<const f32x4*>(acc + e0 + D / 2 + k * stripe_elems);
+    }
+    const int pos = min(max(pos_q[row], 0), max_pos - 1);
+    const f32x4 c = *reinterpret_cast<const f32x4*>(rcos + (int64_t)pos * (D / 2) + 4 * g);
+    const f32x4 sn = *reinterpret_cast<const f32x4*>(rsin + (int64_t)pos * (D / 2) + 4 * g);
+    bf16x4 olo, ohi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a0 = lo[e] * scale, b0 = hi[e] * scale;
+      olo[e] = (bf16)(a0 * c[e] + b0 * sn[e]);
+      ohi[e] = (bf16)(b0 * c[e] - a0 * sn[e]);
+    }
+    *reinterpret_cast<bf16x4*>(dq + e0) = olo;
+    *reinterpret_cast<bf16x4*>(dq + e0 + D / 2) = ohi;
+  }
+}
+
+template <int D, int NW, bool BCAST, bool CAUSAL, bool DIRECT, bool ROPE>
 hipError_t launch_bwd_one(const BwdArgs& a, hipStream_t s, int64_t max_tiles) {
-  const void* fn = reinterpret_cast<const void*>(&bwd_kernel<D, NW, BCAST, CAUSAL, DIRECT>);
+  const void* fn = reinterpret_cast<const void*>(&bwd_kernel<D, NW, BCAST, CAUSAL, DIRECT, ROPE>);
   const int grid = persistent_grid(fn, 64 * NW, max_tiles);
-  hipLaunchKernelGGL((bwd_kernel<D, NW, BCAST, CAUSAL, DIRECT>), dim3(grid), dim3(64 * NW), 0, s, a);
+  hipLaunchKernelGGL((bwd_kernel<D, NW, BCAST, CAUSAL, DIRECT, ROPE>), dim3(grid), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 // Broadcast mode has one variant.  In self mode whether every sequence fits one
 // tile is known on the device only (meta[3], from the plan), so both variants are
-// launched and the one that does not match returns at once.
-template <int D, int NW, bool BCAST, bool CAUSAL>
+// launched and the one that does not match returns at once.  With the rotary
+// conjugate the single-tile variant exists only for two d tiles per wave (D = 128,
+// two waves), see single_tile_allowed.
+template <int D, int NW, bool BCAST, bool CAUSAL, bool ROPE>
 hipError_t launch_bwd_inst(const BwdArgs& a, hipStream_t s, int64_t max_tiles, bool maybe_single) {
   if constexpr (BCAST) {
-    return launch_bwd_one<D, NW, true, false, false>(a, s, max_tiles);
+    return launch_bwd_one<D, NW, true, false, false, ROPE>(a, s, max_tiles);
   } else {
-    if (maybe_single) {
-      const hipError_t e = launch_bwd_one<D, NW, false, CAUSAL, true>(a, s, max_tiles);
-      if (e != hipSuccess) return e;
+    constexpr bool kDirect = !ROPE || (D == 128 && NW == 2);
+    if constexpr (kDirect) {
+      if (maybe_single) {
+        const hipError_t e = launch_bwd_one<D, NW, false, CAUSAL, true, ROPE>(a, s, max_tiles);
+        if (e != hipSuccess) return e;
+      }
     }
-    return launch_bwd_one<D, NW, false, CAUSAL, false>(a, s, max_tiles);
+    return launch_bwd_one<D, NW, false, CAUSAL, false, ROPE>(a, s, max_tiles);
   }
+}
+
+template <int D, int NW, bool ROPE>
+hipError_t launch_bwd_dwr(const Problem& p, const BwdArgs& a, hipStream_t s) {
+  const int64_t max_tiles = bwd_max_items(p) * p.heads;
+  const bool ms = maybe_single_tile(p);
+  if (p.broadcast) {
+    if constexpr (NW == 8) return launch_bwd_inst<D, NW, true, false, ROPE>(a, s, max_tiles, ms);
+    return hipErrorInvalidValue;   // broadcast mode always takes eight waves
+  }
+  if (p.causal) return launch_bwd_inst<D, NW, false, true, ROPE>(a, s, max_tiles, ms);
+  return launch_bwd_inst<D, NW, false, false, ROPE>(a, s, max_tiles, ms);
 }
 
 template <int D, int NW>
 hipError_t launch_bwd_dw(const Problem& p, const BwdArgs& a, hipStream_t s) {
-  const int64_t max_tiles = bwd_max_items(p) * p.heads;
-  const bool ms = maybe_single_tile(p);
-  if (p.broadcast) return launch_bwd_inst<D, NW, true, false>(a, s, max_tiles, ms);
-  if (p.causal) return launch_bwd_inst<D, NW, false, true>(a, s, max_tiles, ms);
-  return launch_bwd_inst<D, NW, false, false>(a, s, max_tiles, ms);
+  return p.rope ? launch_bwd_dwr<D, NW, true>(p, a, s) : launch_bwd_dwr<D, NW, false>(p, a, s);
 }
 
 template <int D>
@@ -927,8 +1075,14 @@ int bwd_waves(const Problem& p) {
 
 // Whether every sequence may lie within one backward tile (self mode, and the mean
 // length at most the tile's keys); the plan decides on the device (meta[3]).
+bool single_tile_allowed(const Problem& p) {
+  // with the rotary conjugate the tiles can rotate dQ only when a lane holds both
+  // halves of its columns: two d tiles per wave (D = 128, two waves)
+  return !p.broadcast && (!p.rope || (p.head_dim == 128 && bwd_waves(p) == 2));
+}
+
 bool maybe_single_tile(const Problem& p) {
-  return !p.broadcast && p.total_kv <= (int64_t)p.batch * 32 * bwd_waves(p);
+  return single_tile_allowed(p) && p.total_kv <= (int64_t)p.batch * 32 * bwd_waves(p);
 }
 
 int64_t bwd_max_items(const Problem& p) {
@@ -961,7 +1115,7 @@ hipError_t launch_bwd_pre(const Problem& p, const void* o, const void* d_o, cons
 
 hipError_t launch_bwd(const Problem& p, const Plan& plan, int sched, const float* rowstat,
                       const float* lse, const void* d_o, float* dq_acc, void* dq, void* dk, void* dv,
-                      hipStream_t s) {
+                      const Rope& rope, hipStream_t s) {
   BwdArgs a;
   a.q = static_cast<const bf16*>(p.q);
   a.k = static_cast<const bf16*>(p.k);
@@ -980,6 +1134,11 @@ hipError_t launch_bwd(const Problem& p, const Plan& plan, int sched, const float
   a.dq = static_cast<bf16*>(dq);
   a.dk = static_cast<bf16*>(dk);
   a.dv = static_cast<bf16*>(dv);
+  a.rope_cos = rope.cos;
+  a.rope_sin = rope.sin;
+  a.rope_pos_k = rope.pos_k;
+  a.rope_pos_q = rope.pos_q;
+  a.rope_max_pos = rope.max_pos;
   a.items = plan.items;
   a.meta = plan.meta;
   a.sched = sched;
@@ -987,9 +1146,27 @@ hipError_t launch_bwd(const Problem& p, const Plan& plan, int sched, const float
 }
 
 hipError_t launch_dq_finalize(const Problem& p, const float* dq_acc, void* dq, const int* meta,
-                              hipStream_t s) {
+                              const Rope& rope, hipStream_t s) {
   const int64_t q_rows = p.broadcast ? p.q_len : p.total_kv;
   const int64_t n = q_rows * p.heads * p.head_dim;
+  if (rope.cos != nullptr) {
+    const int64_t threads = q_rows * p.heads * (p.head_dim / 8);
+    int64_t rblocks = (threads + 255) / 256;
+    if (rblocks == 0) return hipSuccess;
+    const bool check = maybe_single_tile(p);
+    if (check) rblocks = std::min<int64_t>(rblocks, (int64_t)device_cu_count() * 32);
+    auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3((unsigned)rblocks), dim3(256), 0, s, dq_acc, static_cast<bf16*>(dq),
+                         q_rows, p.heads, n, p.broadcast ? kDqStripes : 1, p.scale, rope.cos, rope.sin,
+                         rope.pos_q, rope.max_pos, meta);
+    };
+    if (p.head_dim == 128) {
+      check ? go(dq_finalize_rope_kernel<128, true>) : go(dq_finalize_rope_kernel<128, false>);
+    } else {
+      check ? go(dq_finalize_rope_kernel<64, true>) : go(dq_finalize_rope_kernel<64, false>);
+    }
+    return hipGetLastError();
+  }
   const int64_t vec4 = n / 4;
   int64_t blocks = (vec4 + 255) / 256;
   if (blocks == 0) return hipSuccess;

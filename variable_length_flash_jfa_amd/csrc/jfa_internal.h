@@ -31,6 +31,18 @@ struct Problem {
   int broadcast;
   int causal;
   float scale;
+  int rope = 0;       // the backward applies the rotary conjugate (no direct dQ store)
+};
+
+// Rotary-embedding conjugate of the backward: fp32 tables [max_pos][D/2] and int32
+// positions of the query rows ([q rows]) and key rows ([T]), clamped to
+// [0, max_pos).  Inactive when cos is null.
+struct Rope {
+  const float* cos = nullptr;
+  const float* sin = nullptr;
+  const int* pos_q = nullptr;
+  const int* pos_k = nullptr;
+  int max_pos = 0;
 };
 
 // Plan written on the device: meta[0] = number of items, meta[1] = dynamic-schedule
@@ -47,7 +59,8 @@ int fwd_waves(const Problem& p);                 // waves per forward workgroup
 int64_t fwd_max_items(const Problem& p);         // capacity of the forward item list
 int64_t bwd_max_items(const Problem& p);         // capacity of the backward item list
 int bwd_waves(const Problem& p);                 // waves per backward workgroup (2, 4 or 8)
-bool maybe_single_tile(const Problem& p);        // every sequence may fit one backward tile
+bool single_tile_allowed(const Problem& p);      // the single-tile backward path may be used
+bool maybe_single_tile(const Problem& p);        // ... and every sequence may fit one tile
 
 hipError_t launch_plan_fwd(const Problem& p, const Plan& plan, int sched, hipStream_t s);
 hipError_t launch_fwd(const Problem& p, const Plan& plan, int sched, void* o, float* lse,
@@ -64,10 +77,10 @@ hipError_t launch_plan_bwd(const Problem& p, const Plan& plan, int sched, hipStr
 // holds a whole self-mode sequence (meta[3]).
 hipError_t launch_bwd(const Problem& p, const Plan& plan, int sched, const float* rowstat,
                       const float* lse, const void* d_o, float* dq_acc, void* dq, void* dk, void* dv,
-                      hipStream_t s);
+                      const Rope& rope, hipStream_t s);
 // Does nothing when meta[3] is set (the tiles wrote dQ).
 hipError_t launch_dq_finalize(const Problem& p, const float* dq_acc, void* dq, const int* meta,
-                              hipStream_t s);
+                              const Rope& rope, hipStream_t s);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

@@ -197,14 +197,15 @@ struct PlanBwdArgs {
   int batch;
   int heads;
   int bn;          // keys per backward tile
-  int self_mode;   // queries are the packed sequences themselves
+  int allow_direct;   // single-tile calls may store dQ directly (single_tile_allowed)
   int4* items;
   int* meta;
 };
 
 // Valid (sequence, K/V block) pairs in natural order; tile t = (items[t / H], t % H).
 // meta[3] = 1 when, in self mode, every sequence fits one tile: each tile then sees
-// all keys of its queries, so its dQ is final and is written directly.
+// all keys of its queries, so its dQ is final and is written directly (with the
+// rotary conjugate only where the tiles can rotate dQ, see single_tile_allowed).
 // Each item also carries the sequence's first row and length (int32: the library
 // rejects T >= 2^30), so a tile's geometry is one 16-byte load.
 __global__ __launch_bounds__(kPlanThreads) void plan_bwd_kernel(PlanBwdArgs a) {
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_bwd_kernel(PlanBwdArgs a) {
     a.meta[0] = total;
     a.meta[1] = 0;
     a.meta[2] = total * a.heads;
-    a.meta[3] = a.self_mode && all_single;   // read after the scan's barriers
+    a.meta[3] = a.allow_direct && all_single;   // read after the scan's barriers
   }
 }
 
@@ -264,7 +265,7 @@ hipError_t launch_plan_bwd(const Problem& p, const Plan& plan, int /*sched*/, hi
   a.batch = p.batch;
   a.heads = p.heads;
   a.bn = 32 * bwd_waves(p);
-  a.self_mode = !p.broadcast;
+  a.allow_direct = single_tile_allowed(p) ? 1 : 0;
   a.items = plan.items;
   a.meta = plan.meta;
   hipLaunchKernelGGL(plan_bwd_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
