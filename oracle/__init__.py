@@ -12,3 +12,4 @@ from .attention import (  # noqa: F401
     row_count,
 )
 from .rope import rope_rotate, rope_conjugate, backward_rope  # noqa: F401
+from . import sparse  # noqa: F401  (block-sparse top-k forward)

@@ -448,3 +448,86 @@ def test_rope_inputs_recipe():
     ang = 3 * 10000.0 ** (-2 * 2 / 8)
     assert r["cos"][3, 2].item() == np.float32(math.cos(ang))
     assert r["sin"][3, 2].item() == np.float32(math.sin(ang))
+
+
+# ---- block-sparse top-k forward (oracle/sparse.py) ---------------------------------
+
+def _block_mask_reference(q, k, v, off, selection, broadcast_q, scale):
+    """Padded dense torch SDPA (fp64, CPU) with a key mask that keeps, for every query
+    block, the keys of its selected blocks."""
+    from oracle.sparse import KV_BLOCK, Q_BLOCK
+    b, h, d = len(off) - 1, k.shape[1], k.shape[2]
+    lens = np.diff(off)
+    lmax = max(int(lens.max()), 1)
+    nq = q.shape[0] if broadcast_q else lmax
+    qp = torch.zeros(b, h, nq, d, dtype=torch.float64)
+    kp = torch.zeros(b, h, lmax, d, dtype=torch.float64)
+    vp = torch.zeros(b, h, lmax, d, dtype=torch.float64)
+    mask = torch.zeros(b, h, nq, lmax, dtype=torch.bool)
+    for i in range(b):
+        a, e = int(off[i]), int(off[i + 1])
+        qp[i, :, :, :] = torch.from_numpy(q.transpose(1, 0, 2) if broadcast_q else
+                                          np.pad(q[a:e], ((0, nq - (e - a)), (0, 0), (0, 0))).transpose(1, 0, 2))
+        kp[i, :, :e - a] = torch.from_numpy(k[a:e].transpose(1, 0, 2))
+        vp[i, :, :e - a] = torch.from_numpy(v[a:e].transpose(1, 0, 2))
+        rows = nq if broadcast_q else e - a
+        for hh in range(h):
+            for m, blocks in enumerate(selection[hh][i]):
+                r0, r1 = m * Q_BLOCK, min((m + 1) * Q_BLOCK, rows)
+                for j in blocks:
+                    mask[i, hh, r0:r1, j * KV_BLOCK:min((j + 1) * KV_BLOCK, e - a)] = True
+    o = F.scaled_dot_product_attention(qp, kp, vp, attn_mask=mask, scale=scale)
+    return o, mask
+
+
+@pytest.mark.parametrize("broadcast_q", [True, False])
+def test_sparse_forward_matches_block_masked_sdpa(broadcast_q):
+    """A fixed selection equals dense attention with the matching block mask."""
+    rng = np.random.default_rng(41)
+    lengths, h, d, lq, scale = [70, 200, 129], 2, 8, 150, 0.3
+    q, k, v, g, off = _rand_case(rng, lengths, h, d, broadcast_q, lq)
+    sel = oracle.sparse.select_all(q, k, off, 2, broadcast_q=broadcast_q, scale=scale)
+    o, lse = oracle.sparse.sparse_forward(q, k, v, off, sel, broadcast_q=broadcast_q, scale=scale)
+    ref, mask = _block_mask_reference(q, k, v, off, sel, broadcast_q, scale)
+    for i in range(len(lengths)):
+        a, e = int(off[i]), int(off[i + 1])
+        r0, r1 = (i * lq, (i + 1) * lq) if broadcast_q else (a, e)
+        got = o[r0:r1].transpose(1, 0, 2)
+        np.testing.assert_allclose(got, ref[i, :, :r1 - r0].numpy(), atol=1e-12)
+
+
+def test_sparse_with_every_block_is_dense():
+    rng = np.random.default_rng(42)
+    lengths, h, d, scale = [1, 64, 65, 300], 2, 8, 0.5
+    for bq, lq in ((True, 130), (False, 0)):
+        q, k, v, g, off = _rand_case(rng, lengths, h, d, bq, lq)
+        sel = oracle.sparse.select_all(q, k, off, 99, broadcast_q=bq, scale=scale)
+        o, lse = oracle.sparse.sparse_forward(q, k, v, off, sel, broadcast_q=bq, scale=scale)
+        o_ref, lse_ref = oracle.forward(q, k, v, off, broadcast_q=bq, scale=scale)
+        np.testing.assert_allclose(o, o_ref, atol=1e-12)
+        np.testing.assert_allclose(lse, lse_ref, atol=1e-12)
+
+
+def test_block_scores_by_explicit_loops():
+    rng = np.random.default_rng(43)
+    qb, kb, scale = rng.standard_normal((200, 4)), rng.standard_normal((130, 4)), 0.7
+    got = oracle.sparse.block_scores(qb, kb, scale)
+    assert got.shape == (2, 3)
+    for m, (q0, q1) in enumerate(((0, 128), (128, 200))):
+        for j, (k0, k1) in enumerate(((0, 64), (64, 128), (128, 130))):
+            qm = [sum(qb[r, c] for r in range(q0, q1)) / (q1 - q0) for c in range(4)]
+            km = [sum(kb[r, c] for r in range(k0, k1)) / (k1 - k0) for c in range(4)]
+            assert abs(got[m, j] - scale * sum(a * b for a, b in zip(qm, km))) <= 1e-12
+
+
+def test_top_k_selection_by_brute_force():
+    scores = np.array([[0.5, 2.0, -1.0, 2.0, 0.1],
+                       [3.0, 3.0, 3.0, 0.0, -2.0],
+                       [1.0, 0.0, 0.0, 0.0, 0.0]])
+    assert oracle.sparse.select_top_k(scores, 2) == [[1, 3], [0, 1], [0, 1]]   # ties to the lower index
+    assert oracle.sparse.select_top_k(scores, 9) == [[0, 1, 2, 3, 4]] * 3
+    rng = np.random.default_rng(44)
+    s = rng.standard_normal((6, 11))
+    for row, sel in zip(s, oracle.sparse.select_top_k(s, 4)):
+        assert len(sel) == 4 and sel == sorted(sel)
+        assert min(row[sel]) >= max(np.delete(row, sel))
