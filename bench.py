@@ -31,7 +31,7 @@ import torch  # noqa: E402
 import workloads  # noqa: E402
 
 METRIC = "useful TFLOP/s fwd & bwd, jagged broadcast-Q attn bf16; % of MFMA peak"
-KERNEL_SOURCES = ["fwd.hip", "bwd.hip", "plan.hip", "jfa_device.h", "jfa_internal.h"]
+KERNEL_SOURCES = ["fwd.hip", "bwd.hip", "plan.hip", "sparse.hip", "jfa_device.h", "jfa_internal.h"]
 PROFILES = os.path.join(ROOT, "profiles")
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
@@ -140,6 +140,48 @@ def cpu_baseline(case, w, budget_s: float):
     }
 
 
+def sparse_comparison(args, jfa, w, case, o, lse, ws_f):
+    """Dense forward vs the block-sparse forward (scoring, selection and attention)
+    for several top-k values; also the fraction of 64-key blocks the selection keeps."""
+    if w.causal:
+        print("the block-sparse forward is defined for non-causal workloads", file=sys.stderr)
+        sys.exit(2)
+    q, k, v, off = case["q"], case["k"], case["v"], case["offsets"]
+    bq, scale = w.broadcast_q, case["scale"]
+    lengths = case["lengths"]
+    nkv = (lengths + 63) // 64
+    qblocks = ((w.q_len + 255) // 256) * np.ones_like(lengths) if bq else (lengths + 127) // 128
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(args.steps):
+            fn()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        return round(start.elapsed_time(stop) / args.steps, 4)
+
+    res = {"dense": timed(lambda: jfa.fwd(q, k, v, off, broadcast_q=bq, scale=scale, out=o, lse=lse,
+                                          workspace=ws_f))}
+    kept = {}
+    for kk in [int(x) for x in args.sparse.split(",")]:
+        sizes = (len(lengths), w.heads, w.head_dim, w.q_len if bq else 0, int(lengths.sum()), bq, kk)
+        ws = torch.empty(jfa._binding.library().jfa_fwd_sparse_workspace_size(*sizes), dtype=torch.uint8,
+                         device=q.device)
+        res[f"sparse_k{kk}"] = timed(lambda: jfa.fwd_sparse(q, k, v, off, broadcast_q=bq, topk=kk,
+                                                            scale=scale, out=o, lse=lse, workspace=ws))
+        kept[f"k{kk}"] = round(float((np.minimum(nkv, kk) * qblocks).sum() / (nkv * qblocks).sum()), 4)
+        log(f"k={kk}: {res[f'sparse_k{kk}']:.4f} ms, blocks kept {kept[f'k{kk}']:.3f}")
+    print(json.dumps({"mode": "sparse", "workload": w.name, "steps": args.steps, "ms": res,
+                      "blocks_kept": kept,
+                      "speedup_over_dense": {k_: round(res["dense"] / v_, 4) for k_, v_ in res.items()
+                                             if k_ != "dense"}}), flush=True)
+
+
 def rope_comparison(args, jfa, w, case, o, lse, dq, dk, dv, ws_f, ws_b):
     """Fused rotary backward vs plain backward vs plain backward + separate rotary
     backward, as in the Block Attention page's rotary-fusion table.  The separate
@@ -199,6 +241,9 @@ def main():
                     help="instead of the step: time the backward with the fused rotary conjugate "
                          "(jfa_bwd_rope) against the plain backward, and against the plain backward "
                          "followed by a separate rotary backward (torch elementwise ops)")
+    ap.add_argument("--sparse", type=str, default="", metavar="K[,K...]",
+                    help="instead of the step: time the block-sparse forward (jfa_fwd_sparse) with "
+                         "these top-k values against the dense forward (non-causal workloads)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (3 times); used to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -246,6 +291,9 @@ def main():
 
     if args.rope:
         rope_comparison(args, jfa, w, case, o, lse, dq, dk, dv, ws_f, ws_b)
+        return
+    if args.sparse:
+        sparse_comparison(args, jfa, w, case, o, lse, ws_f)
         return
 
     log(f"workload {w.name}: B={len(lengths)} H={w.heads} D={w.head_dim} Lq={w.q_len} "

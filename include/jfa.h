@@ -153,10 +153,43 @@ jfa_status_t jfa_bwd_rope(const void* q, const void* k, const void* v,
                           void* dq, void* dk, void* dv,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Block-sparse top-k forward (the JFA news page and the reading note name a
+ * block-sparse fork of the kernel: a scoring step picks the top k key/value blocks
+ * for each query block, and attention runs only over those blocks).  Non-causal
+ * modes only (causal gives JFA_ERR_UNSUPPORTED).
+ *   Key blocks: 64 consecutive keys of a sequence (the last may be partial).
+ *   Query blocks: 256 consecutive rows of the broadcast query sequence, or 128
+ *     consecutive rows of the sequence itself in self mode (the rows one workgroup
+ *     of the forward covers).
+ *   Score of (query block, key block), per head: softmax_scale * (mean query row) .
+ *     (mean key row), computed in fp32.
+ *   Selection: the topk highest scores (ties to the lower block index); a sequence
+ *     with topk or fewer key blocks keeps all of them.  topk must be in [1, 64].
+ *     Key blocks past the 4096th of a sequence (262144 keys) are not candidates.
+ *   o, lse: as jfa_fwd, with attention restricted to the keys of the selected blocks.
+ *   blocks: optional (may be null) int32 output [num_heads][Q][topk] listing each
+ *     query block's selection in ascending order, -1 padded, where
+ *     Q = jfa_fwd_sparse_query_blocks(batch, q_len, total_kv, broadcast_q) and the
+ *     query block of sequence b, block m is b * ceil(q_len / 256) + m (broadcast) or
+ *     sum over b' < b of ceil(n_b' / 128), plus m (self mode).
+ * Workspace: jfa_fwd_sparse_workspace_size(...) bytes (0 for invalid sizes or topk).
+ * Other rules as jfa_fwd. */
+size_t jfa_fwd_sparse_workspace_size(int64_t batch, int64_t num_heads, int64_t head_dim, int64_t q_len,
+                                     int64_t total_kv, int broadcast_q, int topk);
+int64_t jfa_fwd_sparse_query_blocks(int64_t batch, int64_t q_len, int64_t total_kv, int broadcast_q);
+jfa_status_t jfa_fwd_sparse(const void* q, const void* k, const void* v,
+                            const void* offsets, int offsets_is_int64,
+                            int64_t batch, int64_t num_heads, int64_t head_dim,
+                            int64_t q_len, int64_t total_kv, int broadcast_q,
+                            float softmax_scale, int topk,
+                            void* o, float* lse, int32_t* blocks,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Measurement support.  While enabled on a thread, every kernel this library
  * launches from that thread is bracketed by two HIP events recorded on the
  * launch stream (events are created on first use and reused).  Kernel names:
- * "plan_fwd", "fwd", "bwd_pre", "plan_bwd", "bwd", "dq_finalize". */
+ * "plan_fwd", "fwd", "bwd_pre", "plan_bwd", "bwd", "dq_finalize", and for the
+ * block-sparse forward "plan_sparse", "sparse_select", "fwd_sparse". */
 jfa_status_t jfa_profile_enable(int enable);
 
 /* Waits for the recorded launches of this thread, then writes per-kernel totals:

@@ -11,8 +11,9 @@ and attention then runs only over the keys of the selected blocks.
 Readings where the pages are silent (each also listed in the design notes):
 
 * Key/value blocks are 64 consecutive keys of a sequence (the last one may be
-  partial); query blocks are 128 consecutive query rows (of the broadcast query
-  sequence, or of the sequence itself in self-attention).
+  partial); query blocks are 256 consecutive rows of the broadcast query sequence,
+  or 128 consecutive rows of the sequence itself in self-attention (the query rows
+  one workgroup of the forward covers in each mode).
 * The score of (query block m, key block j) for a head is
   c * mean(Q rows of m) . mean(K rows of j): the dot product of the mean query row
   and the mean key row, times the softmax scale c.
@@ -39,27 +40,32 @@ import numpy as np
 from .attention import sequence_forward
 
 KV_BLOCK = 64
-Q_BLOCK = 128
+Q_BLOCK_BROADCAST = 256
+Q_BLOCK_SELF = 128
 
 
 def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def query_blocks(n_rows: int) -> int:
-    return (n_rows + Q_BLOCK - 1) // Q_BLOCK
+def q_block(broadcast_q: bool) -> int:
+    return Q_BLOCK_BROADCAST if broadcast_q else Q_BLOCK_SELF
+
+
+def query_blocks(n_rows: int, qblk: int) -> int:
+    return (n_rows + qblk - 1) // qblk
 
 
 def kv_blocks(n_keys: int) -> int:
     return (n_keys + KV_BLOCK - 1) // KV_BLOCK
 
 
-def block_scores(qb, kb, scale: float):
-    """Scores [query blocks, key blocks] for one sequence and head:
-    c * mean(query block rows) . mean(key block rows)."""
+def block_scores(qb, kb, scale: float, qblk: int):
+    """Scores [query blocks, key blocks] for one sequence and head, query blocks of
+    qblk rows: c * mean(query block rows) . mean(key block rows)."""
     qb, kb = _f64(qb), _f64(kb)
-    nq, nk = query_blocks(len(qb)), kv_blocks(len(kb))
-    qm = np.stack([qb[m * Q_BLOCK:(m + 1) * Q_BLOCK].mean(axis=0) for m in range(nq)]) if nq else \
+    nq, nk = query_blocks(len(qb), qblk), kv_blocks(len(kb))
+    qm = np.stack([qb[m * qblk:(m + 1) * qblk].mean(axis=0) for m in range(nq)]) if nq else \
         np.zeros((0, qb.shape[1]))
     km = np.stack([kb[j * KV_BLOCK:(j + 1) * KV_BLOCK].mean(axis=0) for j in range(nk)]) if nk else \
         np.zeros((0, kb.shape[1]))
@@ -76,14 +82,14 @@ def select_top_k(scores, topk: int):
     return out
 
 
-def sequence_sparse_forward(qb, kb, vb, selection, scale: float):
-    """Exact attention of each query block over the keys of its selected blocks.
-    selection[m] lists the key blocks of query block m.  Returns (o, lse)."""
+def sequence_sparse_forward(qb, kb, vb, selection, scale: float, qblk: int):
+    """Exact attention of each query block (qblk rows) over the keys of its selected
+    blocks.  selection[m] lists the key blocks of query block m.  Returns (o, lse)."""
     qb, kb, vb = _f64(qb), _f64(kb), _f64(vb)
     o = np.zeros((len(qb), vb.shape[1]))
     lse = np.full(len(qb), -np.inf)
-    for m in range(query_blocks(len(qb))):
-        rows = slice(m * Q_BLOCK, min((m + 1) * Q_BLOCK, len(qb)))
+    for m in range(query_blocks(len(qb), qblk)):
+        rows = slice(m * qblk, min((m + 1) * qblk, len(qb)))
         keys = np.concatenate([np.arange(j * KV_BLOCK, min((j + 1) * KV_BLOCK, len(kb)))
                                for j in selection[m]]) if len(selection[m]) else np.zeros(0, dtype=np.int64)
         o[rows], lse[rows] = sequence_forward(qb[rows], kb[keys], vb[keys], scale)
@@ -106,7 +112,8 @@ def sparse_forward(q, k, v, offsets, selection, *, broadcast_q: bool, scale: flo
         r0, r1 = (b * lq, (b + 1) * lq) if broadcast_q else (a, e)
         for h in range(h_count):
             qb = q[:, h, :] if broadcast_q else q[a:e, h, :]
-            o_b, l_b = sequence_sparse_forward(qb, k[a:e, h, :], v[a:e, h, :], selection[h][b], scale)
+            o_b, l_b = sequence_sparse_forward(qb, k[a:e, h, :], v[a:e, h, :], selection[h][b], scale,
+                                               q_block(broadcast_q))
             out[r0:r1, h, :] = o_b
             lse[h, r0:r1] = l_b
     return out, lse
@@ -122,6 +129,6 @@ def select_all(q, k, offsets, topk: int, *, broadcast_q: bool, scale: float):
         for b in range(len(offsets) - 1):
             a, e = int(offsets[b]), int(offsets[b + 1])
             qb = q[:, h, :] if broadcast_q else q[a:e, h, :]
-            per_b.append(select_top_k(block_scores(qb, k[a:e, h, :], scale), topk))
+            per_b.append(select_top_k(block_scores(qb, k[a:e, h, :], scale, q_block(broadcast_q)), topk))
         sel.append(per_b)
     return sel

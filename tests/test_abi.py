@@ -133,3 +133,26 @@ def test_rope_rejections(lib):
     assert b"jfa_bwd_rope" in lib.jfa_last_error()
     assert bwd_rope(lib, ws_bytes=16) == WS_SMALL
     assert bwd_rope(lib, batch=0, ws=None) == OK                            # empty: a no-op
+
+
+def fwd_sparse(lib, *, batch=4, heads=2, head_dim=128, q_len=64, total_kv=100, bq=1, scale=0.1, topk=4,
+               ws=FAKE, ws_bytes=1 << 30, blocks=None):
+    return lib.jfa_fwd_sparse(FAKE, FAKE, FAKE, FAKE, 0, batch, heads, head_dim, q_len, total_kv, bq, scale,
+                              topk, FAKE, FAKE, blocks, ws, ws_bytes, None)
+
+
+def test_sparse_rejections_and_sizes(lib):
+    assert fwd_sparse(lib, topk=0) == INVALID
+    assert fwd_sparse(lib, topk=65) == INVALID
+    assert b"topk" in lib.jfa_last_error()
+    assert fwd_sparse(lib, head_dim=96) == UNSUPPORTED
+    assert fwd_sparse(lib, bq=0, q_len=5) == INVALID
+    assert fwd_sparse(lib, blocks=ctypes.c_void_p((1 << 20) + 2)) == INVALID   # 4-byte aligned output
+    assert fwd_sparse(lib, ws_bytes=16) == WS_SMALL
+    assert fwd_sparse(lib, batch=0, ws=None) == OK
+    ws = lib.jfa_fwd_sparse_workspace_size
+    assert ws(4, 2, 128, 64, 100, 1, 4) > lib.jfa_fwd_workspace_size(4, 2, 128, 64, 100, 1, 0)
+    assert ws(4, 2, 128, 64, 100, 1, 0) == 0 and ws(4, 2, 128, 64, 100, 1, 65) == 0
+    nqb = lib.jfa_fwd_sparse_query_blocks
+    assert nqb(4, 600, 1000, 1) == 4 * 3              # broadcast: B * ceil(Lq / 256)
+    assert nqb(3, 0, 1000, 0) >= 1000 // 128 + 3       # self: an upper bound of sum ceil(n_b / 128)

@@ -455,7 +455,8 @@ def test_rope_inputs_recipe():
 def _block_mask_reference(q, k, v, off, selection, broadcast_q, scale):
     """Padded dense torch SDPA (fp64, CPU) with a key mask that keeps, for every query
     block, the keys of its selected blocks."""
-    from oracle.sparse import KV_BLOCK, Q_BLOCK
+    from oracle.sparse import KV_BLOCK, q_block
+    Q_BLOCK = q_block(broadcast_q)
     b, h, d = len(off) - 1, k.shape[1], k.shape[2]
     lens = np.diff(off)
     lmax = max(int(lens.max()), 1)
@@ -484,7 +485,7 @@ def _block_mask_reference(q, k, v, off, selection, broadcast_q, scale):
 def test_sparse_forward_matches_block_masked_sdpa(broadcast_q):
     """A fixed selection equals dense attention with the matching block mask."""
     rng = np.random.default_rng(41)
-    lengths, h, d, lq, scale = [70, 200, 129], 2, 8, 150, 0.3
+    lengths, h, d, lq, scale = [70, 200, 129], 2, 8, 300, 0.3
     q, k, v, g, off = _rand_case(rng, lengths, h, d, broadcast_q, lq)
     sel = oracle.sparse.select_all(q, k, off, 2, broadcast_q=broadcast_q, scale=scale)
     o, lse = oracle.sparse.sparse_forward(q, k, v, off, sel, broadcast_q=broadcast_q, scale=scale)
@@ -511,7 +512,7 @@ def test_sparse_with_every_block_is_dense():
 def test_block_scores_by_explicit_loops():
     rng = np.random.default_rng(43)
     qb, kb, scale = rng.standard_normal((200, 4)), rng.standard_normal((130, 4)), 0.7
-    got = oracle.sparse.block_scores(qb, kb, scale)
+    got = oracle.sparse.block_scores(qb, kb, scale, 128)
     assert got.shape == (2, 3)
     for m, (q0, q1) in enumerate(((0, 128), (128, 200))):
         for j, (k0, k1) in enumerate(((0, 64), (64, 128), (128, 130))):

@@ -10,6 +10,7 @@ from ._binding import (  # noqa: F401
     SCHED_IDENTITY,
     SCHED_DYNAMIC,
     fwd,
+    fwd_sparse,
     bwd,
     fwd_workspace_size,
     bwd_workspace_size,

@@ -68,6 +68,13 @@ def library() -> ctypes.CDLL:
             lib.jfa_bwd_rope.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, i64, i32, i32, f32,
                                          vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
             lib.jfa_bwd_rope.restype = i32
+            lib.jfa_fwd_sparse_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32]
+            lib.jfa_fwd_sparse_workspace_size.restype = sz
+            lib.jfa_fwd_sparse_query_blocks.argtypes = [i64, i64, i64, i32]
+            lib.jfa_fwd_sparse_query_blocks.restype = i64
+            lib.jfa_fwd_sparse.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, i64, i32, f32, i32,
+                                           vp, vp, vp, vp, sz, vp]
+            lib.jfa_fwd_sparse.restype = i32
             lib.jfa_last_error.argtypes = []
             lib.jfa_last_error.restype = ctypes.c_char_p
             lib.jfa_version.argtypes = []
@@ -187,6 +194,35 @@ def fwd(q, k, v, offsets, *, broadcast_q: bool, causal: bool = False, scale=None
                            _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st)
     return out, lse
+
+
+def fwd_sparse(q, k, v, offsets, *, broadcast_q: bool, topk: int, scale=None, out=None, lse=None,
+               blocks=False, workspace=None):
+    """O, LSE (, blocks) = jfa_fwd_sparse(...): attention of every 128-row query block
+    over its topk best-scoring 64-key blocks.  With blocks=True also returns the
+    selection, int32 [H, query blocks, topk] (ascending, -1 padded)."""
+    _validate(q, k, v, offsets)
+    batch, heads, head_dim, q_len, total_kv, rows = _sizes(q, k, offsets, broadcast_q)
+    scale = 1.0 / math.sqrt(head_dim) if scale is None else float(scale)
+    dev = q.device
+    if out is None:
+        out = torch.empty((rows, heads, head_dim), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((heads, rows), dtype=torch.float32, device=dev)
+    sel = None
+    if blocks:
+        nqb = int(library().jfa_fwd_sparse_query_blocks(batch, q_len, total_kv, int(broadcast_q)))
+        sel = torch.empty((heads, nqb, int(topk)), dtype=torch.int32, device=dev)
+    need = int(library().jfa_fwd_sparse_workspace_size(batch, heads, head_dim, q_len, total_kv,
+                                                       int(broadcast_q), int(topk)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = library().jfa_fwd_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(offsets),
+                                  int(offsets.dtype == torch.int64), batch, heads, head_dim, q_len,
+                                  total_kv, int(broadcast_q), scale, int(topk), _ptr(out), _ptr(lse),
+                                  _ptr(sel), _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st)
+    return (out, lse, sel) if blocks else (out, lse)
 
 
 def bwd(q, k, v, offsets, o, lse, d_o, *, broadcast_q: bool, causal: bool = False, scale=None,

@@ -92,6 +92,29 @@ size_t fwd_ws_bytes(const jfa::Problem& p) {
   return kAlign + align_up(64) + align_up((size_t)jfa::fwd_max_items(p) * sizeof(int4));
 }
 
+// Block-sparse forward: capacities of the pooled key / query blocks and of the
+// natural-order selection output.
+int64_t sparse_kv_cap(const jfa::Problem& p) { return p.total_kv / jfa::kFwdBN + p.batch + 1; }
+int64_t sparse_bcast_qblocks(const jfa::Problem& p) {   // query blocks of the broadcast query
+  return (p.q_len + jfa::kSparseQBBroadcast - 1) / jfa::kSparseQBBroadcast;
+}
+int64_t sparse_q_cap(const jfa::Problem& p) {
+  return p.broadcast ? sparse_bcast_qblocks(p) : p.total_kv / jfa::kSparseQBSelf + p.batch + 1;
+}
+int64_t sparse_out_qblocks(const jfa::Problem& p) {
+  return p.broadcast ? (int64_t)p.batch * sparse_bcast_qblocks(p) : sparse_q_cap(p);
+}
+int64_t sparse_tiles(const jfa::Problem& p) {
+  return jfa::fwd_max_items(p) * (p.broadcast ? sparse_bcast_qblocks(p) * p.heads : p.heads);
+}
+
+size_t fwd_sparse_ws_bytes(const jfa::Problem& p) {
+  return fwd_ws_bytes(p) + 2 * align_up((size_t)(p.batch + 1) * sizeof(int)) +
+         align_up((size_t)p.heads * sparse_kv_cap(p) * p.head_dim * sizeof(float)) +
+         align_up((size_t)p.heads * sparse_q_cap(p) * p.head_dim * sizeof(float)) +
+         align_up((size_t)sparse_tiles(p) * p.topk * sizeof(int));
+}
+
 size_t bwd_ws_bytes(const jfa::Problem& p) {
   const int64_t q_rows = p.broadcast ? (int64_t)p.q_len * jfa::kDqStripes : p.total_kv;
   return kAlign + align_up(64) + align_up((size_t)jfa::bwd_max_items(p) * sizeof(int4)) +
@@ -345,6 +368,75 @@ jfa_status_t jfa_bwd_rope(const void* q, const void* k, const void* v, const voi
   return bwd_impl("jfa_bwd_rope", q, k, v, offsets, offsets_is_int64, batch, num_heads, head_dim, q_len,
                   total_kv, broadcast_q, causal, softmax_scale, o, lse, d_o, dq, dk, dv, rope, workspace,
                   workspace_bytes, stream);
+}
+
+size_t jfa_fwd_sparse_workspace_size(int64_t batch, int64_t num_heads, int64_t head_dim, int64_t q_len,
+                                     int64_t total_kv, int broadcast_q, int topk) {
+  if (!check_sizes(batch, num_heads, head_dim, q_len, total_kv, broadcast_q, 0).ok) return 0;
+  if (topk < 1 || topk > jfa::kSparseMaxTopk) return 0;
+  jfa::Problem p = make_problem(nullptr, nullptr, nullptr, nullptr, 0, batch, num_heads, head_dim, q_len,
+                                total_kv, broadcast_q, 0, 1.f);
+  p.topk = topk;
+  return fwd_sparse_ws_bytes(p);
+}
+
+int64_t jfa_fwd_sparse_query_blocks(int64_t batch, int64_t q_len, int64_t total_kv, int broadcast_q) {
+  jfa::Problem p = make_problem(nullptr, nullptr, nullptr, nullptr, 0, batch, 1, 128, q_len, total_kv,
+                                broadcast_q, 0, 1.f);
+  return sparse_out_qblocks(p);
+}
+
+jfa_status_t jfa_fwd_sparse(const void* q, const void* k, const void* v, const void* offsets,
+                            int offsets_is_int64, int64_t batch, int64_t num_heads, int64_t head_dim,
+                            int64_t q_len, int64_t total_kv, int broadcast_q, float softmax_scale, int topk,
+                            void* o, float* lse, int32_t* blocks, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  g_error[0] = '\0';
+  const Sizes sz = check_sizes(batch, num_heads, head_dim, q_len, total_kv, broadcast_q, 0);
+  if (!sz.ok) return fail(sz.st, "jfa_fwd_sparse: %s", sz.why);
+  if (topk < 1 || topk > jfa::kSparseMaxTopk)
+    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_fwd_sparse: topk must be in [1, %d]", jfa::kSparseMaxTopk);
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
+    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_fwd_sparse: softmax_scale must be finite and > 0");
+  jfa::Problem p = make_problem(q, k, v, offsets, offsets_is_int64, batch, num_heads, head_dim, q_len,
+                                total_kv, broadcast_q, 0, softmax_scale);
+  p.topk = topk;
+  if (p.batch == 0 || p.rows == 0) return JFA_OK;
+  if (!q || !offsets || !o || !lse || !workspace || (p.total_kv > 0 && (!k || !v)))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_fwd_sparse: null pointer argument");
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(workspace) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3) || (reinterpret_cast<uintptr_t>(blocks) & 3) ||
+      (reinterpret_cast<uintptr_t>(offsets) & (offsets_is_int64 ? 7 : 3)))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_fwd_sparse: tensors must be 16-byte aligned");
+  const size_t need = fwd_sparse_ws_bytes(p);
+  if (workspace_bytes < need)
+    return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "jfa_fwd_sparse: workspace of %zu bytes, need %zu",
+                workspace_bytes, need);
+  char* cur = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(workspace)));
+  jfa::Plan plan;
+  plan.meta = reinterpret_cast<int*>(carve(cur, 64));
+  plan.max_items = jfa::fwd_max_items(p);
+  plan.items = reinterpret_cast<int4*>(carve(cur, plan.max_items * sizeof(int4)));
+  jfa::Sparse sp;
+  sp.kv_first = reinterpret_cast<int*>(carve(cur, (size_t)(p.batch + 1) * sizeof(int)));
+  sp.q_first = reinterpret_cast<int*>(carve(cur, (size_t)(p.batch + 1) * sizeof(int)));
+  sp.kv_blocks_cap = sparse_kv_cap(p);
+  sp.q_blocks_cap = sparse_q_cap(p);
+  sp.pooled_k = reinterpret_cast<float*>(carve(cur, (size_t)p.heads * sp.kv_blocks_cap * p.head_dim * sizeof(float)));
+  sp.pooled_q = reinterpret_cast<float*>(carve(cur, (size_t)p.heads * sp.q_blocks_cap * p.head_dim * sizeof(float)));
+  sp.tile_blocks = reinterpret_cast<int*>(carve(cur, (size_t)sparse_tiles(p) * p.topk * sizeof(int)));
+  sp.out_blocks = blocks;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int sched = g_schedule.load();
+  hipError_t e = timed_launch("plan_sparse", s, [&] { return jfa::launch_plan_sparse(p, sp.kv_first, sp.q_first, s); });
+  if (e != hipSuccess) return hip_fail(e, "jfa_fwd_sparse: plan launch");
+  e = timed_launch("plan_fwd", s, [&] { return jfa::launch_plan_fwd(p, plan, sched, s); });
+  if (e != hipSuccess) return hip_fail(e, "jfa_fwd_sparse: plan launch");
+  e = timed_launch("sparse_select", s, [&] { return jfa::launch_sparse_select(p, plan, sp, s); });
+  if (e != hipSuccess) return hip_fail(e, "jfa_fwd_sparse: selection launch");
+  e = timed_launch("fwd_sparse", s, [&] { return jfa::launch_fwd_sparse(p, plan, sched, sp, o, lse, s); });
+  if (e != hipSuccess) return hip_fail(e, "jfa_fwd_sparse: kernel launch");
+  return JFA_OK;
 }
 
 jfa_status_t jfa_profile_enable(int enable) {

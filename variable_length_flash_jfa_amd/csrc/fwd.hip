@@ -48,9 +48,15 @@ struct FwdArgs {
   const int4* items;
   int* meta;
   int sched;
+  // block-sparse forward: [tiles][topk] selected key blocks (ascending) per tile
+  const int* tile_blocks;
+  int topk;
 };
 
-template <int D, int NW, bool BCAST, bool CAUSAL>
+// SPARSE: the block-sparse forward (no causal mask); a tile visits only the key
+// blocks its selection lists, read from a per-tile list in LDS (`lists`, two
+// buffers of 64 entries: the current tile's and the next one's).
+template <int D, int NW, bool BCAST, bool CAUSAL, bool SPARSE = false>
 struct FwdKernel {
   static constexpr int BN = kFwdBN;
   static constexpr int BM = 32 * NW;
@@ -81,6 +87,8 @@ struct FwdKernel {
   };
 
   // Per-tile state.
+  const int* lists = nullptr;   // SPARSE: LDS list buffers
+  int lb = 0;                   // SPARSE: the current tile's list buffer
   Geo g;               // the current tile
   int q_rows, m0, i0;
   int64_t out_row0;    // first output row of the sequence
@@ -124,7 +132,19 @@ struct FwdKernel {
   // K/V blocks the tile visits.
   __device__ __forceinline__ int num_blocks(const Geo& t) const {
     const int64_t kv_end = CAUSAL ? min((int64_t)t.n, (int64_t)(t.m + 1) * BM) : (int64_t)t.n;
-    return (int)((kv_end + BN - 1) / BN);
+    const int nb = (int)((kv_end + BN - 1) / BN);
+    if constexpr (SPARSE) return min(nb, min(a.topk, 64 * 64));
+    return nb;
+  }
+  // Key block visited at position t of the current tile, and the first block of the
+  // next tile.
+  __device__ __forceinline__ int blk_of(int t) const {
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane(lists[lb * 64 + t]);
+    return t;
+  }
+  __device__ __forceinline__ int first_next() const {
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane(lists[(lb ^ 1) * 64]);
+    return 0;
   }
 
   // This wave's Q fragment of tile t (rows past the query end read as zeros).
@@ -248,11 +268,12 @@ struct FwdKernel {
     for (int t = t_begin; t < t_end; ++t) {
       const int buf = (pb + t) & 1;
       if (t + 1 < nblk) {
-        load_block(g, t + 1, buf ^ 1);
+        load_block(g, blk_of(t + 1), buf ^ 1);
       } else if (has_next) {
-        load_block(nxt, 0, buf ^ 1);
+        load_block(nxt, first_next(), buf ^ 1);
       }
-      if (wave_needs(t)) compute_block<MASKED>(buf, t);
+      const int blk = blk_of(t);
+      if (wave_needs(blk)) compute_block<MASKED>(buf, blk);
       if (t + 1 < nblk) wait_lds_loads();
       __syncthreads();
     }
@@ -285,11 +306,15 @@ struct FwdKernel {
     int nfull = (int)(g.n / BN);
     if constexpr (CAUSAL) nfull = min(nfull, (m0 + 1) / BN);
     nfull = min(nfull, nblk);
+    if constexpr (SPARSE) {   // ascending list: only its last block can be the partial one
+      nfull = nblk;
+      if (nblk > 0 && (int64_t)(blk_of(nblk - 1) + 1) * BN > g.n) nfull = nblk - 1;
+    }
     run_blocks<false>(0, nfull, nblk, pb, nxt, has_next);
     run_blocks<true>(nfull, nblk, nblk, pb, nxt, has_next);
     if (nblk == 0) {   // an empty sequence (broadcast mode): no block barrier ran
       __syncthreads();
-      if (has_next) load_block(nxt, 0, pb);
+      if (has_next) load_block(nxt, first_next(), pb);
     }
     if (has_next) load_q(nxt);   // this tile is done with its Q fragment
     between();
@@ -310,16 +335,18 @@ struct FwdKernel {
 // index of tile r + 2 is claimed (or computed, for the static schedules) and, after
 // tile r's last block, its plan item is copied into LDS by a direct load, so that
 // tile r + 1's first K/V block and Q fragment can be issued during tile r.
-template <int D, int NW, bool BCAST, bool CAUSAL>
+template <int D, int NW, bool BCAST, bool CAUSAL, bool SPARSE = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_kernel(FwdArgs a) {
-  using K = FwdKernel<D, NW, BCAST, CAUSAL>;
+  using K = FwdKernel<D, NW, BCAST, CAUSAL, SPARSE>;
   using Geo = typename K::Geo;
   __shared__ __attribute__((aligned(16))) char smem[4 * K::TILE_BYTES];
   __shared__ __attribute__((aligned(16))) int next_item[64];   // one dword per lane of the copy
+  __shared__ __attribute__((aligned(16))) int lists[SPARSE ? 2 * 64 : 1];
   __shared__ int next_idx;
   __shared__ int first_idx[2];
   K kern(a, smem);
+  kern.lists = lists;
   const int num_wg = gridDim.x;
   const int lwg = xcd_logical_wg(blockIdx.x, num_wg);
   const int ntiles = a.meta[2];
@@ -332,6 +359,13 @@ void fwd_kernel(FwdArgs a) {
   auto fetch_item = [&](int idx) {   // plan item of tile idx -> next_item[0 .. 3]
     lds_load4(make_rsrc_sgpr(a.items + idx / per_item, 16u), (uint32_t)kern.lane * 4u,
               reinterpret_cast<char*>(next_item));
+  };
+  // SPARSE: key-block list of tile idx -> list buffer `buf` (entries past topk read
+  // as zeros and are never used)
+  auto fetch_list = [&](int idx, int buf) {
+    if constexpr (SPARSE)
+      lds_load4(make_rsrc_sgpr(a.tile_blocks + (int64_t)idx * a.topk, (uint32_t)a.topk * 4u),
+                (uint32_t)kern.lane * 4u, reinterpret_cast<char*>(lists + buf * 64));
   };
 
   int idx0, idx1;
@@ -353,8 +387,16 @@ void fwd_kernel(FwdArgs a) {
     if (idx1 < ntiles) fetch_item(idx1);
     if (threadIdx.x == 0) next_idx = idx1;
   }
+  if constexpr (SPARSE) {   // the first two tiles' lists, before the first block's address
+    if (kern.wave == 0) {
+      fetch_list(idx0, 0);
+      if (idx1 < ntiles) fetch_list(idx1, 1);
+    }
+    wait_lds_loads();
+    __syncthreads();
+  }
   kern.load_q(kern.g);
-  if (kern.num_blocks(kern.g) > 0) kern.load_block(kern.g, 0, 0);
+  if (kern.num_blocks(kern.g) > 0) kern.load_block(kern.g, kern.blk_of(0), 0);
 
   int pb = 0;
   for (int r = 0;; ++r) {
@@ -379,20 +421,24 @@ void fwd_kernel(FwdArgs a) {
     pb = kern.tile(pb, nxt, has_next, [&]() {
       if (has_next && kern.wave == 0) {
         const int i2 = __builtin_amdgcn_readfirstlane(pend);
-        if (i2 < ntiles) fetch_item(i2);
+        if (i2 < ntiles) {
+          fetch_item(i2);
+          fetch_list(i2, kern.lb);   // tile r + 2 takes this tile's (finished) list buffer
+        }
         if (threadIdx.x == 0) next_idx = i2;
       }
     });
     if (!has_next) break;
     kern.g = nxt;
+    kern.lb ^= 1;
   }
 }
 
-template <int D, int NW, bool BCAST, bool CAUSAL>
+template <int D, int NW, bool BCAST, bool CAUSAL, bool SPARSE = false>
 hipError_t launch_inst(const FwdArgs& a, hipStream_t s, int64_t max_tiles) {
-  const void* fn = reinterpret_cast<const void*>(&fwd_kernel<D, NW, BCAST, CAUSAL>);
+  const void* fn = reinterpret_cast<const void*>(&fwd_kernel<D, NW, BCAST, CAUSAL, SPARSE>);
   const int grid = persistent_grid(fn, 64 * NW, max_tiles);
-  hipLaunchKernelGGL((fwd_kernel<D, NW, BCAST, CAUSAL>), dim3(grid), dim3(64 * NW), 0, s, a);
+  hipLaunchKernelGGL((fwd_kernel<D, NW, BCAST, CAUSAL, SPARSE>), dim3(grid), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
@@ -413,6 +459,7 @@ hipError_t launch_d(const Problem& p, const FwdArgs& a, hipStream_t s) {
 }  // namespace
 
 int fwd_waves(const Problem& p) {
+  if (p.topk > 0) return sparse_qb(p) / 32;   // block-sparse: the tile is one query block
   if (!p.broadcast) return 4;
   if (p.q_len > 128) return 8;
   if (p.q_len > 64) return 4;
@@ -442,7 +489,40 @@ hipError_t launch_fwd(const Problem& p, const Plan& plan, int sched, void* o, fl
   a.items = plan.items;
   a.meta = plan.meta;
   a.sched = sched;
+  a.tile_blocks = nullptr;
+  a.topk = 0;
   return p.head_dim == 128 ? launch_d<128>(p, a, s) : launch_d<64>(p, a, s);
+}
+
+hipError_t launch_fwd_sparse(const Problem& p, const Plan& plan, int sched, const Sparse& sp, void* o,
+                             float* lse, hipStream_t s) {
+  FwdArgs a;
+  a.q = static_cast<const bf16*>(p.q);
+  a.k = static_cast<const bf16*>(p.k);
+  a.v = static_cast<const bf16*>(p.v);
+  a.offsets = p.offsets;
+  a.off64 = p.off64;
+  a.heads = p.heads;
+  a.q_len = p.q_len;
+  a.rows = p.rows;
+  a.scale_log2 = p.scale * kLog2e;
+  a.o = static_cast<bf16*>(o);
+  a.lse = lse;
+  a.items = plan.items;
+  a.meta = plan.meta;
+  a.sched = sched;
+  a.tile_blocks = sp.tile_blocks;
+  a.topk = p.topk;
+  constexpr int NWB = kSparseQBBroadcast / 32, NWS = kSparseQBSelf / 32;
+  const int64_t per_item =
+      p.broadcast ? ((p.q_len + kSparseQBBroadcast - 1) / kSparseQBBroadcast) * p.heads : p.heads;
+  const int64_t max_tiles = fwd_max_items(p) * per_item;
+  if (p.head_dim == 128) {
+    return p.broadcast ? launch_inst<128, NWB, true, false, true>(a, s, max_tiles)
+                       : launch_inst<128, NWS, false, false, true>(a, s, max_tiles);
+  }
+  return p.broadcast ? launch_inst<64, NWB, true, false, true>(a, s, max_tiles)
+                     : launch_inst<64, NWS, false, false, true>(a, s, max_tiles);
 }
 
 }  // namespace jfa

@@ -32,6 +32,27 @@ struct Problem {
   int causal;
   float scale;
   int rope = 0;       // the backward applies the rotary conjugate (no direct dQ store)
+  int topk = 0;       // block-sparse forward: key blocks kept per query block (0: dense)
+};
+
+// Block-sparse forward: key blocks of kFwdBN keys; query blocks of the rows one
+// forward workgroup covers: 256 rows of the broadcast query (eight waves), 128 rows
+// of a sequence in self mode (four waves).
+constexpr int kSparseQBBroadcast = 256;
+constexpr int kSparseQBSelf = 128;
+inline int sparse_qb(const Problem& p) { return p.broadcast ? kSparseQBBroadcast : kSparseQBSelf; }
+constexpr int kSparseMaxTopk = 64;
+
+// Workspace of the block-sparse forward (all device pointers).
+struct Sparse {
+  int* kv_first = nullptr;      // [B + 1] first global key block of each sequence
+  int* q_first = nullptr;       // [B + 1] first global query block (self mode)
+  float* pooled_k = nullptr;    // [H][key blocks][D] mean key rows
+  float* pooled_q = nullptr;    // [H][query blocks][D] mean query rows
+  int* tile_blocks = nullptr;   // [tiles][topk] selected key blocks, in forward tile order
+  int* out_blocks = nullptr;    // optional [H][query blocks][topk], natural order, -1 padded
+  int64_t kv_blocks_cap = 0;    // capacity of pooled_k's block dimension
+  int64_t q_blocks_cap = 0;     // capacity of pooled_q's block dimension
 };
 
 // Rotary-embedding conjugate of the backward: fp32 tables [max_pos][D/2] and int32
@@ -63,6 +84,11 @@ bool single_tile_allowed(const Problem& p);      // the single-tile backward pat
 bool maybe_single_tile(const Problem& p);        // ... and every sequence may fit one tile
 
 hipError_t launch_plan_fwd(const Problem& p, const Plan& plan, int sched, hipStream_t s);
+hipError_t launch_plan_sparse(const Problem& p, int* kv_first, int* q_first, hipStream_t s);
+// Pooling and top-k selection of the block-sparse forward (after the forward plan).
+hipError_t launch_sparse_select(const Problem& p, const Plan& plan, const Sparse& sp, hipStream_t s);
+hipError_t launch_fwd_sparse(const Problem& p, const Plan& plan, int sched, const Sparse& sp, void* o,
+                             float* lse, hipStream_t s);
 hipError_t launch_fwd(const Problem& p, const Plan& plan, int sched, void* o, float* lse,
                       hipStream_t s);
 

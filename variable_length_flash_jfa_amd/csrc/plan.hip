@@ -89,6 +89,7 @@ struct PlanFwdArgs {
   int causal;
   int heads;
   int sched;
+  int topk;        // block-sparse forward: a tile visits at most topk key blocks (0: dense)
   int4* items;
   int* meta;
 };
@@ -102,7 +103,8 @@ __device__ __forceinline__ int fwd_items_of(const PlanFwdArgs& a, int64_t n) {
 __device__ __forceinline__ int fwd_cost(const PlanFwdArgs& a, int64_t n, int m) {
   int64_t kv = n;
   if (a.causal) kv = min(n, (int64_t)(m + 1) * a.bm);
-  const int64_t c = (kv + kFwdBN - 1) / kFwdBN;
+  int64_t c = (kv + kFwdBN - 1) / kFwdBN;
+  if (a.topk > 0) c = min(c, (int64_t)a.topk);
   return (int)min(c, (int64_t)(kKeys - 1));
 }
 
@@ -239,7 +241,58 @@ __global__ __launch_bounds__(kPlanThreads) void plan_bwd_kernel(PlanBwdArgs a) {
   }
 }
 
+// Block-sparse forward: first global key block (64 keys) and first query block
+// (kSparseQBSelf rows; self mode) of every sequence, as exclusive prefix sums:
+// kv_first[b] = sum over b' < b of ceil(n_b' / 64), q_first likewise (entry B holds
+// the totals).
+struct PlanSparseArgs {
+  const void* offsets;
+  int off64;
+  int batch;
+  int* kv_first;
+  int* q_first;
+};
+
+__global__ __launch_bounds__(kPlanThreads) void plan_sparse_kernel(PlanSparseArgs a) {
+  __shared__ int wave_sums[kPlanThreads / 64 + 1];
+  const int tid = threadIdx.x;
+  const int per = (a.batch + kPlanThreads - 1) / kPlanThreads;
+  const int b_begin = min(a.batch, tid * per);
+  const int b_end = min(a.batch, b_begin + per);
+  int ckv = 0, cq = 0;
+  for (int b = b_begin; b < b_end; ++b) {
+    const int64_t n = load_offset(a.offsets, a.off64, b + 1) - load_offset(a.offsets, a.off64, b);
+    ckv += (int)((n + kFwdBN - 1) / kFwdBN);
+    cq += (int)((n + kSparseQBSelf - 1) / kSparseQBSelf);
+  }
+  int tkv = 0, tq = 0;
+  int pkv = block_exclusive_scan(ckv, wave_sums, &tkv);
+  int pq = block_exclusive_scan(cq, wave_sums, &tq);
+  for (int b = b_begin; b < b_end; ++b) {
+    a.kv_first[b] = pkv;
+    a.q_first[b] = pq;
+    const int64_t n = load_offset(a.offsets, a.off64, b + 1) - load_offset(a.offsets, a.off64, b);
+    pkv += (int)((n + kFwdBN - 1) / kFwdBN);
+    pq += (int)((n + kSparseQBSelf - 1) / kSparseQBSelf);
+  }
+  if (tid == 0) {
+    a.kv_first[a.batch] = tkv;
+    a.q_first[a.batch] = tq;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_plan_sparse(const Problem& p, int* kv_first, int* q_first, hipStream_t s) {
+  PlanSparseArgs a;
+  a.offsets = p.offsets;
+  a.off64 = p.off64;
+  a.batch = p.batch;
+  a.kv_first = kv_first;
+  a.q_first = q_first;
+  hipLaunchKernelGGL(plan_sparse_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_plan_fwd(const Problem& p, const Plan& plan, int sched, hipStream_t s) {
   PlanFwdArgs a;
@@ -252,6 +305,7 @@ hipError_t launch_plan_fwd(const Problem& p, const Plan& plan, int sched, hipStr
   a.causal = p.causal;
   a.heads = p.heads;
   a.sched = sched;
+  a.topk = p.topk;
   a.items = plan.items;
   a.meta = plan.meta;
   hipLaunchKernelGGL(plan_fwd_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
