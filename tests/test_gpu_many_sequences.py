@@ -1,0 +1,180 @@
+"""GPU coverage of batches larger than one planner segment (8192 sequences).
+
+The tile planners stage the offsets through LDS 8192 sequences at a time and carry
+running bases across segments; a mistake there drops, duplicates or misplaces
+whole sequences, which sampled checks can miss.  These tests therefore check EVERY
+sequence of batches of 9,000 to 17,000 short sequences against a plain PyTorch
+fp32 reference of the same attention run on the GPU (padded to the longest
+sequence, with key-padding and causal masks), at the oracle parity tolerances:
+max |O - O_ref| <= 1e-2, max |LSE - LSE_ref| <= 1e-3, gradients <= 2e-2 * max |ref|.
+The fp32 reference itself is the definition written out with library products
+(softmax(c Q K^T) V and its autograd gradients); it is independent of the HIP path.
+
+O is stored in bf16, so each element is allowed 1e-2 plus half a bf16 ulp of its
+magnitude (the one rounding to the output format): with ~10^8 outputs drawn from
+unit normals a few have |O| > 4, where that half-ulp alone (up to 1.6e-2) exceeds
+the 1e-2 bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = 1e-2
+TOL_LSE = 1e-3
+TOL_GRAD = 2e-2
+
+
+def _jfa():
+    import variable_length_flash_jfa_amd as jfa
+    return jfa
+
+
+def _lengths(seed, batch, lo, hi, zero_every=0, long_at=None, long_len=0):
+    rng = np.random.default_rng(seed)
+    n = rng.integers(lo, hi + 1, size=batch)
+    if zero_every:
+        n[::zero_every] = 0
+    if long_at is not None:
+        n[long_at] = long_len
+    return [int(x) for x in n]
+
+
+def _padded_reference(q, k, v, g, off, *, broadcast_q, causal, scale):
+    """fp32 attention over the padded batch; returns (O, LSE, dQ, dK, dV) packed."""
+    dev = k.device
+    off = off.to(torch.int64)
+    n = off[1:] - off[:-1]
+    batch, lmax = n.numel(), max(int(n.max().item()), 1)
+    j = torch.arange(lmax, device=dev)
+    valid = j[None, :] < n[:, None]                        # [B, Lmax]
+    idx = torch.where(valid, off[:-1, None] + j[None, :], torch.zeros_like(j)[None, :])
+    kf = k.float().requires_grad_(True)
+    vf = v.float().requires_grad_(True)
+    qf = q.float().requires_grad_(True)
+    kp = kf[idx].permute(0, 2, 1, 3).contiguous()          # [B, H, Lmax, D]
+    vp = vf[idx].permute(0, 2, 1, 3).contiguous()
+    if broadcast_q:
+        lq = q.shape[0]
+        qp = qf.permute(1, 0, 2)[None].expand(batch, -1, -1, -1).contiguous()   # [B, H, Lq, D]
+        gp = g.float().view(batch, lq, *g.shape[1:]).permute(0, 2, 1, 3).contiguous()
+        row_ok = torch.ones(batch, lq, dtype=torch.bool, device=dev)
+    else:
+        qp = qf[idx].permute(0, 2, 1, 3).contiguous()
+        gp = g.float()[idx].permute(0, 2, 1, 3).contiguous() * valid[:, None, :, None]
+        row_ok = valid
+    s = torch.matmul(qp, kp.transpose(-1, -2).contiguous()) * scale   # [B, H, R, Lmax]
+    keep = valid[:, None, None, :].expand_as(s)
+    if causal:
+        rows = torch.arange(s.shape[2], device=dev)
+        keep = keep & (j[None, None, None, :] <= rows[None, None, :, None])
+    s = s.masked_fill(~keep, float("-inf"))
+    m = s.amax(dim=-1, keepdim=True)
+    m = torch.where(torch.isfinite(m), m, torch.zeros_like(m)).detach()
+    e = torch.exp(s - m)
+    l = e.sum(dim=-1, keepdim=True)
+    p = e / l.clamp_min(1e-30)
+    o = torch.matmul(p, vp)
+    lse = torch.where(l > 0, m + torch.log(l.clamp_min(1e-30)), torch.full_like(l, float("-inf")))
+    dq, dk, dv = torch.autograd.grad((o * gp).sum(), (qf, kf, vf))
+    o = o.detach()
+    lse = lse.detach()[..., 0]                              # [B, H, R]
+    if broadcast_q:
+        o_packed = o.permute(0, 2, 1, 3).reshape(batch * q.shape[0], *q.shape[1:])
+        lse_packed = lse.permute(1, 0, 2).reshape(q.shape[1], -1)
+    else:
+        o_packed = o.permute(0, 2, 1, 3)[row_ok]
+        lse_packed = lse.permute(0, 2, 1)[row_ok].t()
+    return o_packed, lse_packed, dq, dk, dv
+
+
+def _check(got, ref, tol, what):
+    err = (got.float() - ref.float()).abs().max().item() if ref.numel() else 0.0
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.3e}"
+
+
+def _check_o(got, ref):
+    got, ref = got.float(), ref.float()
+    _, e = torch.frexp(torch.maximum(got.abs(), ref.abs()))
+    half_ulp = torch.ldexp(torch.ones_like(ref), e - 9)      # bf16: 8 significant bits
+    excess = ((got - ref).abs() - half_ulp).max().item() if ref.numel() else 0.0
+    assert excess <= TOL_O, f"O: max abs err beyond bf16 rounding {excess:.3e} > {TOL_O}"
+
+
+def _check_lse(got, ref):
+    inf_ref = torch.isneginf(ref)
+    assert torch.equal(torch.isneginf(got), inf_ref), "LSE: -inf pattern differs"
+    fin = ~inf_ref
+    if fin.any():
+        _check(got[fin], ref[fin], TOL_LSE, "LSE")
+
+
+def _case(lengths, *, heads, head_dim, broadcast_q, causal, q_len, seed, offsets_dtype=torch.int64):
+    case = workloads.make_case(lengths, heads=heads, head_dim=head_dim, broadcast_q=broadcast_q,
+                               causal=causal, q_len=q_len, seed=seed)
+    dev = "cuda"
+    q, k, v, g = (case[x].to(dev) for x in ("q", "k", "v", "g"))
+    off = case["offsets"].to(dev).to(offsets_dtype)
+    return case, q, k, v, g, off
+
+
+MANY = {
+    # name: (lengths, heads, head_dim, broadcast_q, causal, q_len)
+    "self_17k": (_lengths(1, 17000, 1, 130, zero_every=97), 2, 64, False, False, 0),
+    "self_causal_17k": (_lengths(2, 17000, 1, 200, zero_every=89), 2, 128, False, True, 0),
+    # every sequence within one 64-key backward tile: the single-tile backward
+    "self_causal_short_17k": (_lengths(3, 17000, 1, 64), 2, 64, False, True, 0),
+    # as above except one sequence in the last segment: the multi-tile backward
+    "self_causal_short_one_long": (_lengths(4, 17000, 1, 64, long_at=16990, long_len=150), 2, 64,
+                                   False, True, 0),
+    "bcast_9k": (_lengths(5, 9000, 0, 120), 2, 128, True, False, 48),
+}
+
+
+@pytest.mark.parametrize("sched", [0, 1, 2])
+@pytest.mark.parametrize("name", list(MANY))
+def test_many_sequences_every_row(name, sched):
+    if sched != 2 and name not in ("self_17k", "bcast_9k"):
+        pytest.skip("schedules other than the default are covered on two of the cases")
+    lengths, h, d, bq, causal, lq = MANY[name]
+    jfa = _jfa()
+    off_dtype = torch.int32 if sched == 1 else torch.int64
+    case, q, k, v, g, off = _case(lengths, heads=h, head_dim=d, broadcast_q=bq, causal=causal,
+                                  q_len=lq, seed=sched + 10, offsets_dtype=off_dtype)
+    old = jfa.get_schedule()
+    jfa.set_schedule(sched)
+    try:
+        o, lse = jfa.fwd(q, k, v, off, broadcast_q=bq, causal=causal, scale=case["scale"])
+        dq, dk, dv = jfa.bwd(q, k, v, off, o, lse, g, broadcast_q=bq, causal=causal, scale=case["scale"])
+        torch.cuda.synchronize()
+    finally:
+        jfa.set_schedule(old)
+    o_ref, lse_ref, dq_ref, dk_ref, dv_ref = _padded_reference(q, k, v, g, off, broadcast_q=bq,
+                                                               causal=causal, scale=case["scale"])
+    _check_o(o, o_ref)
+    _check_lse(lse, lse_ref)
+    for what, got, ref in (("dQ", dq, dq_ref), ("dK", dk, dk_ref), ("dV", dv, dv_ref)):
+        _check(got, ref, TOL_GRAD * max(ref.abs().max().item(), 1e-30), what)
+
+
+@pytest.mark.parametrize("bq", [False, True])
+def test_many_sequences_sparse_every_block_equals_dense(bq):
+    """Block-sparse forward with k covering every block of every sequence of a
+    17,000-sequence batch: the dense forward on every row (tolerance 2x parity, plus
+    one bf16 ulp of O since both sides are rounded)."""
+    jfa = _jfa()
+    lengths = _lengths(6, 17000, 0, 190)
+    case, q, k, v, g, off = _case(lengths, heads=2, head_dim=64, broadcast_q=bq, causal=False,
+                                  q_len=40 if bq else 0, seed=7)
+    o_s, lse_s = jfa.fwd_sparse(q, k, v, off, broadcast_q=bq, topk=4, scale=case["scale"])
+    o_d, lse_d = jfa.fwd(q, k, v, off, broadcast_q=bq, scale=case["scale"])
+    torch.cuda.synchronize()
+    # both outputs are bf16 roundings of nearly equal values: allow one bf16 ulp apart
+    diff = (o_s.float() - o_d.float()).abs() - o_d.float().abs() / 128
+    assert diff.max().item() <= 2 * TOL_O, f"O: {diff.max().item():.3e}"
+    assert torch.equal(torch.isneginf(lse_s), torch.isneginf(lse_d))
+    fin = ~torch.isneginf(lse_d)
+    _check(lse_s[fin], lse_d[fin], 2 * TOL_LSE, "LSE")

@@ -79,6 +79,29 @@ __device__ __forceinline__ int aggregated_increment(int* counters, int key) {
   return result;
 }
 
+// The planners walk the batch in segments of kSeg sequences whose offsets are first
+// copied into LDS with coalesced loads (offsets < 2^30 fit in int); each thread then
+// takes a run of at most kSeg / kPlanThreads consecutive sequences of the segment.
+constexpr int kSeg = 8192;
+struct Segment {
+  int b0;    // first sequence of the segment
+  int len;   // sequences in it
+  int bb, be;   // this thread's run [bb, be) (segment-relative)
+};
+// Copies offsets[b0 .. b0 + len] of segment s into offs; returns the thread's run.
+__device__ Segment stage_segment(const void* offsets, int off64, int batch, int s, int* offs) {
+  Segment g;
+  g.b0 = s * kSeg;
+  g.len = min(kSeg, batch - g.b0);
+  __syncthreads();   // earlier readers of offs are done
+  for (int i = threadIdx.x; i <= g.len; i += kPlanThreads) offs[i] = (int)load_offset(offsets, off64, g.b0 + i);
+  __syncthreads();
+  const int per = (g.len + kPlanThreads - 1) / kPlanThreads;
+  g.bb = min(g.len, (int)threadIdx.x * per);
+  g.be = min(g.len, g.bb + per);
+  return g;
+}
+
 struct PlanFwdArgs {
   const void* offsets;
   int off64;
@@ -111,40 +134,42 @@ __device__ __forceinline__ int fwd_cost(const PlanFwdArgs& a, int64_t n, int m) 
 __global__ __launch_bounds__(kPlanThreads) void plan_fwd_kernel(PlanFwdArgs a) {
   __shared__ int wave_sums[kPlanThreads / 64 + 1];
   __shared__ int hist[kKeys];
+  __shared__ int offs[kSeg + 1];
   const int tid = threadIdx.x;
-  const int per = (a.batch + kPlanThreads - 1) / kPlanThreads;
-  const int b_begin = min(a.batch, tid * per);
-  const int b_end = min(a.batch, b_begin + per);
-
-  int count = 0;
-  for (int b = b_begin; b < b_end; ++b) {
-    const int64_t n = load_offset(a.offsets, a.off64, b + 1) - load_offset(a.offsets, a.off64, b);
-    count += fwd_items_of(a, n);
-  }
+  const int nseg = (a.batch + kSeg - 1) / kSeg;
+  auto seq_len = [&](int b) { return (int64_t)(offs[b + 1] - offs[b]); };
   int total = 0;
-  const int base = block_exclusive_scan(count, wave_sums, &total);
 
   if (a.sched == kIdentity) {
-    int pos = base;
-    for (int b = b_begin; b < b_end; ++b) {
-      const int64_t n = load_offset(a.offsets, a.off64, b + 1) - load_offset(a.offsets, a.off64, b);
-      const int mi = fwd_items_of(a, n);
-      const int kv0 = (int)load_offset(a.offsets, a.off64, b);
-      for (int m = 0; m < mi; ++m) a.items[pos++] = make_int4(b, m, kv0, (int)n);
+    for (int sg = 0; sg < nseg; ++sg) {
+      const Segment g = stage_segment(a.offsets, a.off64, a.batch, sg, offs);
+      int count = 0;
+      for (int b = g.bb; b < g.be; ++b) count += fwd_items_of(a, seq_len(b));
+      int tot = 0;
+      int pos = total + block_exclusive_scan(count, wave_sums, &tot);
+      for (int b = g.bb; b < g.be; ++b) {
+        const int mi = fwd_items_of(a, seq_len(b));
+        for (int m = 0; m < mi; ++m) a.items[pos++] = make_int4(g.b0 + b, m, offs[b], (int)seq_len(b));
+      }
+      total += tot;
     }
   } else {
     for (int i = tid; i < kKeys; i += kPlanThreads) hist[i] = 0;
-    __syncthreads();
-    const int rounds = wave_max(count);
-    // pass 1: histogram of costs
-    {
-      int b = b_begin, m = 0;
+    // pass 1: histogram of costs (and the item count)
+    for (int sg = 0; sg < nseg; ++sg) {
+      const Segment g = stage_segment(a.offsets, a.off64, a.batch, sg, offs);
+      int count = 0;
+      for (int b = g.bb; b < g.be; ++b) count += fwd_items_of(a, seq_len(b));
+      int tot = 0;
+      block_exclusive_scan(count, wave_sums, &tot);
+      total += tot;
+      const int rounds = wave_max(count);
+      int b = g.bb, m = 0, mi = 0;
       int64_t n = 0;
-      int mi = 0;
       for (int r = 0; r < rounds; ++r) {
         if (r < count) {
           while (m >= mi) {  // advance to the next sequence that has items
-            n = load_offset(a.offsets, a.off64, b + 1) - load_offset(a.offsets, a.off64, b);
+            n = seq_len(b);
             mi = fwd_items_of(a, n);
             m = 0;
             if (mi == 0) ++b;
@@ -165,21 +190,23 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fwd_kernel(PlanFwdArgs a) {
     }
     __syncthreads();
     // pass 2: scatter in cost order
-    {
-      int b = b_begin, m = 0;
-      int64_t n = 0, kv0 = 0;
-      int mi = 0;
+    for (int sg = 0; sg < nseg; ++sg) {
+      const Segment g = stage_segment(a.offsets, a.off64, a.batch, sg, offs);
+      int count = 0;
+      for (int b = g.bb; b < g.be; ++b) count += fwd_items_of(a, seq_len(b));
+      const int rounds = wave_max(count);
+      int b = g.bb, m = 0, mi = 0;
+      int64_t n = 0;
       for (int r = 0; r < rounds; ++r) {
         if (r < count) {
           while (m >= mi) {
-            kv0 = load_offset(a.offsets, a.off64, b);
-            n = load_offset(a.offsets, a.off64, b + 1) - kv0;
+            n = seq_len(b);
             mi = fwd_items_of(a, n);
             m = 0;
             if (mi == 0) ++b;
           }
           const int pos = aggregated_increment(hist, fwd_cost(a, n, m));
-          a.items[pos] = make_int4(b, m, (int)kv0, (int)n);
+          a.items[pos] = make_int4(g.b0 + b, m, offs[b], (int)n);
           if (++m >= mi) ++b;
         }
       }
@@ -212,26 +239,28 @@ struct PlanBwdArgs {
 // rejects T >= 2^30), so a tile's geometry is one 16-byte load.
 __global__ __launch_bounds__(kPlanThreads) void plan_bwd_kernel(PlanBwdArgs a) {
   __shared__ int wave_sums[kPlanThreads / 64 + 1];
+  __shared__ int offs[kSeg + 1];
   __shared__ int all_single;
   const int tid = threadIdx.x;
   if (tid == 0) all_single = 1;
-  __syncthreads();
-  const int per = (a.batch + kPlanThreads - 1) / kPlanThreads;
-  const int b_begin = min(a.batch, tid * per);
-  const int b_end = min(a.batch, b_begin + per);
-  int count = 0;
-  for (int b = b_begin; b < b_end; ++b) {
-    const int64_t n = load_offset(a.offsets, a.off64, b + 1) - load_offset(a.offsets, a.off64, b);
-    count += (int)((n + a.bn - 1) / a.bn);
-    if (n > a.bn) all_single = 0;   // every writer stores the same value
-  }
+  const int nseg = (a.batch + kSeg - 1) / kSeg;
   int total = 0;
-  int pos = block_exclusive_scan(count, wave_sums, &total);
-  for (int b = b_begin; b < b_end; ++b) {
-    const int64_t kv0 = load_offset(a.offsets, a.off64, b);
-    const int64_t n = load_offset(a.offsets, a.off64, b + 1) - kv0;
-    const int nb = (int)((n + a.bn - 1) / a.bn);
-    for (int j = 0; j < nb; ++j) a.items[pos++] = make_int4(b, j, (int)kv0, (int)n);
+  for (int sg = 0; sg < nseg; ++sg) {
+    const Segment g = stage_segment(a.offsets, a.off64, a.batch, sg, offs);
+    int count = 0;
+    for (int b = g.bb; b < g.be; ++b) {
+      const int n = offs[b + 1] - offs[b];
+      count += (n + a.bn - 1) / a.bn;
+      if (n > a.bn) all_single = 0;   // every writer stores the same value
+    }
+    int tot = 0;
+    int pos = total + block_exclusive_scan(count, wave_sums, &tot);
+    for (int b = g.bb; b < g.be; ++b) {
+      const int kv0 = offs[b], n = offs[b + 1] - kv0;
+      const int nb = (n + a.bn - 1) / a.bn;
+      for (int j = 0; j < nb; ++j) a.items[pos++] = make_int4(g.b0 + b, j, kv0, n);
+    }
+    total += tot;
   }
   if (tid == 0) {
     a.meta[0] = total;
@@ -255,29 +284,33 @@ struct PlanSparseArgs {
 
 __global__ __launch_bounds__(kPlanThreads) void plan_sparse_kernel(PlanSparseArgs a) {
   __shared__ int wave_sums[kPlanThreads / 64 + 1];
-  const int tid = threadIdx.x;
-  const int per = (a.batch + kPlanThreads - 1) / kPlanThreads;
-  const int b_begin = min(a.batch, tid * per);
-  const int b_end = min(a.batch, b_begin + per);
-  int ckv = 0, cq = 0;
-  for (int b = b_begin; b < b_end; ++b) {
-    const int64_t n = load_offset(a.offsets, a.off64, b + 1) - load_offset(a.offsets, a.off64, b);
-    ckv += (int)((n + kFwdBN - 1) / kFwdBN);
-    cq += (int)((n + kSparseQBSelf - 1) / kSparseQBSelf);
+  __shared__ int offs[kSeg + 1];
+  const int nseg = (a.batch + kSeg - 1) / kSeg;
+  int base_kv = 0, base_q = 0;
+  for (int sg = 0; sg < nseg; ++sg) {
+    const Segment g = stage_segment(a.offsets, a.off64, a.batch, sg, offs);
+    int ckv = 0, cq = 0;
+    for (int b = g.bb; b < g.be; ++b) {
+      const int n = offs[b + 1] - offs[b];
+      ckv += (n + kFwdBN - 1) / kFwdBN;
+      cq += (n + kSparseQBSelf - 1) / kSparseQBSelf;
+    }
+    int tkv = 0, tq = 0;
+    int pkv = base_kv + block_exclusive_scan(ckv, wave_sums, &tkv);
+    int pq = base_q + block_exclusive_scan(cq, wave_sums, &tq);
+    for (int b = g.bb; b < g.be; ++b) {
+      a.kv_first[g.b0 + b] = pkv;
+      a.q_first[g.b0 + b] = pq;
+      const int n = offs[b + 1] - offs[b];
+      pkv += (n + kFwdBN - 1) / kFwdBN;
+      pq += (n + kSparseQBSelf - 1) / kSparseQBSelf;
+    }
+    base_kv += tkv;
+    base_q += tq;
   }
-  int tkv = 0, tq = 0;
-  int pkv = block_exclusive_scan(ckv, wave_sums, &tkv);
-  int pq = block_exclusive_scan(cq, wave_sums, &tq);
-  for (int b = b_begin; b < b_end; ++b) {
-    a.kv_first[b] = pkv;
-    a.q_first[b] = pq;
-    const int64_t n = load_offset(a.offsets, a.off64, b + 1) - load_offset(a.offsets, a.off64, b);
-    pkv += (int)((n + kFwdBN - 1) / kFwdBN);
-    pq += (int)((n + kSparseQBSelf - 1) / kSparseQBSelf);
-  }
-  if (tid == 0) {
-    a.kv_first[a.batch] = tkv;
-    a.q_first[a.batch] = tq;
+  if (threadIdx.x == 0) {
+    a.kv_first[a.batch] = base_kv;
+    a.q_first[a.batch] = base_q;
   }
 }
 
