@@ -13,3 +13,4 @@ from .attention import (  # noqa: F401
 )
 from .rope import rope_rotate, rope_conjugate, backward_rope  # noqa: F401
 from . import sparse  # noqa: F401  (block-sparse top-k forward)
+from . import mxfp8  # noqa: F401  (block-scaled 8-bit forward)
