@@ -31,7 +31,7 @@ import torch  # noqa: E402
 import workloads  # noqa: E402
 
 METRIC = "useful TFLOP/s fwd & bwd, jagged broadcast-Q attn bf16; % of MFMA peak"
-KERNEL_SOURCES = ["fwd.hip", "bwd.hip", "plan.hip", "sparse.hip", "jfa_device.h", "jfa_internal.h"]
+KERNEL_SOURCES = ["fwd.hip", "bwd.hip", "plan.hip", "sparse.hip", "mxfp8.hip", "jfa_device.h", "jfa_internal.h"]
 PROFILES = os.path.join(ROOT, "profiles")
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
@@ -227,6 +227,62 @@ def rope_comparison(args, jfa, w, case, o, lse, dq, dk, dv, ws_f, ws_b):
           flush=True)
 
 
+def mxfp8_comparison(args, jfa, w, case, o, lse, ws_f):
+    """bf16 forward vs the MXFP8 forward (jfa_fwd_mxfp8 on operands quantized once),
+    and the MXFP8 forward with the quantization of Q, K and V included; the kernel
+    times come from HIP events around each launch, and the forward's useful FLOP
+    rate is set against the dense fp8 and bf16 matrix-core peaks."""
+    q, k, v, off = case["q"], case["k"], case["v"], case["offsets"]
+    bq, causal, scale = w.broadcast_q, w.causal, case["scale"]
+    q8, qs = jfa.mxfp8_quantize_rows(q)
+    k8, ks = jfa.mxfp8_quantize_rows(k)
+    v8, vs = jfa.mxfp8_quantize_v(v, off)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        jfa.profile_enable(True)
+        jfa.profile_read()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(args.steps):
+            fn()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        kern = {k_: round(v_[0] / v_[1], 4) for k_, v_ in jfa.profile_read().items()}
+        jfa.profile_enable(False)
+        return round(start.elapsed_time(stop) / args.steps, 4), kern
+
+    def mx_fwd():
+        jfa.fwd_mxfp8(q8, qs, k8, ks, v8, vs, off, broadcast_q=bq, causal=causal, scale=scale, out=o, lse=lse,
+                      workspace=ws_f)
+
+    def mx_all():
+        jfa.mxfp8_quantize_rows(q, q8, qs)
+        jfa.mxfp8_quantize_rows(k, k8, ks)
+        jfa.mxfp8_quantize_v(v, off, v8, vs)
+        mx_fwd()
+
+    res, kernels = {}, {}
+    res["bf16_fwd"], kernels["bf16_fwd"] = timed(
+        lambda: jfa.fwd(q, k, v, off, broadcast_q=bq, causal=causal, scale=scale, out=o, lse=lse, workspace=ws_f))
+    res["mxfp8_fwd"], kernels["mxfp8_fwd"] = timed(mx_fwd)
+    res["mxfp8_quantize_and_fwd"], kernels["mxfp8_quantize_and_fwd"] = timed(mx_all)
+    fwd_flops, _ = useful_flops(w, case["lengths"])
+    t_mx = kernels["mxfp8_fwd"]["fwd_mxfp8"]
+    t_bf = kernels["bf16_fwd"]["fwd"]
+    tflops = {"mxfp8_kernel": round(fwd_flops / t_mx / 1e9, 1), "bf16_kernel": round(fwd_flops / t_bf / 1e9, 1)}
+    for name in res:
+        log(f"{name}: {res[name]:.4f} ms  kernels {kernels[name]}")
+    print(json.dumps({"mode": "mxfp8", "workload": w.name, "steps": args.steps, "ms": res, "kernel_ms": kernels,
+                      "kernel_tflops": tflops,
+                      "frac_of_peak": {"mxfp8_kernel_vs_fp8_5000": round(tflops["mxfp8_kernel"] / 5000.0, 4),
+                                       "bf16_kernel_vs_bf16_2500": round(tflops["bf16_kernel"] / 2500.0, 4)},
+                      "mxfp8_over_bf16_kernel": round(t_bf / t_mx, 4)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,6 +300,9 @@ def main():
     ap.add_argument("--sparse", type=str, default="", metavar="K[,K...]",
                     help="instead of the step: time the block-sparse forward (jfa_fwd_sparse) with "
                          "these top-k values against the dense forward (non-causal workloads)")
+    ap.add_argument("--mxfp8", action="store_true",
+                    help="instead of the step: time the MXFP8 forward (jfa_fwd_mxfp8) against the bf16 "
+                         "forward, with and without the quantization of Q, K and V")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (3 times); used to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -294,6 +353,9 @@ def main():
         return
     if args.sparse:
         sparse_comparison(args, jfa, w, case, o, lse, ws_f)
+        return
+    if args.mxfp8:
+        mxfp8_comparison(args, jfa, w, case, o, lse, ws_f)
         return
 
     log(f"workload {w.name}: B={len(lengths)} H={w.heads} D={w.head_dim} Lq={w.q_len} "

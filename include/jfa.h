@@ -84,7 +84,8 @@ typedef enum {
 jfa_status_t jfa_set_schedule(int schedule);
 int jfa_get_schedule(void);
 
-/* Bytes of workspace jfa_fwd needs for these sizes (0 if the sizes are invalid). */
+/* Bytes of workspace jfa_fwd and jfa_fwd_mxfp8 need for these sizes (0 if the sizes
+ * are invalid). */
 size_t jfa_fwd_workspace_size(int64_t batch, int64_t num_heads, int64_t head_dim,
                               int64_t q_len, int64_t total_kv, int broadcast_q, int causal);
 
@@ -184,6 +185,58 @@ jfa_status_t jfa_fwd_sparse(const void* q, const void* k, const void* v,
                             float softmax_scale, int topk,
                             void* o, float* lse, int32_t* blocks,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* MXFP8 forward ("Meta's TLX attention kernel outpaces FlashAttention-4 on B200",
+ * section on the kernel's variants: E4M3 values with one E8M0 scale per block).
+ *
+ * E4M3: OCP 8-bit float (bias 7, subnormals, largest 448, no infinities).  E8M0:
+ * code c stands for 2^(c - 127).  A block is 32 elements along a product's
+ * contraction axis; its scale is the smallest 2^e with max|x| <= 448 * 2^e (nothing
+ * saturates), and each element is x / 2^e rounded to the nearest E4M3, ties to even.
+ *
+ * jfa_mxfp8_quantize_rows: Q or K rows.  x: bf16 [rows][num_heads][head_dim]
+ *   (head_dim 64 or 128); values: uint8 E4M3, same shape; scales: uint8 E8M0
+ *   [rows][num_heads][head_dim / 32], block c covering columns 32 c .. 32 c + 31.
+ *   x and values 16-byte aligned.  Inputs must be finite (no NaN or infinity).
+ *
+ * jfa_mxfp8_v_blocks(batch, total_kv) = batch + ceil(total_kv / 32): the number of
+ *   V blocks G that values and scales of jfa_mxfp8_quantize_v must hold.
+ * jfa_mxfp8_quantize_v: V by key blocks.  v: bf16 [total_kv][num_heads][head_dim];
+ *   offsets as jfa_fwd.  Block j of sequence b (keys 32 j .. 32 j + 31 of the
+ *   sequence; the last block's missing keys are stored as zeros) has index
+ *   g = b + floor(offsets[b] / 32) + j.  values: uint8 E4M3 [G][num_heads][head_dim][32],
+ *   the 32 bytes of (g, h, d) holding key k of the block at byte
+ *   16 * ((k >> 2) & 1) + 4 * (k >> 3) + (k & 3) (the matrix-core operand order);
+ *   scales: uint8 E8M0 [G][num_heads][head_dim].  Entries at indices no block uses
+ *   are left unwritten and never read.
+ *
+ * jfa_fwd_mxfp8: the forward on these operands (q8/q_scales from Q rows in the
+ *   layout jfa_fwd takes Q: [q_len] or [total_kv] rows; k8/k_scales from K rows;
+ *   v8/v_scales from jfa_mxfp8_quantize_v with the same offsets).  Both products
+ *   run on the block-scaled matrix cores with fp32 accumulation.  Softmax in base 2
+ *   with x = fp32(S) * fp32(softmax_scale * log2 e), the row maximum rounded up to
+ *   an integer m, p = 2^(x - m) in fp32 and l = sum of p; P is quantized in blocks
+ *   of 32 keys (aligned to the sequence start) by the same rule before the product
+ *   with V, so O = (deq P)(deq V) / l in bf16 [rows][num_heads][head_dim], and
+ *   LSE = ln 2 * (m + log2 l) in fp32 [num_heads][rows] (-inf for a row with no
+ *   keys, whose O is zero).  q8, k8, v8, v_scales, o and workspace
+ *   must be 16-byte aligned, k_scales aligned to head_dim / 32 bytes.  Modes,
+ *   offsets, sizes, workspace (jfa_fwd_workspace_size with the same sizes) and errors
+ *   as jfa_fwd.
+ * Profile names: "mx_quantize_rows", "mx_quantize_v", "plan_fwd", "fwd_mxfp8". */
+int64_t jfa_mxfp8_v_blocks(int64_t batch, int64_t total_kv);
+jfa_status_t jfa_mxfp8_quantize_rows(const void* x, int64_t rows, int64_t num_heads, int64_t head_dim,
+                                     void* values, void* scales, void* stream);
+jfa_status_t jfa_mxfp8_quantize_v(const void* v, const void* offsets, int offsets_is_int64,
+                                  int64_t batch, int64_t num_heads, int64_t head_dim, int64_t total_kv,
+                                  void* values, void* scales, void* stream);
+jfa_status_t jfa_fwd_mxfp8(const void* q8, const void* q_scales, const void* k8, const void* k_scales,
+                           const void* v8, const void* v_scales,
+                           const void* offsets, int offsets_is_int64,
+                           int64_t batch, int64_t num_heads, int64_t head_dim,
+                           int64_t q_len, int64_t total_kv, int broadcast_q, int causal,
+                           float softmax_scale, void* o, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Measurement support.  While enabled on a thread, every kernel this library
  * launches from that thread is bracketed by two HIP events recorded on the

@@ -156,3 +156,30 @@ def test_sparse_rejections_and_sizes(lib):
     nqb = lib.jfa_fwd_sparse_query_blocks
     assert nqb(4, 600, 1000, 1) == 4 * 3              # broadcast: B * ceil(Lq / 256)
     assert nqb(3, 0, 1000, 0) >= 1000 // 128 + 3       # self: an upper bound of sum ceil(n_b / 128)
+
+
+def fwd_mx(lib, *, batch=4, heads=2, head_dim=128, q_len=64, total_kv=100, bq=1, causal=0, scale=0.1,
+           ws=FAKE, ws_bytes=1 << 30, q8=FAKE, qs=FAKE):
+    return lib.jfa_fwd_mxfp8(q8, qs, FAKE, FAKE, FAKE, FAKE, FAKE, 0, batch, heads, head_dim, q_len, total_kv,
+                             bq, causal, scale, FAKE, FAKE, ws, ws_bytes, None)
+
+
+def test_mxfp8_rejections_and_sizes(lib):
+    assert fwd_mx(lib, head_dim=96) == UNSUPPORTED
+    assert b"jfa_fwd_mxfp8" in lib.jfa_last_error()
+    assert fwd_mx(lib, bq=1, causal=1) == UNSUPPORTED
+    assert fwd_mx(lib, scale=0.0) == INVALID
+    assert fwd_mx(lib, qs=None) == INVALID                                  # null scales
+    assert fwd_mx(lib, q8=ctypes.c_void_p((1 << 20) + 8)) == INVALID       # 16-byte aligned values
+    assert fwd_mx(lib, ws_bytes=16) == WS_SMALL
+    assert fwd_mx(lib, batch=0, ws=None) == OK
+    assert lib.jfa_mxfp8_v_blocks(3, 100) == 3 + 4 and lib.jfa_mxfp8_v_blocks(0, 0) == 0
+    qr = lib.jfa_mxfp8_quantize_rows
+    assert qr(FAKE, 10, 2, 96, FAKE, FAKE, None) == UNSUPPORTED
+    assert qr(FAKE, -1, 2, 128, FAKE, FAKE, None) == INVALID
+    assert qr(None, 10, 2, 128, FAKE, FAKE, None) == INVALID
+    assert qr(None, 0, 2, 128, None, None, None) == OK                       # empty: a no-op
+    qv = lib.jfa_mxfp8_quantize_v
+    assert qv(FAKE, FAKE, 0, 4, 2, 64, 100, None, FAKE, None) == INVALID
+    assert qv(FAKE, FAKE, 0, 4, 2, 48, 100, FAKE, FAKE, None) == UNSUPPORTED
+    assert qv(None, None, 0, 0, 2, 64, 0, None, None, None) == OK

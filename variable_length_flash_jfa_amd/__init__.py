@@ -11,6 +11,10 @@ from ._binding import (  # noqa: F401
     SCHED_DYNAMIC,
     fwd,
     fwd_sparse,
+    fwd_mxfp8,
+    mxfp8_quantize_rows,
+    mxfp8_quantize_v,
+    mxfp8_v_blocks,
     bwd,
     fwd_workspace_size,
     bwd_workspace_size,

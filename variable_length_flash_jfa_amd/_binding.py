@@ -75,6 +75,15 @@ def library() -> ctypes.CDLL:
             lib.jfa_fwd_sparse.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, i64, i32, f32, i32,
                                            vp, vp, vp, vp, sz, vp]
             lib.jfa_fwd_sparse.restype = i32
+            lib.jfa_mxfp8_v_blocks.argtypes = [i64, i64]
+            lib.jfa_mxfp8_v_blocks.restype = i64
+            lib.jfa_mxfp8_quantize_rows.argtypes = [vp, i64, i64, i64, vp, vp, vp]
+            lib.jfa_mxfp8_quantize_rows.restype = i32
+            lib.jfa_mxfp8_quantize_v.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, vp, vp]
+            lib.jfa_mxfp8_quantize_v.restype = i32
+            lib.jfa_fwd_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, i64,
+                                          i32, i32, f32, vp, vp, vp, sz, vp]
+            lib.jfa_fwd_mxfp8.restype = i32
             lib.jfa_last_error.argtypes = []
             lib.jfa_last_error.restype = ctypes.c_char_p
             lib.jfa_version.argtypes = []
@@ -223,6 +232,81 @@ def fwd_sparse(q, k, v, offsets, *, broadcast_q: bool, topk: int, scale=None, ou
                                   _ptr(sel), _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st)
     return (out, lse, sel) if blocks else (out, lse)
+
+
+def _check_bf16(name, t):
+    if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda or t.dim() != 3:
+        raise ValueError(f"{name} must be a contiguous bf16 GPU tensor [rows, heads, head_dim]")
+
+
+def mxfp8_quantize_rows(x, values=None, scales=None):
+    """Q or K rows -> (E4M3 values uint8 [rows, H, D], E8M0 scales uint8 [rows, H, D / 32])."""
+    _check_bf16("x", x)
+    rows, heads, head_dim = x.shape
+    if values is None:
+        values = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, heads, head_dim // 32), dtype=torch.uint8, device=x.device)
+    _check(library().jfa_mxfp8_quantize_rows(_ptr(x), rows, heads, head_dim, _ptr(values), _ptr(scales),
+                                             _stream(x.device)))
+    return values, scales
+
+
+def mxfp8_v_blocks(batch: int, total_kv: int) -> int:
+    return int(library().jfa_mxfp8_v_blocks(batch, total_kv))
+
+
+def mxfp8_quantize_v(v, offsets, values=None, scales=None):
+    """V -> (E4M3 values uint8 [G, H, D, 32], E8M0 scales uint8 [G, H, D]) in 32-key
+    blocks of each sequence, G = mxfp8_v_blocks(batch, total_kv)."""
+    _check_bf16("v", v)
+    if offsets.dtype not in (torch.int32, torch.int64) or not offsets.is_cuda or not offsets.is_contiguous():
+        raise TypeError("offsets must be a contiguous int32/int64 GPU tensor")
+    total_kv, heads, head_dim = v.shape
+    batch = offsets.numel() - 1
+    g = mxfp8_v_blocks(batch, total_kv)
+    if values is None:
+        values = torch.zeros((g, heads, head_dim, 32), dtype=torch.uint8, device=v.device)
+    if scales is None:
+        scales = torch.zeros((g, heads, head_dim), dtype=torch.uint8, device=v.device)
+    _check(library().jfa_mxfp8_quantize_v(_ptr(v), _ptr(offsets), int(offsets.dtype == torch.int64), batch,
+                                          heads, head_dim, total_kv, _ptr(values), _ptr(scales),
+                                          _stream(v.device)))
+    return values, scales
+
+
+def fwd_mxfp8(q8, q_scales, k8, k_scales, v8, v_scales, offsets, *, broadcast_q: bool,
+              causal: bool = False, scale=None, out=None, lse=None, workspace=None):
+    """O, LSE = jfa_fwd_mxfp8(...) on the outputs of mxfp8_quantize_rows (Q, K) and
+    mxfp8_quantize_v (V).  O: [rows, H, D] bf16; LSE: [H, rows] fp32."""
+    for name, t in (("q8", q8), ("q_scales", q_scales), ("k8", k8), ("k_scales", k_scales), ("v8", v8),
+                    ("v_scales", v_scales)):
+        if t.dtype != torch.uint8 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous uint8 GPU tensor")
+    if offsets.dtype not in (torch.int32, torch.int64) or not offsets.is_cuda or not offsets.is_contiguous():
+        raise TypeError("offsets must be a contiguous int32/int64 GPU tensor")
+    batch, heads, head_dim, q_len, total_kv, rows = _sizes(q8, k8, offsets, broadcast_q)
+    g = mxfp8_v_blocks(batch, total_kv)
+    if tuple(v8.shape) != (g, heads, head_dim, 32) or tuple(v_scales.shape) != (g, heads, head_dim):
+        raise ValueError("v8 / v_scales must come from mxfp8_quantize_v with the same offsets")
+    if tuple(q_scales.shape) != (q8.shape[0], heads, head_dim // 32) or \
+            tuple(k_scales.shape) != (total_kv, heads, head_dim // 32):
+        raise ValueError("q_scales / k_scales must come from mxfp8_quantize_rows")
+    scale = 1.0 / math.sqrt(head_dim) if scale is None else float(scale)
+    dev = q8.device
+    if out is None:
+        out = torch.empty((rows, heads, head_dim), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((heads, rows), dtype=torch.float32, device=dev)
+    need = fwd_workspace_size(batch, heads, head_dim, q_len, total_kv, broadcast_q, causal)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = library().jfa_fwd_mxfp8(_ptr(q8), _ptr(q_scales), _ptr(k8), _ptr(k_scales), _ptr(v8), _ptr(v_scales),
+                                 _ptr(offsets), int(offsets.dtype == torch.int64), batch, heads, head_dim,
+                                 q_len, total_kv, int(broadcast_q), int(causal), scale, _ptr(out), _ptr(lse),
+                                 _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st)
+    return out, lse
 
 
 def bwd(q, k, v, offsets, o, lse, d_o, *, broadcast_q: bool, causal: bool = False, scale=None,

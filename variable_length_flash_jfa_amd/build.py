@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libjfa.so")
-SOURCES = ["api.cpp", "plan.hip", "fwd.hip", "bwd.hip", "sparse.hip"]
+SOURCES = ["api.cpp", "plan.hip", "fwd.hip", "bwd.hip", "sparse.hip", "mxfp8.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

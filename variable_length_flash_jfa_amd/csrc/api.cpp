@@ -224,9 +224,11 @@ int jfa_get_schedule(void) { return g_schedule.load(); }
 size_t jfa_fwd_workspace_size(int64_t batch, int64_t num_heads, int64_t head_dim, int64_t q_len,
                               int64_t total_kv, int broadcast_q, int causal) {
   if (!check_sizes(batch, num_heads, head_dim, q_len, total_kv, broadcast_q, causal).ok) return 0;
-  const jfa::Problem p = make_problem(nullptr, nullptr, nullptr, nullptr, 0, batch, num_heads, head_dim,
-                                      q_len, total_kv, broadcast_q, causal, 1.f);
-  return fwd_ws_bytes(p);
+  jfa::Problem p = make_problem(nullptr, nullptr, nullptr, nullptr, 0, batch, num_heads, head_dim,
+                                q_len, total_kv, broadcast_q, causal, 1.f);
+  const size_t plain = fwd_ws_bytes(p);
+  p.mx = 1;   // the MXFP8 forward takes the same workspace
+  return std::max(plain, fwd_ws_bytes(p));
 }
 
 size_t jfa_bwd_workspace_size(int64_t batch, int64_t num_heads, int64_t head_dim, int64_t q_len,
@@ -436,6 +438,91 @@ jfa_status_t jfa_fwd_sparse(const void* q, const void* k, const void* v, const v
   if (e != hipSuccess) return hip_fail(e, "jfa_fwd_sparse: selection launch");
   e = timed_launch("fwd_sparse", s, [&] { return jfa::launch_fwd_sparse(p, plan, sched, sp, o, lse, s); });
   if (e != hipSuccess) return hip_fail(e, "jfa_fwd_sparse: kernel launch");
+  return JFA_OK;
+}
+
+int64_t jfa_mxfp8_v_blocks(int64_t batch, int64_t total_kv) {
+  if (batch < 0 || total_kv < 0) return 0;
+  return jfa::mx_v_blocks(batch, total_kv);
+}
+
+jfa_status_t jfa_mxfp8_quantize_rows(const void* x, int64_t rows, int64_t num_heads, int64_t head_dim,
+                                     void* values, void* scales, void* stream) {
+  g_error[0] = '\0';
+  if (rows < 0 || num_heads < 1 || num_heads >= 4096)
+    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_mxfp8_quantize_rows: rows must be >= 0, num_heads in [1, 4095]");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(JFA_ERR_UNSUPPORTED, "jfa_mxfp8_quantize_rows: head_dim must be 64 or 128");
+  if (rows >= ((int64_t)1 << 31) / num_heads)
+    return fail(JFA_ERR_UNSUPPORTED, "jfa_mxfp8_quantize_rows: too many rows for this library build");
+  if (rows == 0) return JFA_OK;
+  if (!x || !values || !scales) return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_mxfp8_quantize_rows: null pointer argument");
+  if (misaligned(x) || misaligned(values))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_mxfp8_quantize_rows: x and values must be 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = timed_launch("mx_quantize_rows", s, [&] {
+    return jfa::launch_mx_quantize_rows(x, rows, (int)num_heads, (int)head_dim, values, scales, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "jfa_mxfp8_quantize_rows: kernel launch");
+  return JFA_OK;
+}
+
+jfa_status_t jfa_mxfp8_quantize_v(const void* v, const void* offsets, int offsets_is_int64, int64_t batch,
+                                  int64_t num_heads, int64_t head_dim, int64_t total_kv, void* values,
+                                  void* scales, void* stream) {
+  g_error[0] = '\0';
+  const Sizes sz = check_sizes(batch, num_heads, head_dim, 0, total_kv, 0, 0);
+  if (!sz.ok) return fail(sz.st, "jfa_mxfp8_quantize_v: %s", sz.why);
+  if (batch == 0) return JFA_OK;
+  if (!offsets || !values || !scales || (total_kv > 0 && !v))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_mxfp8_quantize_v: null pointer argument");
+  if (misaligned(v) || misaligned(values) || (reinterpret_cast<uintptr_t>(offsets) & (offsets_is_int64 ? 7 : 3)))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_mxfp8_quantize_v: v and values must be 16-byte aligned");
+  const jfa::Problem p = make_problem(nullptr, nullptr, v, offsets, offsets_is_int64, batch, num_heads, head_dim,
+                                      0, total_kv, 0, 0, 1.f);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = timed_launch("mx_quantize_v", s, [&] { return jfa::launch_mx_quantize_v(p, v, values, scales, s); });
+  if (e != hipSuccess) return hip_fail(e, "jfa_mxfp8_quantize_v: kernel launch");
+  return JFA_OK;
+}
+
+jfa_status_t jfa_fwd_mxfp8(const void* q8, const void* q_scales, const void* k8, const void* k_scales,
+                           const void* v8, const void* v_scales, const void* offsets, int offsets_is_int64,
+                           int64_t batch, int64_t num_heads, int64_t head_dim, int64_t q_len, int64_t total_kv,
+                           int broadcast_q, int causal, float softmax_scale, void* o, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  g_error[0] = '\0';
+  const Sizes sz = check_sizes(batch, num_heads, head_dim, q_len, total_kv, broadcast_q, causal);
+  if (!sz.ok) return fail(sz.st, "jfa_fwd_mxfp8: %s", sz.why);
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
+    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_fwd_mxfp8: softmax_scale must be finite and > 0");
+  jfa::Problem p = make_problem(q8, k8, v8, offsets, offsets_is_int64, batch, num_heads, head_dim, q_len,
+                                total_kv, broadcast_q, causal, softmax_scale);
+  p.mx = 1;
+  if (p.batch == 0 || p.rows == 0) return JFA_OK;
+  if (!q8 || !q_scales || !offsets || !o || !lse || !workspace ||
+      (p.total_kv > 0 && (!k8 || !k_scales || !v8 || !v_scales)))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_fwd_mxfp8: null pointer argument");
+  if (misaligned(q8) || misaligned(k8) || misaligned(v8) || misaligned(v_scales) || misaligned(o) ||
+      misaligned(workspace) || (reinterpret_cast<uintptr_t>(lse) & 3) ||
+      (reinterpret_cast<uintptr_t>(k_scales) & (head_dim / 32 - 1)) ||
+      (reinterpret_cast<uintptr_t>(offsets) & (offsets_is_int64 ? 7 : 3)))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_fwd_mxfp8: tensors must be 16-byte aligned");
+  const size_t need = fwd_ws_bytes(p);
+  if (workspace_bytes < need)
+    return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "jfa_fwd_mxfp8: workspace of %zu bytes, need %zu",
+                workspace_bytes, need);
+  char* cur = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(workspace)));
+  jfa::Plan plan;
+  plan.meta = reinterpret_cast<int*>(carve(cur, 64));
+  plan.max_items = jfa::fwd_max_items(p);
+  plan.items = reinterpret_cast<int4*>(carve(cur, plan.max_items * sizeof(int4)));
+  const jfa::MxOperands x{q8, q_scales, k8, k_scales, v8, v_scales};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = timed_launch("plan_fwd", s, [&] { return jfa::launch_plan_fwd(p, plan, JFA_SCHED_SORTED_ZIGZAG, s); });
+  if (e != hipSuccess) return hip_fail(e, "jfa_fwd_mxfp8: plan launch");
+  e = timed_launch("fwd_mxfp8", s, [&] { return jfa::launch_fwd_mx(p, plan, x, o, lse, s); });
+  if (e != hipSuccess) return hip_fail(e, "jfa_fwd_mxfp8: kernel launch");
   return JFA_OK;
 }
 

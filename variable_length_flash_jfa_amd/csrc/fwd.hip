@@ -460,6 +460,10 @@ hipError_t launch_d(const Problem& p, const FwdArgs& a, hipStream_t s) {
 
 int fwd_waves(const Problem& p) {
   if (p.topk > 0) return sparse_qb(p) / 32;   // block-sparse: the tile is one query block
+  if (p.mx && !p.broadcast) {                  // MXFP8 self mode: tiles near the mean length
+    const int64_t mean = p.batch > 0 ? p.total_kv / p.batch : 0;
+    return mean <= 96 ? 2 : (mean >= 384 ? 8 : 4);
+  }
   if (!p.broadcast) return 4;
   if (p.q_len > 128) return 8;
   if (p.q_len > 64) return 4;

@@ -33,6 +33,7 @@ struct Problem {
   float scale;
   int rope = 0;       // the backward applies the rotary conjugate (no direct dQ store)
   int topk = 0;       // block-sparse forward: key blocks kept per query block (0: dense)
+  int mx = 0;         // the MXFP8 forward (its own workgroup size in self mode)
 };
 
 // Block-sparse forward: key blocks of kFwdBN keys; query blocks of the rows one
@@ -91,6 +92,23 @@ hipError_t launch_fwd_sparse(const Problem& p, const Plan& plan, int sched, cons
                              float* lse, hipStream_t s);
 hipError_t launch_fwd(const Problem& p, const Plan& plan, int sched, void* o, float* lse,
                       hipStream_t s);
+
+// MXFP8 forward operands (device pointers; layouts in the MXFP8 source).
+struct MxOperands {
+  const void* q8;   // E4M3 [q rows, H, D]
+  const void* qs;   // E8M0 [q rows, H, D / 32]
+  const void* k8;   // E4M3 [T, H, D]
+  const void* ks;   // E8M0 [T, H, D / 32]
+  const void* v8;   // E4M3 [G, H, D, 32], G = mx_v_blocks(B, T)
+  const void* vs;   // E8M0 [G, H, D]
+};
+int64_t mx_v_blocks(int64_t batch, int64_t total_kv);
+hipError_t launch_mx_quantize_rows(const void* x, int64_t rows, int heads, int head_dim, void* val, void* scl,
+                                   hipStream_t s);
+hipError_t launch_mx_quantize_v(const Problem& p, const void* v, void* val, void* scl, hipStream_t s);
+// After the forward plan (launch_plan_fwd with the same problem).
+hipError_t launch_fwd_mx(const Problem& p, const Plan& plan, const MxOperands& x, void* o, float* lse,
+                         hipStream_t s);
 
 // rowstat: [heads][rows] pairs (LSE log2 e, delta = rowsum(dO * O)), 2 floats each,
 // and the zeroed dQ accumulator.  Runs after the backward plan and does nothing when
