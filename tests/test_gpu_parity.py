@@ -254,3 +254,89 @@ def test_full_size_workload_sampled(name):
             _check_grad(_f64(out["dq"][rows, h]), ref, f"dQ rows {rows} head {h}")
     assert np.isfinite(out["o"].float().numpy()).all()
     assert np.isfinite(out["dq"].float().numpy()).all()
+
+
+RESCALE_CASES = {
+    # name: (lengths, heads, head_dim, broadcast_q, causal, q_len, log2 growth over a sequence)
+    "bcast_d128_growing": ([1000, 300, 64, 1, 129], 2, 128, True, False, 256, 40.0),
+    "bcast_d64_growing": ([700, 33, 250], 2, 64, True, False, 100, 60.0),
+    "self_d128_causal_growing": ([900, 200, 65], 2, 128, False, True, 0, 40.0),
+    "self_d64_growing": ([500, 64, 127], 3, 64, False, False, 0, 25.0),
+}
+
+
+def _ramp_keys(case, growth_log2):
+    """Keys get a ramp along the mean query direction, so that a row's largest score
+    climbs by about growth_log2 (base 2) from the first key of a sequence to the
+    last, and the running maximum keeps moving by more than a rescale threshold."""
+    q, k = case["q"].float(), case["k"].float()
+    d = q.shape[-1]
+    q = q + 1.0                          # every query has a component along ones(D)
+    per_unit = case["scale"] * d * 1.4426950408889634   # log2 score per unit of ramp
+    lengths = case["lengths"]
+    off = np.concatenate([[0], np.cumsum(lengths)])
+    ramp = torch.zeros(k.shape[0])
+    for b, n in enumerate(lengths):
+        if n > 1:
+            ramp[off[b]:off[b + 1]] = torch.linspace(0.0, growth_log2 / per_unit, int(n))
+    k = 0.5 * k + ramp[:, None, None]
+    case = dict(case)
+    case["q"] = q.to(torch.bfloat16)
+    case["k"] = k.to(torch.bfloat16)
+    return case
+
+
+# Gradient bar for the growing-score inputs.  The ramp gives every key a large common
+# component (|K| up to about 7), and dQ = c dS K then rests on sum_j dS_ij = 0.  The
+# backward rounds dS to bf16 for its MFMA and forms delta = sum_d dO O from the bf16 O,
+# so the cancellation leaves errors proportional to |K|: rounding dS alone gives 1.5%
+# of max |dQ| on the D = 64 case (an fp64 emulation), and the bf16 O in delta adds
+# about as much again (2.6% measured).  The forward outputs keep the usual bars.
+TOL_GRAD_RAMP = 5e-2
+
+
+def _compare_ramp(case, out):
+    kw = dict(broadcast_q=case["broadcast_q"], causal=case["causal"], scale=case["scale"])
+    off = case["offsets"].numpy()
+    q, k, v, g = (_f64(case[x]) for x in ("q", "k", "v", "g"))
+    o_ref, lse_ref = oracle.forward(q, k, v, off, **kw)
+    _check_abs(_f64(out["o"]), o_ref, TOL_O, "O")
+    _check_lse(out["lse"].numpy(), lse_ref)
+    for name, ref in zip(("dq", "dk", "dv"), oracle.backward(q, k, v, off, g, **kw)):
+        _check_abs(_f64(out[name]), ref, TOL_GRAD_RAMP * np.abs(ref).max(), name)
+
+
+@pytest.mark.parametrize("name", list(RESCALE_CASES))
+def test_growing_scores_rescale_running_max(name):
+    """Scores that grow along the keys move every row's running maximum again and
+    again, in both 32-key halves of a block: the forward's rescale of O and of the
+    row sums (taken only when a maximum moves far enough) must keep O and the
+    log-sum-exp within the usual bars; the backward runs on the same outputs."""
+    lengths, h, d, bq, causal, lq, growth = RESCALE_CASES[name]
+    case = workloads.make_case(lengths, heads=h, head_dim=d, broadcast_q=bq, causal=causal,
+                               q_len=lq, seed=zlib.crc32(name.encode()) % 1000)
+    case = _ramp_keys(case, growth)
+    out = _run(case)
+    _compare_ramp(case, out)
+
+
+def test_late_spike_in_second_half_of_first_block():
+    """One key in the second 32-key half of the first block scores about 16 (base 2)
+    above the keys before it, more than the rescale threshold: the maximum moves
+    after the first half's probabilities were already formed.  Later keys fall back
+    to ordinary scores and keep some of the probability mass, so the gradients stay
+    well away from zero."""
+    case = workloads.make_case([300, 90, 40], heads=2, head_dim=128, broadcast_q=True,
+                               q_len=256, seed=5)
+    q = case["q"].float() + 1.0
+    k = case["k"].float()
+    per_unit = case["scale"] * 128 * 1.4426950408889634   # log2 score per unit added to a key
+    off = np.concatenate([[0], np.cumsum(case["lengths"])])
+    for b in range(len(case["lengths"])):
+        j = int(off[b]) + 37                      # key 37: second half of block 0
+        k[j] = k[j] + 16.0 / per_unit
+    case = dict(case)
+    case["q"] = q.to(torch.bfloat16)
+    case["k"] = k.to(torch.bfloat16)
+    out = _run(case)
+    _compare_ramp(case, out)

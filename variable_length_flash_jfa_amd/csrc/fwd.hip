@@ -20,7 +20,9 @@
 //    V^T operands come from the gfx950 transposing LDS read;
 //  * online softmax in the exp2 domain with a running max and a lane-local running
 //    sum (the two halves of a wave hold the two halves of a row's keys and are
-//    combined once, at the end);
+//    combined once, at the end), one step per 32-key half block, each half's
+//    softmax interleaved with the other half's MFMA chain; the max moves (and O is
+//    rescaled) only when it would grow by more than a factor 2^8;
 //  * the K/V loop is peeled: a branch-free bulk loop over fully visible blocks,
 //    then a masked loop over the tail block and the causal diagonal (section
 //    "Five changes unlocked the gains", item 5);
@@ -170,84 +172,138 @@ struct FwdKernel {
     lds_load_tile<D, NW>(vbuf(buf), BN, wave, lane, make_rsrc_sgpr(a.v + base, bytes), row_bytes);
   }
 
-  // One K/V block for this wave's 32 query rows.
+  // One K/V block for this wave's 32 query rows, as two 32-key halves, each its
+  // own online-softmax step.  The MFMA chains and the softmax of the other half
+  // are interleaved step by step, so that matrix and vector work overlap within
+  // the wave:
+  //   S0 = K0 Q^T                  (MFMA only)
+  //   S1 = K1 Q^T                  with the softmax of half 0
+  //   O^T += V0^T P0^T             with the softmax of half 1
+  //   O^T += V1^T P1^T             after half 1's rescale of O, if it made one
+  // Lazy rescaling: the running max of a row moves only when some row of the wave
+  // sees a score above its running max by more than 2^kLazyLog2 (a wave-uniform
+  // test), so O and the row sums are rescaled rarely; otherwise P is taken against
+  // the stale max and may reach 2^kLazyLog2, which O / l and the saved log-sum-exp
+  // divide out exactly.
+  static constexpr float kLazyLog2 = 8.f;
+  // Exponentials of softmax step k (1 <= k < NS) of a phase of NS MFMA steps cover
+  // elements [exp_lo(k), exp_lo(k + 1)) of the half (pairs, for the packed bf16
+  // conversion); step 0 takes the maximum, step 1 also the rescale test.
+  static constexpr int exp_lo(int k, int ns) { return k >= ns ? 16 : 2 * ((8 * (k - 1)) / (ns - 1)); }
+
+  template <bool MASKED>
+  __device__ __forceinline__ void mask_half(f32x16& s, int blk, int c) const {
+    if constexpr (MASKED) {
+      const int64_t i = i0 + c32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t j = (int64_t)blk * BN + 32 * c + 8 * (r >> 2) + 4 * hf + (r & 3);
+        bool vis = j < g.n;
+        if constexpr (CAUSAL) vis = vis && (j <= i);
+        s[r] = vis ? s[r] : -INFINITY;
+      }
+    }
+  }
+  __device__ __forceinline__ static float half_max(const f32x16& s) {
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    return mx;
+  }
+  // Rescale test of a half whose lane maximum is mx; returns the factor O must be
+  // multiplied by when `moved` (row sums are rescaled here).
+  __device__ __forceinline__ float rescale_test(float mx, bool& moved) {
+    const float mc = max_across_halves(mx) * a.scale_log2;
+    float alpha = 1.f;
+    moved = __builtin_amdgcn_ballot_w64(mc > mrun + kLazyLog2) != 0;
+    if (moved) {
+      const float mnew = fmaxf(mrun, mc);
+      alpha = fast_exp2(mrun - mnew);
+      mrun = mnew;
+      lsum *= alpha;
+    }
+    return alpha;
+  }
+  __device__ __forceinline__ void scale_acc(float alpha) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+  }
+  // P of elements [lo, hi) of a half: keys 16 kc + 8 (e / 4) + 4 (lane / 32) + e % 4
+  // of the half for element 8 kc + e.
+  __device__ __forceinline__ void half_exp(const f32x16& s, bf16x8 (&p)[2], int lo, int hi) {
+#pragma unroll
+    for (int r = lo; r < hi; ++r) {
+      const float pv = fast_exp2(fmaf(s[r], a.scale_log2, -mrun));
+      lsum += pv;
+      p[r >> 3][r & 7] = (bf16)pv;
+    }
+  }
+
   template <bool MASKED>
   __device__ __forceinline__ void compute_block(int buf, int blk) {
     const char* kb = kbuf(buf);
     const char* vb = vbuf(buf);
     const uint32_t krb = launder(k_row_base);
     const uint32_t vtb = launder(v_tr_base);
-    // S^T = K Q^T for the block's two 32-key halves as two interleaved MFMA chains
-    // (step i: k step i / 2, half i % 2).  Operands are read PF_S steps ahead of their
-    // MFMAs; the scheduling fences keep that pipeline as written.
-    auto kop = [&](int i) { return lds_read8(kb, row_read_addr(krb, i / 2) + 32 * (i % 2) * 2 * D); };
-    f32x16 s[2] = {zero16(), zero16()};
+    // K operand of half c, k step ks; V^T operand of O step i (keys 16 (i / DT), d
+    // tile i % DT).  Operands are read PF_S (PF_V) MFMA steps ahead; the scheduling
+    // fences keep that pipeline, and the interleaving, as written.
+    auto kop = [&](int i) { return lds_read8(kb, row_read_addr(krb, i % KS) + 32 * (i / KS) * 2 * D); };
+    auto vop = [&](int i) { return lds_operand_tr<D>(vb, vtb, 16 * (i / DT), 16 * (i / DT) + 8, i % DT); };
+    f32x16 s0 = zero16(), s1 = zero16();
+    bf16x8 p[2][2];
+    bf16x8 vr[PF_V + 1];
     {
       bf16x8 kr[PF_S + 1];
 #pragma unroll
       for (int i = 0; i < PF_S; ++i) kr[i] = kop(i);
+      // S0, then S1 with the softmax of half 0
+      float mx0 = 0.f;
 #pragma unroll
       for (int i = 0; i < 2 * KS; ++i) {
         if (i + PF_S < 2 * KS) kr[(i + PF_S) % (PF_S + 1)] = kop(i + PF_S);
-        s[i % 2] = mfma32(kr[i % (PF_S + 1)], qf[i / 2], s[i % 2]);
+        if (i + PF_V >= 2 * KS) vr[i + PF_V - 2 * KS] = vop(i + PF_V - 2 * KS);
+        if (i < KS) {
+          s0 = mfma32(kr[i % (PF_S + 1)], qf[i], s0);
+        } else {
+          s1 = mfma32(kr[i % (PF_S + 1)], qf[i - KS], s1);
+          const int k = i - KS;
+          if (k == 0) {
+            mask_half<MASKED>(s0, blk, 0);
+            mx0 = half_max(s0);
+          } else {
+            if (k == 1) {
+              bool moved;
+              const float alpha = rescale_test(mx0, moved);
+              if (moved) scale_acc(alpha);
+            }
+            half_exp(s0, p[0], exp_lo(k, KS), exp_lo(k + 1, KS));
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // the first V^T operands of O^T += V^T P^T (step i: keys 16 (i / DT), d tile
-    // i % DT) are read before the softmax
-    auto vop = [&](int i) { return lds_operand_tr<D>(vb, vtb, 16 * (i / DT), 16 * (i / DT) + 8, i % DT); };
-    bf16x8 vr[PF_V + 1];
-#pragma unroll
-    for (int i = 0; i < PF_V; ++i) vr[i] = vop(i);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (MASKED) {
-      const int64_t i = i0 + c32;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t j = (int64_t)blk * BN + 32 * c + 8 * (r >> 2) + 4 * hf + (r & 3);
-          bool vis = j < g.n;
-          if constexpr (CAUSAL) vis = vis && (j <= i);
-          s[c][r] = vis ? s[c][r] : -INFINITY;
-        }
-      }
-    }
-    float mx = s[0][0];
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[c][r]);
-    mx = max_across_halves(mx);
-    const float mnew = fmaxf(mrun, mx * a.scale_log2);
-    const float alpha = fast_exp2(mrun - mnew);
-    mrun = mnew;
-    lsum *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-
-    bf16x8 p[2][2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pv = fast_exp2(fmaf(s[c][8 * kc + e], a.scale_log2, -mnew));
-          lsum += pv;
-          p[c][kc][e] = (bf16)pv;
-        }
-      }
-    }
-    // keys 16 ckc + 4 (lane / 32) + e, and + 8, with ckc = 2 c + kc
-    __builtin_amdgcn_sched_barrier(0);
+    // O += P0 V0 with the softmax of half 1, then half 1's rescale of O, then
+    // O += P1 V1
+    float mx1 = 0.f, alpha1 = 1.f;
+    bool moved1 = false;
 #pragma unroll
     for (int i = 0; i < 4 * DT; ++i) {
       if (i + PF_V < 4 * DT) vr[(i + PF_V) % (PF_V + 1)] = vop(i + PF_V);
+      if (i == 2 * DT && moved1) scale_acc(alpha1);
       const int ckc = i / DT;
       acc[i % DT] = mfma32(vr[i % (PF_V + 1)], p[ckc / 2][ckc % 2], acc[i % DT]);
+      if (i < 2 * DT) {
+        if (i == 0) {
+          mask_half<MASKED>(s1, blk, 1);
+          mx1 = half_max(s1);
+        } else {
+          if (i == 1) alpha1 = rescale_test(mx1, moved1);
+          half_exp(s1, p[1], exp_lo(i, 2 * DT), exp_lo(i + 1, 2 * DT));
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
