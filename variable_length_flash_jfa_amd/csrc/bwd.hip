@@ -188,6 +188,11 @@ struct BwdKernel {
   uint32_t row_base;     // Q / dO row reads (add the tile offset)
   uint32_t k_row_base;   // this wave's K rows
   uint32_t tr4_base;     // Q^T / dO^T transposing reads (add the tile offset)
+  // One Q and one dO copy instruction per wave and query block: its lane offset is
+  // computed once (QLD); other shapes compute it at each copy.
+  static constexpr bool QLD = BQ / (64 / (D / 8)) == NW;
+  uint32_t q_voff;
+  uint32_t lds0;         // LDS address of smem
 
   __device__ BwdKernel(const BwdArgs& args, char* sm) : a(args), smem(sm) {
     lane = threadIdx.x & 63;
@@ -200,6 +205,8 @@ struct BwdKernel {
     row_base = row_read_base<D>(lane);
     k_row_base = row_base + (uint32_t)(OFF_K + 32 * wave * 2 * D);
     tr4_base = tr_read_base<D>(lane, 4 * hf);
+    if constexpr (QLD) q_voff = tile_load_voff<D>(wave, lane, (uint32_t)(rs * 2));
+    lds0 = lds_addr(smem);
   }
 
   // Lane parts of the dQ-product, dS^T and reduce-add addresses.  They are formed
@@ -250,10 +257,16 @@ struct BwdKernel {
     const uint32_t bytes = (uint32_t)rows * row_bytes;
     const bf16* qsrc = a.q + ((BCAST ? 0 : kv0_) + qi0) * rs + (int64_t)h_ * D;
     const bf16* gsrc = a.d_o + (grow0_ + qi0) * rs + (int64_t)h_ * D;
-    lds_load_tile<D, NW>(smem + OFF_Q + buf * QT_BYTES, BQ, wave, lane, make_rsrc_sgpr(qsrc, bytes),
-                         row_bytes);
-    lds_load_tile<D, NW>(smem + OFF_DO + buf * QT_BYTES, BQ, wave, lane, make_rsrc_sgpr(gsrc, bytes),
-                         row_bytes);
+    if constexpr (QLD) {
+      const uint32_t dst = lds0 + (uint32_t)(buf * QT_BYTES + wave * 1024);
+      lds_load16_at(make_rsrc_sgpr(qsrc, bytes), q_voff, dst + (uint32_t)OFF_Q);
+      lds_load16_at(make_rsrc_sgpr(gsrc, bytes), q_voff, dst + (uint32_t)OFF_DO);
+    } else {
+      lds_load_tile<D, NW>(smem + OFF_Q + buf * QT_BYTES, BQ, wave, lane, make_rsrc_sgpr(qsrc, bytes),
+                           row_bytes);
+      lds_load_tile<D, NW>(smem + OFF_DO + buf * QT_BYTES, BQ, wave, lane, make_rsrc_sgpr(gsrc, bytes),
+                           row_bytes);
+    }
     if (wave == NW - 1) {
       if constexpr (DIRECT) {   // the forward's LSE, one float per row
         const float* src = a.lse + (int64_t)h_ * a.rows + grow0_ + qi0;

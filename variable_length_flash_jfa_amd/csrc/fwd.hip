@@ -99,6 +99,8 @@ struct FwdKernel {
   float mrun, lsum;
   uint32_t k_row_base;   // lane part of K row reads (rows 32 c + lane % 32)
   uint32_t v_tr_base;    // lane part of V^T transposing reads (k offset 4 (lane / 32))
+  TileLoader<D, NW, BN> ld;   // this wave's share of a K or V block copy
+  uint32_t lds0;              // LDS address of smem
 
   __device__ FwdKernel(const FwdArgs& args, char* sm) : a(args), smem(sm) {
     lane = threadIdx.x & 63;
@@ -108,6 +110,8 @@ struct FwdKernel {
     rs = (int64_t)a.heads * D;
     k_row_base = row_read_base<D>(lane);
     v_tr_base = tr_read_base<D>(lane, 4 * hf);
+    ld.init(wave, lane, (uint32_t)(rs * 2));
+    lds0 = lds_addr(smem);
   }
 
   __device__ __forceinline__ char* kbuf(int buf) { return smem + (buf * 2 + 0) * TILE_BYTES; }
@@ -167,9 +171,8 @@ struct FwdKernel {
     const int64_t rows = max(min((int64_t)t.n - jb, (int64_t)BN), (int64_t)0);
     const uint32_t bytes = (uint32_t)(rows * rs * 2);
     const int64_t base = (t.kv0 + jb) * rs + (int64_t)t.h * D;
-    const uint32_t row_bytes = (uint32_t)(rs * 2);
-    lds_load_tile<D, NW>(kbuf(buf), BN, wave, lane, make_rsrc_sgpr(a.k + base, bytes), row_bytes);
-    lds_load_tile<D, NW>(vbuf(buf), BN, wave, lane, make_rsrc_sgpr(a.v + base, bytes), row_bytes);
+    ld.issue(make_rsrc_sgpr(a.k + base, bytes), lds0 + (uint32_t)((buf * 2 + 0) * TILE_BYTES));
+    ld.issue(make_rsrc_sgpr(a.v + base, bytes), lds0 + (uint32_t)((buf * 2 + 1) * TILE_BYTES));
   }
 
   // One K/V block for this wave's 32 query rows, as two 32-key halves, each its

@@ -287,6 +287,47 @@ __device__ __forceinline__ void lds_load_tile(char* tile, int nrows, int wave, i
   }
 }
 
+// The same copy for a tile of NROWS rows with a fixed row pitch, with each wave's
+// lane offsets computed once (one VGPR per instruction the wave issues, PER of
+// them) instead of at every call, and the LDS destination given as a 32-bit LDS
+// address.  Every wave issues exactly PER instructions (NROWS / RPI is a multiple
+// of NW), so the calls need no per-instruction test either.
+__device__ __forceinline__ void lds_load16_at(u32x4 r, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(lds)
+               : "memory", "m0");
+}
+// Lane part of the global offset of copy instruction u (rows u RPI .. u RPI + RPI - 1).
+template <int D>
+__device__ __forceinline__ uint32_t tile_load_voff(int u, int lane, uint32_t row_bytes) {
+  constexpr int CH = D / 8;
+  constexpr int RPI = 64 / CH;
+  const uint32_t r0 = (uint32_t)lane / CH;
+  const uint32_t base = r0 * row_bytes + ((((uint32_t)lane % CH) ^ (uint32_t)swz_mask<D>((int)r0)) << 4);
+  return (base ^ ((uint32_t)swz_mask<D>(u * RPI) << 4)) + (uint32_t)(u * RPI) * row_bytes;
+}
+template <int D, int NW, int NROWS>
+struct TileLoader {
+  static constexpr int CH = D / 8;
+  static constexpr int RPI = 64 / CH;
+  static constexpr int NI = NROWS / RPI;
+  static constexpr int PER = NI / NW;
+  static_assert(NI % NW == 0 && PER >= 1, "every wave issues the same number of instructions");
+  uint32_t voff[PER];
+  int wave;
+  __device__ __forceinline__ void init(int wave_, int lane, uint32_t row_bytes) {
+    wave = wave_;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) voff[k] = tile_load_voff<D>(wave + k * NW, lane, row_bytes);
+  }
+  // Copies the tile whose first row `r` addresses into the LDS tile at `lds`.
+  __device__ __forceinline__ void issue(u32x4 r, uint32_t lds) const {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) lds_load16_at(r, voff[k], lds + (uint32_t)((wave + k * NW) * 1024));
+  }
+};
+
 // ---- offsets -------------------------------------------------------------------
 
 __device__ __forceinline__ int64_t load_offset(const void* offsets, int is64, int64_t i) {
