@@ -115,6 +115,9 @@ SMALL_CASES = {
     "single_tile_d128_nw4": ([128, 100, 110, 128, 90, 97], 2, 128, False, False, 0),
     "single_tile_d64_nw4_causal": ([128, 120, 99, 128, 70], 2, 64, False, True, 0),
     "single_tile_d64_nw2": ([64, 3, 64, 50, 17], 2, 64, False, False, 0),
+    # self mode with a mean length of at least 512: 256-row forward tiles of eight waves
+    "self_d128_causal_long": ([900, 1200, 64, 700, 1], 2, 128, False, True, 0),
+    "self_d64_long": ([600, 1000, 3, 700], 2, 64, False, False, 0),
 }
 
 

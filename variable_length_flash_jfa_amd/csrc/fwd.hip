@@ -96,7 +96,7 @@ struct FwdKernel {
   int64_t out_row0;    // first output row of the sequence
   bf16x8 qf[KS];
   f32x16 acc[DT];
-  float mrun, lsum;
+  float mrun, lsum, lsum2;   // row sums of even and odd P elements (two short chains)
   uint32_t k_row_base;   // lane part of K row reads (rows 32 c + lane % 32)
   uint32_t v_tr_base;    // lane part of V^T transposing reads (k offset 4 (lane / 32))
   TileLoader<D, NW, BN> ld;   // this wave's share of a K or V block copy
@@ -176,23 +176,24 @@ struct FwdKernel {
   }
 
   // One K/V block for this wave's 32 query rows, as two 32-key halves, each its
-  // own online-softmax step.  The MFMA chains and the softmax of the other half
-  // are interleaved step by step, so that matrix and vector work overlap within
-  // the wave:
+  // own online-softmax step.  A wave's vector work runs under its own MFMA chains
+  // (the matrix cores execute an MFMA while the wave issues independent vector
+  // instructions), so the softmax is spread over the block's four MFMA phases:
   //   S0 = K0 Q^T                  (MFMA only)
-  //   S1 = K1 Q^T                  with the softmax of half 0
-  //   O^T += V0^T P0^T             with the softmax of half 1
-  //   O^T += V1^T P1^T             after half 1's rescale of O, if it made one
+  //   S1 = K1 Q^T                  half 0: mask, maximum, rescale test, exp2 of
+  //                                its first 12 keys (S1 as two independent chains)
+  //   O^T += V0^T P0^T             half 0: last 4 keys (their P is needed from the
+  //                                second half of this phase on); half 1: mask,
+  //                                maximum, rescale test, first 16 keys
+  //   O^T += V1^T P1^T             half 1: last 16 keys (needed from the second
+  //                                half of this phase on), after half 1's rescale
+  //                                of O, if it made one
   // Lazy rescaling: the running max of a row moves only when some row of the wave
   // sees a score above its running max by more than 2^kLazyLog2 (a wave-uniform
   // test), so O and the row sums are rescaled rarely; otherwise P is taken against
   // the stale max and may reach 2^kLazyLog2, which O / l and the saved log-sum-exp
   // divide out exactly.
   static constexpr float kLazyLog2 = 8.f;
-  // Exponentials of softmax step k (1 <= k < NS) of a phase of NS MFMA steps cover
-  // elements [exp_lo(k), exp_lo(k + 1)) of the half (pairs, for the packed bf16
-  // conversion); step 0 takes the maximum, step 1 also the rescale test.
-  static constexpr int exp_lo(int k, int ns) { return k >= ns ? 16 : 2 * ((8 * (k - 1)) / (ns - 1)); }
 
   template <bool MASKED>
   __device__ __forceinline__ void mask_half(f32x16& s, int blk, int c) const {
@@ -207,11 +208,13 @@ struct FwdKernel {
       }
     }
   }
+  // As a tree of depth three (a serial chain would hold the wave for its whole
+  // latency while the MFMAs of the other half wait behind it).
   __device__ __forceinline__ static float half_max(const f32x16& s) {
-    float mx = s[0];
+    float m[5];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    return mx;
+    for (int k = 0; k < 5; ++k) m[k] = fmaxf(fmaxf(s[3 * k], s[3 * k + 1]), s[3 * k + 2]);
+    return fmaxf(fmaxf(fmaxf(m[0], m[1]), m[2]), fmaxf(fmaxf(m[3], m[4]), s[15]));
   }
   // Rescale test of a half whose lane maximum is mx; returns the factor O must be
   // multiplied by when `moved` (row sums are rescaled here).
@@ -224,6 +227,7 @@ struct FwdKernel {
       alpha = fast_exp2(mrun - mnew);
       mrun = mnew;
       lsum *= alpha;
+      lsum2 *= alpha;
     }
     return alpha;
   }
@@ -239,10 +243,18 @@ struct FwdKernel {
 #pragma unroll
     for (int r = lo; r < hi; ++r) {
       const float pv = fast_exp2(fmaf(s[r], a.scale_log2, -mrun));
-      lsum += pv;
+      (r & 1 ? lsum2 : lsum) += pv;
       p[r >> 3][r & 7] = (bf16)pv;
     }
   }
+
+  // Softmax units, coded 32 half + 8 kind + pair: kind 0 mask and maximum, 1 rescale
+  // test, 2 exp2 of elements 2 pair and 2 pair + 1.  Phase B runs units 0..7 over
+  // the KS MFMA steps of S1, phase C units 0..7 over the 2 DT steps of O += P0 V0,
+  // phase D units 0..3 over the first DT steps of O += P1 V1.
+  static constexpr int unit_b(int u) { return u < 2 ? 8 * u : 16 + (u - 2); }
+  static constexpr int unit_c(int u) { return u < 2 ? 16 + 6 + u : (u < 4 ? 32 + 8 * (u - 2) : 48 + (u - 4)); }
+  static constexpr int unit_d(int u) { return 48 + 4 + u; }
 
   template <bool MASKED>
   __device__ __forceinline__ void compute_block(int buf, int blk) {
@@ -255,15 +267,41 @@ struct FwdKernel {
     // fences keep that pipeline, and the interleaving, as written.
     auto kop = [&](int i) { return lds_read8(kb, row_read_addr(krb, i % KS) + 32 * (i / KS) * 2 * D); };
     auto vop = [&](int i) { return lds_operand_tr<D>(vb, vtb, 16 * (i / DT), 16 * (i / DT) + 8, i % DT); };
-    f32x16 s0 = zero16(), s1 = zero16();
+    // S1 runs as two chains (even and odd k steps) so that its MFMAs do not wait on
+    // each other while half 0's softmax is issued between them; they are added
+    // before half 1's maximum.
+    f32x16 s0 = zero16(), s1 = zero16(), s1b = zero16();
     bf16x8 p[2][2];
     bf16x8 vr[PF_V + 1];
+    float mx0 = 0.f, mx1 = 0.f, alpha1 = 1.f;
+    bool moved1 = false;
+    auto unit = [&](int code) {
+      const int c = code >> 5, kind = (code >> 3) & 3, pair = code & 7;
+      f32x16& s = c == 0 ? s0 : s1;
+      if (kind == 0) {
+        if (c == 1) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s1[r] += s1b[r];
+        }
+        mask_half<MASKED>(s, blk, c);
+        (c == 0 ? mx0 : mx1) = half_max(s);
+      } else if (kind == 1) {
+        if (c == 0) {
+          bool moved;
+          const float alpha = rescale_test(mx0, moved);
+          if (moved) scale_acc(alpha);
+        } else {   // applied once the O += P0 V0 products are issued
+          alpha1 = rescale_test(mx1, moved1);
+        }
+      } else {
+        half_exp(s, p[c], 2 * pair, 2 * pair + 2);
+      }
+    };
     {
       bf16x8 kr[PF_S + 1];
 #pragma unroll
       for (int i = 0; i < PF_S; ++i) kr[i] = kop(i);
-      // S0, then S1 with the softmax of half 0
-      float mx0 = 0.f;
+      // S0, then S1 with phase B
 #pragma unroll
       for (int i = 0; i < 2 * KS; ++i) {
         if (i + PF_S < 2 * KS) kr[(i + PF_S) % (PF_S + 1)] = kop(i + PF_S);
@@ -271,27 +309,19 @@ struct FwdKernel {
         if (i < KS) {
           s0 = mfma32(kr[i % (PF_S + 1)], qf[i], s0);
         } else {
-          s1 = mfma32(kr[i % (PF_S + 1)], qf[i - KS], s1);
           const int k = i - KS;
-          if (k == 0) {
-            mask_half<MASKED>(s0, blk, 0);
-            mx0 = half_max(s0);
+          if (k & 1) {
+            s1b = mfma32(kr[i % (PF_S + 1)], qf[k], s1b);
           } else {
-            if (k == 1) {
-              bool moved;
-              const float alpha = rescale_test(mx0, moved);
-              if (moved) scale_acc(alpha);
-            }
-            half_exp(s0, p[0], exp_lo(k, KS), exp_lo(k + 1, KS));
+            s1 = mfma32(kr[i % (PF_S + 1)], qf[k], s1);
           }
+#pragma unroll
+          for (int u = k * 8 / KS; u < (k + 1) * 8 / KS; ++u) unit(unit_b(u));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // O += P0 V0 with the softmax of half 1, then half 1's rescale of O, then
-    // O += P1 V1
-    float mx1 = 0.f, alpha1 = 1.f;
-    bool moved1 = false;
+    // O += P0 V0 with phase C, half 1's rescale of O, then O += P1 V1 with phase D
 #pragma unroll
     for (int i = 0; i < 4 * DT; ++i) {
       if (i + PF_V < 4 * DT) vr[(i + PF_V) % (PF_V + 1)] = vop(i + PF_V);
@@ -299,13 +329,12 @@ struct FwdKernel {
       const int ckc = i / DT;
       acc[i % DT] = mfma32(vr[i % (PF_V + 1)], p[ckc / 2][ckc % 2], acc[i % DT]);
       if (i < 2 * DT) {
-        if (i == 0) {
-          mask_half<MASKED>(s1, blk, 1);
-          mx1 = half_max(s1);
-        } else {
-          if (i == 1) alpha1 = rescale_test(mx1, moved1);
-          half_exp(s1, p[1], exp_lo(i, 2 * DT), exp_lo(i + 1, 2 * DT));
-        }
+#pragma unroll
+        for (int u = i * 8 / (2 * DT); u < (i + 1) * 8 / (2 * DT); ++u) unit(unit_c(u));
+      } else if (i < 3 * DT) {
+        const int k = i - 2 * DT;
+#pragma unroll
+        for (int u = k * 4 / DT; u < (k + 1) * 4 / DT; ++u) unit(unit_d(u));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -360,6 +389,7 @@ struct FwdKernel {
     for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
     mrun = kNegBig;
     lsum = 0.f;
+    lsum2 = 0.f;
 
     const int nblk = num_blocks(g);
     int nfull = (int)(g.n / BN);
@@ -379,7 +409,7 @@ struct FwdKernel {
     between();
 
     // epilogue
-    const float lt = sum_across_halves(lsum);
+    const float lt = sum_across_halves(lsum + lsum2);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     char* slot = smem + ((pb + nblk + 1) & 1) * (2 * TILE_BYTES) + wave * SLOT_BYTES;
     store_acc_rows<D, EPI_PASSES>(acc, inv, slot, a.o + ((out_row0 + i0) * rs + (int64_t)g.h * D), rs,
@@ -511,6 +541,8 @@ hipError_t launch_d(const Problem& p, const FwdArgs& a, hipStream_t s) {
     return launch_inst<D, 2, true, false>(a, s, max_tiles);
   }
   const int64_t max_tiles = fwd_max_items(p) * p.heads;
+  if (nw == 8)
+    return p.causal ? launch_inst<D, 8, false, true>(a, s, max_tiles) : launch_inst<D, 8, false, false>(a, s, max_tiles);
   if (p.causal) return launch_inst<D, 4, false, true>(a, s, max_tiles);
   return launch_inst<D, 4, false, false>(a, s, max_tiles);
 }
@@ -523,7 +555,9 @@ int fwd_waves(const Problem& p) {
     const int64_t mean = p.batch > 0 ? p.total_kv / p.batch : 0;
     return mean <= 96 ? 2 : (mean >= 384 ? 8 : 4);
   }
-  if (!p.broadcast) return 4;
+  // Self mode: 256-row tiles when sequences are long on average, so that the query
+  // tiles of a sequence read its K/V half as often; 128-row tiles otherwise.
+  if (!p.broadcast) return (p.batch > 0 && p.total_kv / p.batch >= 512) ? 8 : 4;
   if (p.q_len > 128) return 8;
   if (p.q_len > 64) return 4;
   return 2;
