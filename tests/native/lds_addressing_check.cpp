@@ -36,8 +36,9 @@ int check() {
       }
     }
   }
-  // lds_load_tile: lane offset (base ^ mask(u RPI) << 4) + u RPI row_bytes equals
-  // row * row_bytes + swz_chunk(row, slot) * 16 for row = u RPI + lane / CH
+  // direct-to-LDS copies: lane offset of copy instruction u (lds_load_tile and
+  // tile_load_voff) equals row * row_bytes + swz_chunk(row, slot) * 16 for row =
+  // u RPI + lane / CH (lane % CH is the LDS chunk slot the lane fills)
   {
     constexpr int CH = D / 8, RPI = 64 / CH;
     for (uint32_t row_bytes : {2u * D, 4u * D, 8u * D, 64u * D})
@@ -49,6 +50,7 @@ int check() {
           const int row = u * RPI + lane / CH;
           const uint32_t ref = (uint32_t)row * row_bytes + (uint32_t)swz_chunk<D>(row, lane % CH) * 16u;
           if (fast != ref) ++bad;
+          if (tile_load_voff<D>(u, lane, row_bytes) != ref) ++bad;
         }
       }
   }

@@ -300,7 +300,7 @@ __device__ __forceinline__ void lds_load16_at(u32x4 r, uint32_t voff, uint32_t l
 }
 // Lane part of the global offset of copy instruction u (rows u RPI .. u RPI + RPI - 1).
 template <int D>
-__device__ __forceinline__ uint32_t tile_load_voff(int u, int lane, uint32_t row_bytes) {
+__host__ __device__ __forceinline__ uint32_t tile_load_voff(int u, int lane, uint32_t row_bytes) {
   constexpr int CH = D / 8;
   constexpr int RPI = 64 / CH;
   const uint32_t r0 = (uint32_t)lane / CH;
