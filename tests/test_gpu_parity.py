@@ -118,6 +118,8 @@ SMALL_CASES = {
     # self mode with a mean length of at least 512: 256-row forward tiles of eight waves
     "self_d128_causal_long": ([900, 1200, 64, 700, 1], 2, 128, False, True, 0),
     "self_d64_long": ([600, 1000, 3, 700], 2, 64, False, False, 0),
+    "self_d128_causal_long_empty": ([900, 0, 1200, 1], 2, 128, False, True, 0),
+    "self_d64_causal_long_empty": ([700, 0, 900], 3, 64, False, True, 0),
 }
 
 
