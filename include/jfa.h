@@ -154,14 +154,25 @@ jfa_status_t jfa_bwd_rope(const void* q, const void* k, const void* v,
                           void* dq, void* dk, void* dv,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Block sizes of the block-sparse top-k forward.  They are constants of the method
+ * as this library defines it (the pages name query blocks and key/value blocks but
+ * give no sizes); the kernels are built to them, not the other way round.
+ *   JFA_SPARSE_KEY_BLOCK              keys per key/value block
+ *   JFA_SPARSE_QUERY_BLOCK_BROADCAST  rows of the broadcast query per query block
+ *   JFA_SPARSE_QUERY_BLOCK_SELF       rows of a sequence per query block (self mode) */
+#define JFA_SPARSE_KEY_BLOCK 64
+#define JFA_SPARSE_QUERY_BLOCK_BROADCAST 256
+#define JFA_SPARSE_QUERY_BLOCK_SELF 128
+
 /* Block-sparse top-k forward (the JFA news page and the reading note name a
  * block-sparse fork of the kernel: a scoring step picks the top k key/value blocks
  * for each query block, and attention runs only over those blocks).  Non-causal
  * modes only (causal gives JFA_ERR_UNSUPPORTED).
- *   Key blocks: 64 consecutive keys of a sequence (the last may be partial).
- *   Query blocks: 256 consecutive rows of the broadcast query sequence, or 128
- *     consecutive rows of the sequence itself in self mode (the rows one workgroup
- *     of the forward covers).
+ *   Key blocks: JFA_SPARSE_KEY_BLOCK (64) consecutive keys of a sequence (the last
+ *     may be partial).
+ *   Query blocks: JFA_SPARSE_QUERY_BLOCK_BROADCAST (256) consecutive rows of the
+ *     broadcast query sequence, or JFA_SPARSE_QUERY_BLOCK_SELF (128) consecutive
+ *     rows of the sequence itself in self mode (the last may be partial).
  *   Score of (query block, key block), per head: softmax_scale * (mean query row) .
  *     (mean key row), computed in fp32.
  *   Selection: the topk highest scores (ties to the lower block index); a sequence
@@ -172,7 +183,8 @@ jfa_status_t jfa_bwd_rope(const void* q, const void* k, const void* v,
  *     query block's selection in ascending order, -1 padded, where
  *     Q = jfa_fwd_sparse_query_blocks(batch, q_len, total_kv, broadcast_q) and the
  *     query block of sequence b, block m is b * ceil(q_len / 256) + m (broadcast) or
- *     sum over b' < b of ceil(n_b' / 128), plus m (self mode).
+ *     sum over b' < b of ceil(n_b' / 128), plus m (self mode), with the block sizes
+ *     above.
  * Workspace: jfa_fwd_sparse_workspace_size(...) bytes (0 for invalid sizes or topk).
  * Other rules as jfa_fwd. */
 size_t jfa_fwd_sparse_workspace_size(int64_t batch, int64_t num_heads, int64_t head_dim, int64_t q_len,

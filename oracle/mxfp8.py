@@ -35,7 +35,10 @@ against its field definition and known values; rounding against brute force over
 all finite values; the scale rule's minimality; scores that are integers in base 2
 reduce the forward to the dense oracle exactly; the P quantization error bound
 against the dense oracle on the dequantized inputs; integer shifts of the scores
-leave the result unchanged.
+leave the result unchanged.  The slack is pinned by brute force over the E4M3
+values: exactly 0 on rows with no decision near a tie or a scale boundary; every
+flagged decision taken the other way (singly and all together) moves O by no more
+than it; and a row with a single near-tie gets exactly that flip's effect.
 """
 from __future__ import annotations
 

@@ -12,8 +12,9 @@ Readings where the pages are silent (each also listed in the design notes):
 
 * Key/value blocks are 64 consecutive keys of a sequence (the last one may be
   partial); query blocks are 256 consecutive rows of the broadcast query sequence,
-  or 128 consecutive rows of the sequence itself in self-attention (the query rows
-  one workgroup of the forward covers in each mode).
+  or 128 consecutive rows of the sequence itself in self-attention (the last one
+  may be partial).  These sizes are fixed constants of the method as read here;
+  the pages give none.
 * The score of (query block m, key block j) for a head is
   c * mean(Q rows of m) . mean(K rows of j): the dot product of the mean query row
   and the mean key row, times the softmax scale c.
@@ -30,8 +31,10 @@ and check that selection against these fp64 scores up to near-ties.
 
 Parity status: pinned by CPU tests (tests/test_oracle.py): k at least the number
 of blocks reduces to the dense oracle; a fixed selection equals a padded dense
-torch reference with the matching block mask; pooled scores against explicit
-loops on a tiny input; the selection against a brute-force sort.
+torch reference with the matching block mask; every block score equals the mean
+of the exact scores c q_i . k_j over the block's rows and keys (linearity),
+computed from the full score matrix, partial last blocks included; the selection
+against a brute-force sort.
 """
 from __future__ import annotations
 

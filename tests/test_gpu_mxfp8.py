@@ -108,6 +108,9 @@ def _mx_run(jfa, q, k, v, off, bq, causal, scale):
 def _check_o(got, ref, slack):
     """got [rows, H, D] bf16 tensor; ref fp64 [rows, H, D]; slack [H, rows]."""
     got = _f64(got)
+    nz = slack[slack > 0]
+    print(f"slack: largest {slack.max() if slack.size else 0.0:.3e}, rows with slack > 0: {nz.size} of "
+          f"{slack.size}", flush=True)
     _, e = np.frexp(np.maximum(np.abs(got), np.abs(ref)))
     half_ulp = np.ldexp(1.0, e - 9)
     excess = np.abs(got - ref) - half_ulp - slack.T[:, :, None]

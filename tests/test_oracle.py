@@ -521,6 +521,37 @@ def test_block_scores_by_explicit_loops():
             assert abs(got[m, j] - scale * sum(a * b for a, b in zip(qm, km))) <= 1e-12
 
 
+@pytest.mark.parametrize("nq,nk,qblk", [(200, 130, 128), (256, 64, 256), (300, 1, 256), (17, 200, 128)])
+def test_block_scores_are_means_of_exact_scores(nq, nk, qblk):
+    """By linearity, c * mean(q rows) . mean(k rows) equals the mean over the block of
+    the exact scores c * q_i . k_j.  The exact scores come from the full score matrix
+    (one product of all rows), so a wrong divisor for a partial block, a sum in place
+    of a mean, a dropped scale or a shifted block boundary fails here."""
+    rng = np.random.default_rng(nq * 1000 + nk)
+    d, scale = 16, 0.37
+    qb, kb = rng.standard_normal((nq, d)), rng.standard_normal((nk, d))
+    got = oracle.sparse.block_scores(qb, kb, scale, qblk)
+    s = scale * (qb @ kb.T)                      # every exact score
+    kv = oracle.sparse.KV_BLOCK
+    nqb, nkb = -(-nq // qblk), -(-nk // kv)
+    assert got.shape == (nqb, nkb)
+    for m in range(nqb):
+        for j in range(nkb):
+            blk = s[m * qblk:min((m + 1) * qblk, nq), j * kv:min((j + 1) * kv, nk)]
+            assert abs(got[m, j] - blk.mean()) <= 1e-12 * max(1.0, np.abs(blk).max())
+
+
+def test_sparse_block_sizes_match_the_library_header():
+    """The oracle's block sizes are the ones the C ABI documents as the method's."""
+    import re
+    with open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "jfa.h")) as f:
+        text = f.read()
+    val = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (JFA_SPARSE_\w+) (\d+)", text)}
+    assert val == {"JFA_SPARSE_KEY_BLOCK": oracle.sparse.KV_BLOCK,
+                   "JFA_SPARSE_QUERY_BLOCK_BROADCAST": oracle.sparse.Q_BLOCK_BROADCAST,
+                   "JFA_SPARSE_QUERY_BLOCK_SELF": oracle.sparse.Q_BLOCK_SELF}
+
+
 def test_top_k_selection_by_brute_force():
     scores = np.array([[0.5, 2.0, -1.0, 2.0, 0.1],
                        [3.0, 3.0, 3.0, 0.0, -2.0],

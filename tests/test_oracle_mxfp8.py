@@ -233,3 +233,137 @@ def test_worked_example_by_hand():
     assert np.allclose(o[0], [0.6875 / l, 0.40625 / l], rtol=1e-7, atol=0)
     assert np.allclose(o[0], [0.6097264, 0.3602928], rtol=0, atol=1e-6)
     assert abs(lse2[0] - (1 + math.log2(l))) <= 1e-7
+
+
+# ---- the slack (sensitivity of P's rounding decisions) ----------------------------
+
+def _e4m3_positive_values():
+    """Finite non-negative E4M3 values from the field definition: subnormals k 2^-9
+    (k = 0..7) and normals (1 + m / 8) 2^(e - 7), e = 1..15, except e = 15, m = 7."""
+    vals = [k * 2.0 ** -9 for k in range(8)]
+    vals += [(1 + m / 8) * 2.0 ** (e - 7) for e in range(1, 16) for m in range(8) if not (e == 15 and m == 7)]
+    return np.array(sorted(vals))
+
+
+def _decisions(x, rel=2.0 ** -12):
+    """Brute-force rounding decisions of P for one row of fp32 base-2 scores x: p in
+    fp32, block exponents e by search, y = p / 2^e, and for every element its two
+    E4M3 neighbours; flags near a rounding midpoint, and blocks whose maximum is near
+    a scale boundary (448 2^e or 448 2^(e - 1))."""
+    table = _e4m3_positive_values()
+    x = np.asarray(x, dtype=np.float32)
+    m = np.float32(np.ceil(np.float64(x.max())))
+    p = np.exp2((x - m).astype(np.float32)).astype(np.float32).astype(np.float64)
+    n = len(p)
+    e = np.zeros(n, dtype=np.int64)
+    edge = np.zeros(n, dtype=bool)
+    for j0 in range(0, n, 32):
+        blk = p[j0:j0 + 32]
+        amax = blk.max()
+        ee = -127
+        while amax > 448.0 * 2.0 ** ee:
+            ee += 1
+        e[j0:j0 + 32] = ee
+        near = lambda a, b: abs(a - b) <= rel * max(abs(a), abs(b))   # noqa: E731
+        edge[j0:j0 + 32] = (near(amax, 448.0 * 2.0 ** ee) or near(amax, 448.0 * 2.0 ** (ee - 1))) and amax > 0
+    y = p / np.ldexp(1.0, e)
+    hi_i = np.searchsorted(table, y, side="left")
+    lo = table[np.maximum(hi_i - 1, 0)]
+    hi = table[np.minimum(hi_i, len(table) - 1)]
+    lo = np.where(table[np.minimum(hi_i, len(table) - 1)] == y, y, lo)   # exactly representable
+    mid = 0.5 * (lo + hi)
+    tie = (np.abs(y - mid) <= rel * np.maximum(np.abs(y), np.abs(mid))) & (p > 0) & (lo != hi)
+    return p, e, y, lo, hi, tie, edge & (p > 0)
+
+
+def _o_from(pd, v, l):
+    return (pd @ v) / l
+
+
+def test_slack_is_zero_exactly_when_no_decision_is_near_a_tie():
+    """Random rows: the slack is exactly 0 on every row whose rounding decisions are
+    all clear of a tie and of a scale boundary (found by brute force over the E4M3
+    values), and positive on every row with such a decision."""
+    rng = np.random.default_rng(11)
+    n, d = 70, 8
+    v = rng.standard_normal((n, d))
+    rows = [rng.standard_normal(n).astype(np.float32) * 3 for _ in range(40)]
+    # rows with a planted near-tie: p = 2^(x - m) lands within fp32 rounding of 1.0625 / 2
+    for k in range(6):
+        x = rng.standard_normal(n).astype(np.float32) - 4.0
+        x[k] = np.float32(np.log2(1.0625))
+        rows.append(x)
+    zero_rows = flagged_rows = 0
+    for x in rows:
+        _, _, slack = mx.attend_base2(x[None, :], v)
+        _, _, _, _, _, tie, edge = _decisions(x)
+        if tie.any() or edge.any():
+            assert slack[0] > 0
+            flagged_rows += 1
+        else:
+            assert slack[0] == 0.0
+            zero_rows += 1
+    assert zero_rows >= 30 and flagged_rows >= 6
+
+
+def test_slack_bounds_every_flipped_decision():
+    """Every flagged decision taken the other way (the other E4M3 neighbour for a
+    near-tie, the neighbouring block exponent for a near-boundary scale), one at a
+    time and all together, moves O by no more than the slack, and a flip of a
+    near-tie does move O."""
+    rng = np.random.default_rng(12)
+    n, d = 90, 6
+    v = rng.standard_normal((n, d))
+    x = (rng.standard_normal(n) - 3.0).astype(np.float32)
+    x[3] = np.float32(np.log2(1.0625))          # near-tie in block 0 (p close to 0.53125)
+    x[40] = np.float32(np.log2(1.0625))         # near-tie in block 1
+    x[70] = np.float32(np.log2(1.8125))         # another binade's midpoint (y near 464 / 2 ...)
+    o, _, slack = mx.attend_base2(x[None, :], v)
+    p, e, y, lo, hi, tie, edge = _decisions(x)
+    assert tie.sum() >= 2
+    scale = np.ldexp(1.0, e)
+    q = np.where(np.abs(y - lo) < np.abs(y - hi), lo, hi)
+    q = np.where(np.abs(y - lo) == np.abs(y - hi), mx.e4m3_round(y), q)
+    pd = q * scale
+    l = p.sum()
+    np.testing.assert_allclose(_o_from(pd, v, l), o[0], rtol=0, atol=1e-12)   # the same decisions
+    flips = []
+    for j in np.nonzero(tie)[0]:
+        alt = pd.copy()
+        alt[j] = (lo[j] if q[j] == hi[j] else hi[j]) * scale[j]
+        flips.append(alt)
+    for j0 in sorted({int(j) // 32 * 32 for j in np.nonzero(edge)[0]}):
+        for de in (-1, 1):
+            alt = pd.copy()
+            s2 = np.ldexp(1.0, e[j0] + de)
+            yy = np.minimum(p[j0:j0 + 32] / s2, 448.0)
+            alt[j0:j0 + 32] = mx.e4m3_round(yy) * s2
+            flips.append(alt)
+    assert flips
+    moved = 0.0
+    for alt in flips:
+        delta = np.abs(_o_from(alt, v, l) - o[0]).max()
+        assert delta <= slack[0] * (1 + 1e-9)
+        moved = max(moved, delta)
+    assert moved > 0
+    all_flipped = pd.copy()
+    for j in np.nonzero(tie)[0]:
+        all_flipped[j] = (lo[j] if q[j] == hi[j] else hi[j]) * scale[j]
+    assert np.abs(_o_from(all_flipped, v, l) - o[0]).max() <= slack[0] * (1 + 1e-9)
+
+
+def test_slack_of_a_single_tie_is_that_flip_exactly():
+    """With one near-tie and no near-boundary scale in a row, flipping that one
+    decision moves O by exactly the slack (so the slack is not loose)."""
+    rng = np.random.default_rng(13)
+    n, d = 50, 5
+    v = rng.standard_normal((n, d))
+    x = (rng.standard_normal(n) - 5.0).astype(np.float32)
+    x[7] = np.float32(np.log2(1.0625))
+    _, _, slack = mx.attend_base2(x[None, :], v)
+    p, e, y, lo, hi, tie, edge = _decisions(x)
+    assert tie.sum() == 1 and not edge.any()
+    j = int(np.nonzero(tie)[0][0])
+    step = (hi[j] - lo[j]) * np.ldexp(1.0, e[j])
+    delta = step * np.abs(v[j]).max() / p.sum()
+    assert abs(slack[0] - delta) <= 1e-12 * delta

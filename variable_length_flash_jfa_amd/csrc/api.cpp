@@ -33,6 +33,9 @@ jfa_status_t fail(jfa_status_t st, const char* fmt, ...) {
 jfa_status_t hip_fail(hipError_t e, const char* what) {
   return fail(JFA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
+jfa_status_t hip_fail(hipError_t e, const char* fn, const char* what) {
+  return fail(JFA_ERR_HIP, "%s: %s: %s", fn, what, hipGetErrorString(e));
+}
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -316,20 +319,20 @@ jfa_status_t bwd_impl(const char* fn, const void* q, const void* k, const void* 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int sched = g_schedule.load();
   hipError_t e = timed_launch("plan_bwd", s, [&] { return jfa::launch_plan_bwd(p, plan, sched, s); });
-  if (e != hipSuccess) return hip_fail(e, "jfa_bwd: plan launch");
+  if (e != hipSuccess) return hip_fail(e, fn, "plan launch");
   e = timed_launch("bwd_pre", s, [&] {
     return jfa::launch_bwd_pre(p, o, d_o, lse, rowstat, dq_acc, acc_elems, plan.meta, s);
   });
-  if (e != hipSuccess) return hip_fail(e, "jfa_bwd: delta launch");
+  if (e != hipSuccess) return hip_fail(e, fn, "delta launch");
   if (p.total_kv > 0) {
     e = timed_launch("bwd", s, [&] {
       return jfa::launch_bwd(p, plan, sched, rowstat, lse, d_o, dq_acc, dq, dk, dv, rope, s);
     });
-    if (e != hipSuccess) return hip_fail(e, "jfa_bwd: kernel launch");
+    if (e != hipSuccess) return hip_fail(e, fn, "kernel launch");
   }
   e = timed_launch("dq_finalize", s,
                    [&] { return jfa::launch_dq_finalize(p, dq_acc, dq, plan.meta, rope, s); });
-  if (e != hipSuccess) return hip_fail(e, "jfa_bwd: dq finalize launch");
+  if (e != hipSuccess) return hip_fail(e, fn, "dq finalize launch");
   return JFA_OK;
 }
 

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "jfa.h"
+
 namespace jfa {
 
 // Forward tile geometry.  A forward tile is (sequence, block of BM query rows, head);
@@ -36,11 +38,15 @@ struct Problem {
   int mx = 0;         // the MXFP8 forward (its own workgroup size in self mode)
 };
 
-// Block-sparse forward: key blocks of kFwdBN keys; query blocks of the rows one
-// forward workgroup covers: 256 rows of the broadcast query (eight waves), 128 rows
-// of a sequence in self mode (four waves).
-constexpr int kSparseQBBroadcast = 256;
-constexpr int kSparseQBSelf = 128;
+// Block-sparse forward: the method's block sizes (include/jfa.h).  The sparse
+// forward kernel takes one query block per workgroup (32 rows per wave), so these
+// fix its wave counts, and its key blocks are the dense forward's K/V blocks.
+constexpr int kSparseQBBroadcast = JFA_SPARSE_QUERY_BLOCK_BROADCAST;
+constexpr int kSparseQBSelf = JFA_SPARSE_QUERY_BLOCK_SELF;
+static_assert(JFA_SPARSE_KEY_BLOCK == kFwdBN, "sparse key blocks are the forward's K/V blocks");
+static_assert(kSparseQBBroadcast % 32 == 0 && kSparseQBBroadcast / 32 <= 8 && kSparseQBSelf % 32 == 0 &&
+                  kSparseQBSelf / 32 <= 8,
+              "a sparse query block must be whole 32-row waves of one workgroup");
 inline int sparse_qb(const Problem& p) { return p.broadcast ? kSparseQBBroadcast : kSparseQBSelf; }
 constexpr int kSparseMaxTopk = 64;
 
