@@ -106,6 +106,28 @@ jfa_status_t jfa_fwd(const void* q, const void* k, const void* v,
                      void* o, float* lse,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Forward pass that allocates nothing, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Arguments, results and errors are those of jfa_fwd without the
+ * workspace: the tile plan lives in a device array of JFA_FWD_NOALLOC_SCRATCH_BYTES
+ * (2 MiB) inside the library, one copy per GPU, held until the process ends; its
+ * address is looked up on the first call on each device.  A problem whose
+ * jfa_fwd_workspace_size exceeds that size gives JFA_ERR_WORKSPACE_TOO_SMALL (2 MiB
+ * hold about 131,000 plan items of 16 bytes: one per sequence in broadcast mode, one
+ * per 128- or 256-row query tile of each sequence in self mode, plus one per
+ * sequence).  Every call on a GPU uses that GPU's one copy and leaves its plan there:
+ * calls that overlap on one GPU (on other streams or threads) race, so the caller
+ * serialises them.  Each call's plan kernel rewrites every plan word it uses, the
+ * work counter included, before the attention kernel reads them.  The call is not
+ * timed by jfa_profile_enable (it creates no events). */
+#define JFA_FWD_NOALLOC_SCRATCH_BYTES (2u << 20)
+jfa_status_t jfa_fwd_noalloc(const void* q, const void* k, const void* v,
+                             const void* offsets, int offsets_is_int64,
+                             int64_t batch, int64_t num_heads, int64_t head_dim,
+                             int64_t q_len, int64_t total_kv,
+                             int broadcast_q, int causal, float softmax_scale,
+                             void* o, float* lse, void* stream);
+
 /* Backward pass: gradients of sum(O * dO) with respect to q, k and v, given the
  * o and lse that jfa_fwd returned for the same inputs.  In broadcast mode dq is
  * the sum over all sequences (JFA news page, "GEM's sequences do not fit a fixed

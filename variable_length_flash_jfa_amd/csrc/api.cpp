@@ -242,40 +242,108 @@ size_t jfa_bwd_workspace_size(int64_t batch, int64_t num_heads, int64_t head_dim
   return bwd_ws_bytes(p);
 }
 
-jfa_status_t jfa_fwd(const void* q, const void* k, const void* v, const void* offsets,
-                     int offsets_is_int64, int64_t batch, int64_t num_heads, int64_t head_dim,
-                     int64_t q_len, int64_t total_kv, int broadcast_q, int causal, float softmax_scale,
-                     void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+// Plan scratch of jfa_fwd_noalloc: one copy of this array per GPU, held until the
+// process ends.  Host code never uses the array's name as an address (on the host it
+// is only a stand-in): each device's copy is looked up once with
+// hipGetSymbolAddress, with that device current, and only that pointer is passed on.
+static __device__ __align__(256) char scratch[JFA_FWD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::map<int, char*> g_scratch_ptr;   // device -> address of its copy of `scratch`
+
+jfa_status_t scratch_address(const char* fn, char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, fn, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, fn, "hipGetSymbolAddress of the plan scratch");
+    if (ptr == nullptr) return fail(JFA_ERR_HIP, "%s: hipGetSymbolAddress gave a null plan scratch", fn);
+    it = g_scratch_ptr.emplace(dev, static_cast<char*>(ptr)).first;
+  }
+  *out = it->second;
+  return JFA_OK;
+}
+
+// jfa_fwd (plan in the caller's workspace) and jfa_fwd_noalloc (plan in this
+// device's copy of `scratch`; no event timing, so that nothing is created).
+jfa_status_t fwd_impl(const char* fn, const void* q, const void* k, const void* v, const void* offsets,
+                      int offsets_is_int64, int64_t batch, int64_t num_heads, int64_t head_dim,
+                      int64_t q_len, int64_t total_kv, int broadcast_q, int causal, float softmax_scale,
+                      void* o, float* lse, void* workspace, size_t workspace_bytes, bool noalloc,
+                      void* stream) {
   g_error[0] = '\0';
   const Sizes sz = check_sizes(batch, num_heads, head_dim, q_len, total_kv, broadcast_q, causal);
-  if (!sz.ok) return fail(sz.st, "jfa_fwd: %s", sz.why);
+  if (!sz.ok) return fail(sz.st, "%s: %s", fn, sz.why);
   if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f)
-    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_fwd: softmax_scale must be finite and > 0");
+    return fail(JFA_ERR_INVALID_ARGUMENT, "%s: softmax_scale must be finite and > 0", fn);
   const jfa::Problem p = make_problem(q, k, v, offsets, offsets_is_int64, batch, num_heads, head_dim,
                                       q_len, total_kv, broadcast_q, causal, softmax_scale);
   if (p.batch == 0 || p.rows == 0) return JFA_OK;
-  if (!q || !offsets || !o || !lse || !workspace || (p.total_kv > 0 && (!k || !v)))
-    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_fwd: null pointer argument");
-  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(workspace) ||
+  if (!q || !offsets || !o || !lse || (!noalloc && !workspace) || (p.total_kv > 0 && (!k || !v)))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "%s: null pointer argument", fn);
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || (!noalloc && misaligned(workspace)) ||
       (reinterpret_cast<uintptr_t>(lse) & 3) ||
       (reinterpret_cast<uintptr_t>(offsets) & (offsets_is_int64 ? 7 : 3)))
-    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_fwd: tensors must be 16-byte aligned");
+    return fail(JFA_ERR_INVALID_ARGUMENT, "%s: tensors must be 16-byte aligned", fn);
   const size_t need = fwd_ws_bytes(p);
-  if (workspace_bytes < need)
-    return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "jfa_fwd: workspace of %zu bytes, need %zu",
-                workspace_bytes, need);
-  char* cur = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(workspace)));
+  char* base = nullptr;
+  if (noalloc) {
+    if (need > (size_t)JFA_FWD_NOALLOC_SCRATCH_BYTES)
+      return fail(JFA_ERR_WORKSPACE_TOO_SMALL,
+                  "%s: the tile plan of this problem needs %zu bytes, more than the %zu bytes of plan "
+                  "scratch the library holds; use jfa_fwd with a workspace",
+                  fn, need, (size_t)JFA_FWD_NOALLOC_SCRATCH_BYTES);
+    const jfa_status_t st = scratch_address(fn, &base);
+    if (st != JFA_OK) return st;
+  } else {
+    if (workspace_bytes < need)
+      return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes,
+                  need);
+    base = static_cast<char*>(workspace);
+  }
+  char* cur = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(base)));
   jfa::Plan plan;
   plan.meta = reinterpret_cast<int*>(carve(cur, 64));
   plan.max_items = jfa::fwd_max_items(p);
   plan.items = reinterpret_cast<int4*>(carve(cur, plan.max_items * sizeof(int4)));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int sched = g_schedule.load();
-  hipError_t e = timed_launch("plan_fwd", s, [&] { return jfa::launch_plan_fwd(p, plan, sched, s); });
-  if (e != hipSuccess) return hip_fail(e, "jfa_fwd: plan launch");
-  e = timed_launch("fwd", s, [&] { return jfa::launch_fwd(p, plan, sched, o, lse, s); });
-  if (e != hipSuccess) return hip_fail(e, "jfa_fwd: kernel launch");
+  // the plan kernel rewrites every word of the plan it uses, the work counter included
+  hipError_t e = noalloc ? jfa::launch_plan_fwd(p, plan, sched, s)
+                         : timed_launch("plan_fwd", s, [&] { return jfa::launch_plan_fwd(p, plan, sched, s); });
+  if (e != hipSuccess) return hip_fail(e, fn, "plan launch");
+  e = noalloc ? jfa::launch_fwd(p, plan, sched, o, lse, s)
+              : timed_launch("fwd", s, [&] { return jfa::launch_fwd(p, plan, sched, o, lse, s); });
+  if (e != hipSuccess) return hip_fail(e, fn, "kernel launch");
   return JFA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+jfa_status_t jfa_fwd(const void* q, const void* k, const void* v, const void* offsets,
+                     int offsets_is_int64, int64_t batch, int64_t num_heads, int64_t head_dim,
+                     int64_t q_len, int64_t total_kv, int broadcast_q, int causal, float softmax_scale,
+                     void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl("jfa_fwd", q, k, v, offsets, offsets_is_int64, batch, num_heads, head_dim, q_len, total_kv,
+                  broadcast_q, causal, softmax_scale, o, lse, workspace, workspace_bytes, false, stream);
+}
+
+jfa_status_t jfa_fwd_noalloc(const void* q, const void* k, const void* v, const void* offsets,
+                             int offsets_is_int64, int64_t batch, int64_t num_heads, int64_t head_dim,
+                             int64_t q_len, int64_t total_kv, int broadcast_q, int causal,
+                             float softmax_scale, void* o, float* lse, void* stream) {
+  return fwd_impl("jfa_fwd_noalloc", q, k, v, offsets, offsets_is_int64, batch, num_heads, head_dim, q_len,
+                  total_kv, broadcast_q, causal, softmax_scale, o, lse, nullptr, 0, true, stream);
 }
 
 namespace {
