@@ -16,9 +16,10 @@
 //      v_mfma_f32_32x32x16_bf16.  Waves whose 32 keys all lie past the sequence
 //      end skip their work;
 //   4. the dQ contribution of the whole 256-key tile is reduced on chip first: the
-//      waves publish dS^T to LDS, each computes one 32-column slice of dS K over
-//      one part of the keys, the parts are summed through LDS, and a tile adds one
-//      fp32 partial per query row into HBM.  In broadcast-Q mode every sequence
+//      waves publish dS^T to LDS and each computes one 32-column slice of dS K over
+//      all keys of the tile (with eight waves and four slices, the waves take two
+//      consecutive query blocks, one each, so no partial sums are exchanged), and a
+//      tile adds one fp32 partial per query row into HBM.  In broadcast-Q mode every sequence
 //      adds into the same dQ ("Meta's TLX attention kernel outpaces
 //      FlashAttention-4 on B200", section "GEM's sequences do not fit a fixed
 //      grid"), so the accumulator is striped per XCD (8 fp32 copies).  The
@@ -143,44 +144,44 @@ struct BwdKernel {
   static constexpr int DT = D / 32;          // 32-wide d tiles
   static constexpr int KS = D / 16;          // 16-deep k steps over d
   static constexpr int DTW = DT > NW ? DT / NW : 1;   // d tiles of the dQ product per wave
-  static constexpr int KP = DT > NW ? 1 : NW / DT;    // key parts of the dQ product
-  static constexpr int KPART = BN / KP;      // keys per part
+  // With more waves than d tiles the waves split the query blocks instead: G
+  // consecutive query blocks form a group, and wave (d tile, g) computes the dQ of
+  // block g of the group over all BN keys, once the whole group's dS^T is in LDS.
+  static constexpr int G = DT > NW ? 1 : NW / DT;     // query blocks per dQ group
+  static constexpr int NDS = G > 1 ? G + 1 : 1;      // dS^T slots (a ring when G > 1)
   static constexpr int KT_BYTES = BN * D * 2;
   static constexpr int QT_BYTES = BQ * D * 2;
   static constexpr int DS_BYTES = BN * BQ * 2;
-  static constexpr int DQP_BYTES = KP > 1 ? KP * DT * 32 * 32 * 4 : 0;
   static constexpr int ROW_BYTES = BQ * 8;   // (LSE log2 e, delta) per query row
   // LDS map
   static constexpr int OFF_K = 0;
   static constexpr int OFF_Q = OFF_K + KT_BYTES;              // 2 buffers
   static constexpr int OFF_DO = OFF_Q + 2 * QT_BYTES;         // 2 buffers
-  static constexpr int OFF_DS = OFF_DO + 2 * QT_BYTES;
-  static constexpr int OFF_DQP = OFF_DS + DS_BYTES;           // dQ partials of the key parts
-  static constexpr int OFF_ROW = OFF_DQP + DQP_BYTES;         // 2 buffers
+  static constexpr int OFF_DS = OFF_DO + 2 * QT_BYTES;        // NDS slots
+  static constexpr int OFF_ROW = OFF_DS + NDS * DS_BYTES;     // 2 buffers
   static constexpr int OFF_DEL = OFF_ROW + 2 * ROW_BYTES;     // per-wave partial deltas (self mode)
   static constexpr int DEL_BYTES = DIRECT ? NW * BQ * 4 : 0;
   static constexpr int SMEM = OFF_DEL + DEL_BYTES;
   static constexpr uint32_t GQ = OFF_DO - OFF_Q;              // dO tile minus Q tile, same buffer
   static constexpr int XB = D == 128 ? 256 : 128;             // the XOR-free granule
-  static_assert(BN == 32 * NW && KP * DT == NW * DTW && DTW <= 2 && KPART % 16 == 0, "tile shape");
-  static_assert(!(DIRECT && ROPE) || (KP == 1 && DTW == 2),
+  static_assert(BN == 32 * NW && G * DT == NW * DTW && DTW <= 2, "tile shape");
+  static_assert(!(DIRECT && ROPE) || (G == 1 && DTW == 2),
                 "the single-tile rotary path needs both halves of a dQ column pair in one wave");
-  static_assert(OFF_Q % XB == 0 && QT_BYTES % XB == 0 && GQ % XB == 0 && (KPART * 2 * D) % XB == 0 &&
-                    (32 * 2 * D) % XB == 0 && OFF_DS % 64 == 0 && (KPART * BQ * 2) % 64 == 0,
+  static_assert(OFF_Q % XB == 0 && QT_BYTES % XB == 0 && GQ % XB == 0 && (32 * 2 * D) % XB == 0 &&
+                    OFF_DS % 64 == 0 && DS_BYTES % 64 == 0,
                 "tile offsets must commute with the swizzle XOR");
 
   BwdArgs a;
   char* smem;
   int lane, wave, c32, hf;
   int64_t rs;
-  int dq_dt, dq_part;    // this wave's (first) d tile and key part in the dQ product
+  int dq_dt, dq_qb;      // this wave's (first) d tile and query block of a group in the dQ product
 
   // per tile
   int64_t kv0;           // first K/V row of the sequence
   int64_t grow0;         // first dO / LSE row of the sequence
   int n, j0, h, q_rows;
   int nvalid;            // keys of this tile inside the sequence (1..BN)
-  int nparts;            // key parts holding at least one of them
   bool active;           // this wave owns at least one key inside the sequence
   bf16x8 vf[KS];
   f32x16 dvt[DT], dkt[DT];
@@ -201,7 +202,7 @@ struct BwdKernel {
     hf = lane >> 5;
     rs = (int64_t)a.heads * D;
     dq_dt = wave % (DT / DTW);   // with two d tiles a wave takes dq_dt and dq_dt + DT / 2
-    dq_part = wave / (DT / DTW);
+    dq_qb = wave / (DT / DTW);
     row_base = row_read_base<D>(lane);
     k_row_base = row_base + (uint32_t)(OFF_K + 32 * wave * 2 * D);
     tr4_base = tr_read_base<D>(lane, 4 * hf);
@@ -212,29 +213,29 @@ struct BwdKernel {
   // Lane parts of the dQ-product, dS^T and reduce-add addresses.  They are formed
   // where they are used, from a laundered lane index, instead of being held in
   // VGPRs for the whole kernel.
-  // K transposing reads of this wave's dQ slice and key part:
+  // K transposing reads of this wave's dQ slice (all BN keys):
   __device__ __forceinline__ uint32_t kq_base() const {
     const int l = (int)launder((uint32_t)lane);
-    return (tr_read_base<D>(l, 8 * (l >> 5)) ^ (uint32_t)((4 * dq_dt) << 4)) +
-           (uint32_t)(OFF_K + dq_part * KPART * 2 * D);
+    return (tr_read_base<D>(l, 8 * (l >> 5)) ^ (uint32_t)((4 * dq_dt) << 4)) + (uint32_t)OFF_K;
   }
   // dS^T tile [BN keys][BQ queries] bf16, 64-byte rows of eight 8-byte units; unit u
   // of row j is stored at u ^ ((j >> 2) & 7), which keeps both the 32-row writes
   // and the 4-row transposing reads free of bank conflicts.
-  // dS^T transposing reads of this wave's key part:
-  __device__ __forceinline__ uint32_t dsq_base() const {
+  // dS^T transposing reads (all BN keys) of the block in dS^T slot `slot`:
+  __device__ __forceinline__ uint32_t dsq_base(int slot) const {
     const int l = (int)launder((uint32_t)lane);
     const int t = l & 15, h2 = l >> 5;
     const int unit = 4 * ((l >> 4) & 1) + (t & 3);
-    return (uint32_t)(OFF_DS + dq_part * KPART * (BQ * 2) + (8 * h2 + (t >> 2)) * (BQ * 2) +
-                      ((unit ^ (2 * h2)) << 3));
+    return (uint32_t)(OFF_DS + slot * DS_BYTES + (8 * h2 + (t >> 2)) * (BQ * 2) + ((unit ^ (2 * h2)) << 3));
   }
-  // dS^T writes of this lane's key row:
-  __device__ __forceinline__ uint32_t dsw_base() const {
+  // dS^T writes of this lane's key row into slot `slot`:
+  __device__ __forceinline__ uint32_t dsw_base(int slot) const {
     const int l = (int)launder((uint32_t)lane);
     const int j = 32 * wave + (l & 31);
-    return (uint32_t)(OFF_DS + j * (BQ * 2) + (((l >> 5) ^ ((j >> 2) & 7)) << 3));
+    return (uint32_t)(OFF_DS + slot * DS_BYTES + j * (BQ * 2) + (((l >> 5) ^ ((j >> 2) & 7)) << 3));
   }
+  // dS^T slot of the query block starting at row qi0
+  __device__ __forceinline__ static int ds_slot(int qi0) { return NDS > 1 ? (qi0 / BQ) % NDS : 0; }
   // byte offset of this lane's fp32 dQ element within a query block:
   __device__ __forceinline__ uint32_t dq_lane_off() const {
     const int l = (int)launder((uint32_t)lane);
@@ -242,10 +243,6 @@ struct BwdKernel {
   }
 
   __device__ __forceinline__ char* rowbuf(int b) { return smem + OFF_ROW + b * ROW_BYTES; }
-  // partial of key part p, d tile dt: 32 x 32 fp32 in MFMA C layout
-  __device__ __forceinline__ float* dq_partial(int p, int dt) {
-    return reinterpret_cast<float*>(smem + OFF_DQP) + (p * DT + dt) * 32 * 32;
-  }
 
   // Issues the direct LDS loads of query block [qi0, qi0 + BQ): Q and dO rows, and
   // the (LSE, delta) pairs of those rows.  Rows past the end read as zeros; the
@@ -290,7 +287,7 @@ struct BwdKernel {
   // (half_lane_sums16), the partial sums meet in LDS at a barrier (the MID_BAR one
   // when there is one), and every wave adds the NW partials of its rows.
   template <bool MASKED, bool MID_BAR>
-  __device__ __forceinline__ void qblock(int buf, int qi0) {
+  __device__ __forceinline__ void qblock(int buf, int qi0, int slot) {
     if (!active) {
       if constexpr (MID_BAR || DIRECT) __syncthreads();
       return;
@@ -402,7 +399,7 @@ struct BwdKernel {
       }
       // publish dS^T [key][query] (bf16)
       auto publish_ds = [&]() {
-        const uint32_t wb = dsw_base();
+        const uint32_t wb = dsw_base(slot);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           bf16x4 w;
@@ -460,12 +457,12 @@ struct BwdKernel {
     }
   }
 
-  // dQ partial of the block whose dS^T is in LDS: this wave's 32-column slice
-  // (d tile dq_dt) over all keys of its part.  The rows of keys past the sequence
-  // end hold zeros (zero probability, or zeroed at the start of the tile for waves
-  // with no key inside), so the loop needs no bounds.
-  __device__ __forceinline__ void dq_compute(f32x16 (&out)[DTW]) {
-    const uint32_t dsb = dsq_base();
+  // dQ of the block whose dS^T is in slot `slot`: this wave's 32-column slice
+  // (d tile dq_dt, and dq_dt + DT / 2 with two d tiles) over all BN keys.  The rows
+  // of keys past the sequence end hold zeros (zero probability, or zeroed at the
+  // start of the tile for waves with no key inside), so the loop needs no bounds.
+  __device__ __forceinline__ void dq_compute(f32x16 (&out)[DTW], int slot) {
+    const uint32_t dsb = dsq_base(slot);
     const uint32_t kb8 = kq_base();
     auto ds_op = [&](int jj) {   // dS[query l % 32][keys jj + 8 (l / 32) + e] of the part
       const uint32_t x = (uint32_t)(((jj >> 2) & 4) << 3);
@@ -477,9 +474,9 @@ struct BwdKernel {
       bf16x8 sa = ds_op(0);
       bf16x8 kb = lds_operand_tr<D>(smem, kb8, 0, 4, 0);
 #pragma unroll
-      for (int jj = 0; jj < KPART; jj += 16) {
+      for (int jj = 0; jj < BN; jj += 16) {
         bf16x8 sa_n = sa, kb_n = kb;
-        if (jj + 16 < KPART) {
+        if (jj + 16 < BN) {
           sa_n = ds_op(jj + 16);
           kb_n = lds_operand_tr<D>(smem, kb8, jj + 16, jj + 20, 0);
         }
@@ -507,9 +504,9 @@ struct BwdKernel {
       bf16x8 k0 = lds_operand_tr<D>(smem, kb8, 0, 4, 0);
       bf16x8 k1 = lds_operand_tr<D>(smem, kb8, 0, 4, DT / 2);
 #pragma unroll
-      for (int jj = 0; jj < KPART; jj += 16) {
+      for (int jj = 0; jj < BN; jj += 16) {
         bf16x8 sa_n = sa, k0_n = k0, k1_n = k1;
-        if (jj + 16 < KPART) {
+        if (jj + 16 < BN) {
           sa_n = ds_op(jj + 16);
           k0_n = lds_operand_tr<D>(smem, kb8, jj + 16, jj + 20, 0);
           k1_n = lds_operand_tr<D>(smem, kb8, jj + 16, jj + 20, DT / 2);
@@ -523,23 +520,6 @@ struct BwdKernel {
       }
     }
   }
-  __device__ __forceinline__ f32x16 dq_compute1() {
-    f32x16 o[DTW];
-    dq_compute(o);
-    return o[0];
-  }
-
-  // Several key parts: every part with keys publishes its partial to LDS (summed by
-  // dq_flush after the next barrier).
-  __device__ __forceinline__ void dq_publish(const f32x16& acc) {
-    float* dstp = dq_partial(dq_part, dq_dt);
-#pragma unroll
-    for (int r = 0; r < 16; r += 4) {
-      const f32x4 v4 = {acc[r], acc[r + 1], acc[r + 2], acc[r + 3]};
-      *reinterpret_cast<f32x4*>(dstp + (r / 4) * 256 + lane * 4) = v4;
-    }
-  }
-
   // Reduce-add of rows 8 g .. 8 g + 7 (g = g0 .. g0 + NG - 1) of a block's dQ slice
   // into the fp32 accumulator with buffer atomics; vals[k] holds registers 4 (g0 + k)
   // .. + 3, i.e. rows 8 g + 4 (lane / 32) + e.  One descriptor per group bounds the
@@ -583,10 +563,11 @@ struct BwdKernel {
         __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(vals[k][e], acc, o[e], 0, 0);
     }
   }
-  // One key part: reduce-add (or store) every row of this wave's d tile(s).
-  __device__ __forceinline__ void dq_atomics_all(int qi0) {
+  // dQ of the query block starting at row qi0 (its dS^T in LDS): reduce-add (or
+  // store) every row of this wave's d tile(s).
+  __device__ __forceinline__ void dq_block(int qi0) {
     f32x16 dq[DTW];
-    dq_compute(dq);
+    dq_compute(dq, ds_slot(qi0));
     if constexpr (DIRECT && ROPE) rope_conjugate_dq(dq, qi0);
 #pragma unroll
     for (int k = 0; k < DTW; ++k) {
@@ -597,73 +578,52 @@ struct BwdKernel {
       dq_atomics<4>(v, 0, qi0, k);
     }
   }
-
-  // Rows handled by each key part in the flush: 32 / KP rows, 16 / KP reduce-adds.
-  static constexpr int FLUSH_GROUPS = 4 / KP;
-
-  // After a barrier: every wave sums the parts' partials of its d tile over the rows
-  // of its own key part (groups dq_part FLUSH_GROUPS ..) and reduce-adds them, so
-  // the flush work is spread evenly over the parts.
-  __device__ __forceinline__ void dq_flush(int qi0) {
-    const int g0 = dq_part * FLUSH_GROUPS;
-    f32x4 v[FLUSH_GROUPS];
-#pragma unroll
-    for (int k = 0; k < FLUSH_GROUPS; ++k)
-      v[k] = *reinterpret_cast<const f32x4*>(dq_partial(0, dq_dt) + (g0 + k) * 256 + lane * 4);
-#pragma unroll
-    for (int p = 1; p < KP; ++p) {
-      if (p < nparts) {
-#pragma unroll
-        for (int k = 0; k < FLUSH_GROUPS; ++k) {
-          const f32x4 w = *reinterpret_cast<const f32x4*>(dq_partial(p, dq_dt) + (g0 + k) * 256 + lane * 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[k][e] += w[e];
-        }
-      }
-    }
-    dq_atomics<FLUSH_GROUPS>(v, g0, qi0);
+  // The dQ of a group of `cnt` query blocks from row g0: wave (d tile, g) takes
+  // block g.
+  __device__ __forceinline__ void dq_group(int g0, int cnt) {
+    if (dq_qb < cnt) dq_block(g0 + dq_qb * BQ);
   }
+  // reduce-adds (or stores) one wave issues for one query block
+  static constexpr int DQ_OPS = 16 * DTW;
 
-  // Query-block loop.  Iteration t issues the LDS loads of block t + 1, computes the
-  // dQ partial of block t - 1 (its dS^T is still in LDS), then block t.  With one key
-  // part a wave reduce-adds its partial at once and the barrier that retires the
-  // readers of dS^T(t - 1) sits inside block t, before its dS^T write; with
-  // several, the partials are published to LDS, a barrier follows, and every part
-  // sums and reduce-adds its share of the rows before block t.  Vector memory
-  // operations retire in issue order, so the wait before the closing barrier (for
-  // the loads) leaves the reduce-adds issued after them in flight; the last block
-  // loads nothing and does not wait.
+  // Query-block loop.  Iteration t issues the LDS loads of block t + 1, runs the dQ
+  // products of the pending group once it is complete (G blocks whose dS^T has been
+  // in LDS since the previous closing barrier), then block t.  With G = 1 the
+  // barrier that retires the readers of the one dS^T slot sits inside block t,
+  // before its dS^T write; with G > 1 the blocks' dS^T go round a ring of G + 1
+  // slots, so that block t never writes a slot the products of its iteration read,
+  // and one barrier per block remains.  Vector memory operations retire in issue
+  // order, so the wait before the closing barrier (for the loads) leaves the
+  // reduce-adds issued after them in flight; the last block loads nothing and does
+  // not wait.  (gfirst, npend): first row and count of the blocks whose dQ is
+  // still to be formed.
   template <bool MASKED>
-  __device__ __forceinline__ void run(int qs, int qe, int q_last, int& pending) {
+  __device__ __forceinline__ void run(int qs, int qe, int q_last, int& gfirst, int& npend) {
     for (int qi0 = qs; qi0 < qe; qi0 += BQ) {
       const int buf = (qi0 / BQ) & 1;
+      const bool group = npend == G;   // wave-uniform
       // With the rotary conjugate in the single-tile path the dQ of the pending block
       // reads table entries: done before the next block's loads are issued, so that
       // waiting for those entries does not wait for the loads (vector memory
       // operations complete in order).
       constexpr bool kDqFirst = DIRECT && ROPE;
       if constexpr (kDqFirst) {
-        if (pending >= 0) dq_atomics_all(pending);
+        if (group) dq_group(gfirst, G);
       }
       if (qi0 + BQ < q_last) load_qblock(qi0 + BQ, buf ^ 1);   // one block ahead
-      if constexpr (KP == 1) {
-        if (!kDqFirst && pending >= 0) dq_atomics_all(pending);
-        qblock<MASKED, true>(buf, qi0);
-      } else {
-        if (pending >= 0 && dq_part < nparts) dq_publish(dq_compute1());
-        __syncthreads();
-        if (pending >= 0) dq_flush(pending);
-        qblock<MASKED, false>(buf, qi0);
-      }
+      if (!kDqFirst && group) dq_group(gfirst, G);
+      qblock<MASKED, G == 1>(buf, qi0, ds_slot(qi0));
+      if (group) npend = 0;
+      if (npend == 0) gfirst = qi0;
+      ++npend;
       if (qi0 + BQ < q_last) {   // the next block's loads must have landed
-        if (!kDqFirst && pending >= 0) {
-          wait_vmcnt<4 * FLUSH_GROUPS * DTW>();   // the reduce-adds issued after them stay in flight
+        if (!kDqFirst && group) {
+          wait_vmcnt<DQ_OPS>();   // the reduce-adds issued after them stay in flight
         } else {
           wait_lds_loads();
         }
       }
       __syncthreads();
-      pending = qi0;
     }
   }
 
@@ -721,13 +681,12 @@ struct BwdKernel {
 
   // Epilogue slots: wave 0 stages through the query buffer that the next tile's
   // first block leaves free, wave 1 through the matching dO buffer, the others
-  // through the dS^T / dQ-partial region; EPI_PASSES splits a slot's 32 rows so that
-  // they fit.
+  // through the dS^T slots; EPI_PASSES splits a slot's 32 rows so that they fit.
   static constexpr int EPI_PASSES =
-      (NW - 2) * 32 * 2 * D <= DS_BYTES + DQP_BYTES ? 1 : ((NW - 2) * 16 * 2 * D <= DS_BYTES + DQP_BYTES ? 2 : 4);
+      (NW - 2) * 32 * 2 * D <= NDS * DS_BYTES ? 1 : ((NW - 2) * 16 * 2 * D <= NDS * DS_BYTES ? 2 : 4);
   static constexpr int SLOT_BYTES = 32 * 2 * D / EPI_PASSES;
-  static_assert((NW - 2) * SLOT_BYTES <= DS_BYTES + DQP_BYTES && SLOT_BYTES <= QT_BYTES,
-                "epilogue slots must fit in the free query buffers and the dS^T / dQ regions");
+  static_assert((NW - 2) * SLOT_BYTES <= NDS * DS_BYTES && SLOT_BYTES <= QT_BYTES,
+                "epilogue slots must fit in the free query buffers and the dS^T slots");
   static constexpr int EPI_STORES = 2 * (D / 16);   // store instructions of one epilogue
   __device__ __forceinline__ char* epilogue_slot(int free_buf) const {
     if (wave == 0) return smem + OFF_Q + free_buf * QT_BYTES;
@@ -815,7 +774,6 @@ struct BwdKernel {
     n = g.n;
     j0 = g.j0;
     nvalid = min(n - j0, BN);
-    nparts = (nvalid + KPART - 1) / KPART;
     active = 32 * wave < nvalid;
     q_rows = BCAST ? a.q_len : n;
     grow0 = BCAST ? (int64_t)g.b * a.q_len : kv0;
@@ -825,10 +783,13 @@ struct BwdKernel {
     // a wave with no key inside the sequence never writes its dS^T rows in this
     // tile: zero them once for the dQ products
     if (!active) {
-      const uint32_t wb = dsw_base();
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<bf16x4*>(smem + (wb ^ (uint32_t)(q4 << 4))) = bf16x4{};
+      for (int slot = 0; slot < NDS; ++slot) {
+        const uint32_t wb = dsw_base(slot);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<bf16x4*>(smem + (wb ^ (uint32_t)(q4 << 4))) = bf16x4{};
+      }
       // nor its partial deltas
       if (DIRECT && lane < BQ) reinterpret_cast<float*>(smem + OFF_DEL)[wave * BQ + lane] = 0.f;
     }
@@ -856,22 +817,14 @@ struct BwdKernel {
     if constexpr (CAUSAL) qm = min(q_last, ((j0 + BN - 1 + BQ - 1) / BQ) * BQ);
     if (kv_tail) qm = q_last;
     const int qfull = max(qm, (q_last / BQ) * BQ);
-    int pending = -1;   // query block whose dQ is still to be reduced
-    run<true>(qs, qm, q_last, pending);
-    run<false>(qm, qfull, q_last, pending);
-    run<true>(qfull, q_last, q_last, pending);
+    int gfirst = 0, npend = 0;   // query blocks whose dQ is still to be formed
+    run<true>(qs, qm, q_last, gfirst, npend);
+    run<false>(qm, qfull, q_last, gfirst, npend);
+    run<true>(qfull, q_last, q_last, gfirst, npend);
     const bool more = next(ng);
     constexpr bool kDqFirst = DIRECT && ROPE;   // as in run(): the table reads go first
     if (more && !kDqFirst) issue_v(ng);
-    if (pending >= 0) {
-      if constexpr (KP == 1) {
-        dq_atomics_all(pending);
-      } else {
-        if (dq_part < nparts) dq_publish(dq_compute1());
-        __syncthreads();
-        dq_flush(pending);
-      }
-    }
+    if (npend > 0) dq_group(gfirst, npend);   // the closing barrier published their dS^T
     if (more && kDqFirst) issue_v(ng);
     __syncthreads();   // every wave is past its last read of the K tile, dQ partials and query blocks
     if (more) {
