@@ -163,7 +163,7 @@ jfa_status_t jfa_bwd(const void* q, const void* k, const void* v,
  * jfa_bwd (every self-mode sequence within one 64-key tile, D = 128), by the tiles
  * before they store it; other single-tile calls take the finalize route.  Same workspace
  * (jfa_bwd_workspace_size), ownership and error rules as jfa_bwd; null tables or
- * positions, max_pos outside [1, 2^30] or misaligned tables give
+ * positions, max_pos outside [1, 2^24] or misaligned tables give
  * JFA_ERR_INVALID_ARGUMENT. */
 jfa_status_t jfa_bwd_rope(const void* q, const void* k, const void* v,
                           const void* offsets, int offsets_is_int64,

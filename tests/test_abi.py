@@ -126,6 +126,7 @@ def test_rope_rejections(lib):
     assert bwd_rope(lib, pos_k=None) == INVALID
     assert b"rotary" in lib.jfa_last_error()
     assert bwd_rope(lib, max_pos=0) == INVALID
+    assert bwd_rope(lib, max_pos=(1 << 24) + 1) == INVALID
     assert bwd_rope(lib, cos=ctypes.c_void_p((1 << 20) + 4)) == INVALID    # tables 16-byte aligned
     assert bwd_rope(lib, pos_k=ctypes.c_void_p((1 << 20) + 2)) == INVALID  # positions 4-byte aligned
     # the plain backward's checks apply too, under this entry point's name

@@ -426,8 +426,8 @@ jfa_status_t jfa_bwd_rope(const void* q, const void* k, const void* v, const voi
   g_error[0] = '\0';
   if (!rope_cos || !rope_sin || !pos_q || (total_kv > 0 && !pos_k))
     return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_bwd_rope: null rotary table or position pointer");
-  if (max_pos < 1 || max_pos > (int64_t)1 << 30)
-    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_bwd_rope: max_pos must be in [1, 2^30]");
+  if (max_pos < 1 || max_pos > (int64_t)1 << 24)
+    return fail(JFA_ERR_INVALID_ARGUMENT, "jfa_bwd_rope: max_pos must be in [1, 2^24]");
   if (misaligned(rope_cos) || misaligned(rope_sin) || (reinterpret_cast<uintptr_t>(pos_q) & 3) ||
       (reinterpret_cast<uintptr_t>(pos_k) & 3))
     return fail(JFA_ERR_INVALID_ARGUMENT,

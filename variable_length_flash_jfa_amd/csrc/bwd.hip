@@ -161,11 +161,20 @@ struct BwdKernel {
   static constexpr int OFF_ROW = OFF_DS + NDS * DS_BYTES;     // 2 buffers
   static constexpr int OFF_DEL = OFF_ROW + 2 * ROW_BYTES;     // per-wave partial deltas (self mode)
   static constexpr int DEL_BYTES = DIRECT ? NW * BQ * 4 : 0;
-  static constexpr int SMEM = OFF_DEL + DEL_BYTES;
+  // The single-tile rotary path rotates dQ in its tiles: the positions of each query
+  // block's rows come with the block (2 buffers of 64 dwords), and each wave copies
+  // the (cos, sin) table rows of its 32 columns for the block's 32 rows into a region
+  // of its own, one block ahead of the rotation.
+  static constexpr bool RTAB = DIRECT && ROPE;
+  static constexpr int OFF_RPOS = OFF_DEL + DEL_BYTES;
+  static constexpr int RPOS_BYTES = RTAB ? 2 * 256 : 0;
+  static constexpr int RTAB_WAVE = 2 * BQ * 32 * 4;            // cos, then sin: [32 rows][32 columns] fp32
+  static constexpr int OFF_RTAB = OFF_RPOS + RPOS_BYTES;
+  static constexpr int SMEM = OFF_RTAB + (RTAB ? NW * RTAB_WAVE : 0);
   static constexpr uint32_t GQ = OFF_DO - OFF_Q;              // dO tile minus Q tile, same buffer
   static constexpr int XB = D == 128 ? 256 : 128;             // the XOR-free granule
   static_assert(BN == 32 * NW && G * DT == NW * DTW && DTW <= 2, "tile shape");
-  static_assert(!(DIRECT && ROPE) || (G == 1 && DTW == 2),
+  static_assert(!(DIRECT && ROPE) || (G == 1 && DTW == 2 && D == 128 && NW == 2),
                 "the single-tile rotary path needs both halves of a dQ column pair in one wave");
   static_assert(OFF_Q % XB == 0 && QT_BYTES % XB == 0 && GQ % XB == 0 && (32 * 2 * D) % XB == 0 &&
                     OFF_DS % 64 == 0 && DS_BYTES % 64 == 0,
@@ -183,6 +192,7 @@ struct BwdKernel {
   int n, j0, h, q_rows;
   int nvalid;            // keys of this tile inside the sequence (1..BN)
   bool active;           // this wave owns at least one key inside the sequence
+  int kpos;              // RTAB: position of this lane's key, loaded at the start of the tile
   bf16x8 vf[KS];
   f32x16 dvt[DT], dkt[DT];
   // lane parts of the LDS addresses (see row_read_base / tr_read_base)
@@ -263,6 +273,12 @@ struct BwdKernel {
                            row_bytes);
       lds_load_tile<D, NW>(smem + OFF_DO + buf * QT_BYTES, BQ, wave, lane, make_rsrc_sgpr(gsrc, bytes),
                            row_bytes);
+    }
+    if constexpr (RTAB) {   // the rows' positions
+      if (wave == 0) {
+        const int* src = a.rope_pos_q + kv0_ + qi0;
+        lds_load4(make_rsrc_sgpr(src, (uint32_t)rows * 4u), (uint32_t)lane * 4u, smem + OFF_RPOS + buf * 256);
+      }
     }
     if (wave == NW - 1) {
       if constexpr (DIRECT) {   // the forward's LSE, one float per row
@@ -568,7 +584,7 @@ struct BwdKernel {
   __device__ __forceinline__ void dq_block(int qi0) {
     f32x16 dq[DTW];
     dq_compute(dq, ds_slot(qi0));
-    if constexpr (DIRECT && ROPE) rope_conjugate_dq(dq, qi0);
+    if constexpr (RTAB) rope_conjugate_dq(dq);
 #pragma unroll
     for (int k = 0; k < DTW; ++k) {
       const f32x4 v[4] = {{dq[k][0], dq[k][1], dq[k][2], dq[k][3]},
@@ -609,6 +625,9 @@ struct BwdKernel {
       constexpr bool kDqFirst = DIRECT && ROPE;
       if constexpr (kDqFirst) {
         if (group) dq_group(gfirst, G);
+        // this block's table rows, for its rotation in the next iteration (the
+        // rotation just done has read the region)
+        issue_rope_tables(buf);
       }
       if (qi0 + BQ < q_last) load_qblock(qi0 + BQ, buf ^ 1);   // one block ahead
       if (!kDqFirst && group) dq_group(gfirst, G);
@@ -688,31 +707,53 @@ struct BwdKernel {
   static_assert((NW - 2) * SLOT_BYTES <= NDS * DS_BYTES && SLOT_BYTES <= QT_BYTES,
                 "epilogue slots must fit in the free query buffers and the dS^T slots");
   static constexpr int EPI_STORES = 2 * (D / 16);   // store instructions of one epilogue
+  static_assert(!RTAB || SLOT_BYTES >= 2 * 32 * 32 * 4, "the slot holds dK's second table rows");
   __device__ __forceinline__ char* epilogue_slot(int free_buf) const {
     if (wave == 0) return smem + OFF_Q + free_buf * QT_BYTES;
     if (wave == 1) return smem + OFF_DO + free_buf * QT_BYTES;
     return smem + OFF_DS + (wave - 2) * SLOT_BYTES;
   }
 
+  // Copies the (cos, sin) table rows of the query block in buffer `buf` (its rows'
+  // positions are in LDS since the barrier that published the block) for this wave's
+  // 32 columns, 32 dq_dt .. 32 dq_dt + 31, into the wave's table region: copy i takes
+  // rows 8 i .. 8 i + 7, lane l row 8 i + l / 8 and columns 4 (l % 8) .. + 3.  Only
+  // this wave reads the region, after its own wait for these loads.
+  __device__ __forceinline__ void issue_rope_tables(int buf) {
+    if constexpr (RTAB) {
+      const int* pos = reinterpret_cast<const int*>(smem + OFF_RPOS + buf * 256);
+      const uint32_t l = launder((uint32_t)lane);
+      const uint32_t col = (uint32_t)(32 * dq_dt) + 4u * (l & 7);
+      const uint32_t bytes = (uint32_t)min((int64_t)a.rope_max_pos * (D / 2) * 4, (int64_t)0xFFFFFFFF);
+      const u32x4 rc = make_rsrc_sgpr(a.rope_cos, bytes), rsn = make_rsrc_sgpr(a.rope_sin, bytes);
+      const uint32_t dst = lds0 + (uint32_t)(OFF_RTAB + wave * RTAB_WAVE);
+#pragma unroll
+      for (int i = 0; i < BQ / 8; ++i) {
+        const int p = min(max(pos[8 * i + (int)(l >> 3)], 0), a.rope_max_pos - 1);
+        const uint32_t voff = ((uint32_t)p * (uint32_t)(D / 2) + col) * 4u;   // < 2^32 for max_pos <= 2^24
+        lds_load16_at(rc, voff, dst + (uint32_t)(i * 1024));
+        lds_load16_at(rsn, voff, dst + (uint32_t)(BQ * 32 * 4 + i * 1024));
+      }
+    }
+  }
+
   // Rotary conjugate of a query block's dQ in the single-tile path, where the tile
   // stores dQ itself: with two d tiles per wave, register r of dq[0] and dq[1] holds
   // columns d = 32 dq_dt + lane % 32 and d + D / 2 of row
-  // 8 (r / 4) + 4 (lane / 32) + r % 4 (the MFMA C layout), the rotated pair.
-  __device__ __forceinline__ void rope_conjugate_dq(f32x16 (&dq)[DTW], int qi0) {
-    const int d = 32 * dq_dt + c32;
-    // eight rows at a time (their 16 table values live together; the kernel has
-    // little register room here)
+  // 8 (r / 4) + 4 (lane / 32) + r % 4 (the MFMA C layout), the rotated pair; the
+  // (cos, sin) entries of (row, d) are in the wave's table region.
+  __device__ __forceinline__ void rope_conjugate_dq(f32x16 (&dq)[DTW]) {
+    const float* tc = reinterpret_cast<const float*>(smem + OFF_RTAB + wave * RTAB_WAVE) + c32;
+    const float* ts = tc + BQ * 32;
 #pragma unroll
     for (int r0 = 0; r0 < 16; r0 += 8) {
       float c[8], sn[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int r = r0 + i;
-        const int row = qi0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        int pos = row < q_rows ? a.rope_pos_q[kv0 + row] : 0;
-        pos = min(max(pos, 0), a.rope_max_pos - 1);
-        c[i] = a.rope_cos[(int64_t)pos * (D / 2) + d];
-        sn[i] = a.rope_sin[(int64_t)pos * (D / 2) + d];
+        const int row = 8 * (r >> 2) + 4 * hf + (r & 3);
+        c[i] = tc[row * 32];
+        sn[i] = ts[row * 32];
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -725,6 +766,51 @@ struct BwdKernel {
     }
   }
 
+  // Copies the (cos, sin) table rows of this wave's 32 keys (positions kpos; lane
+  // c32 holds key c32), columns 32 cp .. 32 cp + 31, to the LDS address dst: cos, then
+  // sin 4 KB further, each [32 keys][8 chunks of 4 columns] with chunk c of key r at
+  // slot c ^ (r & 7), so that the rotation's reads of one chunk for 32 keys spread
+  // over the banks.  Copy i takes keys 8 i .. 8 i + 7: lane l fills slot l % 8 of key
+  // 8 i + l / 8.
+  __device__ __forceinline__ void issue_rope_k_tables(uint32_t dst, int cp) {
+    if constexpr (RTAB) {
+      const uint32_t l = launder((uint32_t)lane);
+      const uint32_t bytes = (uint32_t)min((int64_t)a.rope_max_pos * (D / 2) * 4, (int64_t)0xFFFFFFFF);
+      const u32x4 rc = make_rsrc_sgpr(a.rope_cos, bytes), rsn = make_rsrc_sgpr(a.rope_sin, bytes);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 8 * i + (int)(l >> 3);
+        const int p = min(max(__shfl(kpos, r), 0), a.rope_max_pos - 1);
+        const uint32_t c = (l & 7) ^ (uint32_t)(r & 7);
+        const uint32_t voff = ((uint32_t)p * (uint32_t)(D / 2) + 32u * (uint32_t)cp + 4u * c) * 4u;
+        lds_load16_at(rc, voff, dst + (uint32_t)(i * 1024));
+        lds_load16_at(rsn, voff, dst + (uint32_t)(4096 + i * 1024));
+      }
+    }
+  }
+  // The conjugate of dK^T (as rope_conjugate_dk) with the table rows of d tiles
+  // (0, 2) at t0 and of d tiles (1, 3) at t1, laid out by issue_rope_k_tables.
+  __device__ __forceinline__ void rope_conjugate_dk_lds(const char* t0, const char* t1) {
+#pragma unroll
+    for (int dt = 0; dt < DT / 2; ++dt) {
+      const char* t = dt == 0 ? t0 : t1;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int chunk = 2 * q4 + hf;   // columns 8 q4 + 4 hf .. + 3 of the pair's 32
+        const int off = c32 * 128 + ((chunk ^ (c32 & 7)) << 4);
+        const f32x4 c4 = *reinterpret_cast<const f32x4*>(t + off);
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(t + 4096 + off);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q4 + e;
+          const float lo = dkt[dt][r], hi = dkt[dt + DT / 2][r];
+          dkt[dt][r] = lo * c4[e] + hi * s4[e];
+          dkt[dt + DT / 2][r] = hi * c4[e] - lo * s4[e];
+        }
+      }
+    }
+  }
+
   // Rotary conjugate of this wave's dK^T accumulators, in fp32 before the bf16
   // rounding ("Meta's TLX Block Attention Beats Flash Attention v2 by 2.3x on
   // Blackwell GPUs", section "The Rotary Fusion Bonus").  The pair (d, d + D/2) of
@@ -734,8 +820,11 @@ struct BwdKernel {
   // d = 32 dt + 8 (r / 4) + 4 (lane / 32) + r % 4, so four consecutive table entries
   // serve four registers.
   __device__ __forceinline__ void rope_conjugate_dk() {
-    const int j = j0 + 32 * wave + c32;
-    int pos = j < n ? a.rope_pos_k[kv0 + j] : 0;
+    int pos = kpos;
+    if constexpr (!RTAB) {   // (the multi-tile variants have no register to hold it across the tile)
+      const int j = j0 + 32 * wave + c32;
+      pos = j < n ? a.rope_pos_k[kv0 + j] : 0;
+    }
     pos = min(max(pos, 0), a.rope_max_pos - 1);
     const float* cr = a.rope_cos + (int64_t)pos * (D / 2);
     const float* sr = a.rope_sin + (int64_t)pos * (D / 2);
@@ -743,21 +832,25 @@ struct BwdKernel {
     // (the epilogue holds little register room)
 #pragma unroll
     for (int dt = 0; dt < DT / 2; ++dt) {
-      f32x4 c4[4], s4[4];
+      constexpr int QG = RTAB ? 4 : 2;   // table quads loaded together (fewer where registers are short)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * dt + 8 * q4 + 4 * hf;
-        c4[q4] = *reinterpret_cast<const f32x4*>(cr + d0);
-        s4[q4] = *reinterpret_cast<const f32x4*>(sr + d0);
-      }
+      for (int qg = 0; qg < 4; qg += QG) {
+        f32x4 c4[QG], s4[QG];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float c = c4[r / 4][r % 4], sn = s4[r / 4][r % 4];
-        const float lo = dkt[dt][r], hi = dkt[dt + DT / 2][r];
-        dkt[dt][r] = lo * c + hi * sn;
-        dkt[dt + DT / 2][r] = hi * c - lo * sn;
+        for (int k = 0; k < QG; ++k) {
+          const int d0 = 32 * dt + 8 * (qg + k) + 4 * hf;
+          c4[k] = *reinterpret_cast<const f32x4*>(cr + d0);
+          s4[k] = *reinterpret_cast<const f32x4*>(sr + d0);
+        }
+#pragma unroll
+        for (int r = 4 * qg; r < 4 * (qg + QG); ++r) {
+          const float c = c4[r / 4 - qg][r % 4], sn = s4[r / 4 - qg][r % 4];
+          const float lo = dkt[dt][r], hi = dkt[dt + DT / 2][r];
+          dkt[dt][r] = lo * c + hi * sn;
+          dkt[dt + DT / 2][r] = hi * c - lo * sn;
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -777,6 +870,10 @@ struct BwdKernel {
     active = 32 * wave < nvalid;
     q_rows = BCAST ? a.q_len : n;
     grow0 = BCAST ? (int64_t)g.b * a.q_len : kv0;
+    if constexpr (RTAB) {   // used by the epilogue: the load has the whole tile to land
+      const int j = j0 + 32 * wave + c32;
+      kpos = j < n ? a.rope_pos_k[kv0 + j] : 0;
+    }
 
     __syncthreads();   // the previous tile's epilogue is done with its LDS slots
     pre();
@@ -822,10 +919,27 @@ struct BwdKernel {
     run<false>(qm, qfull, q_last, gfirst, npend);
     run<true>(qfull, q_last, q_last, gfirst, npend);
     const bool more = next(ng);
+    char* slot = epilogue_slot(more ? first_qbuf(ng) ^ 1 : 0);
     constexpr bool kDqFirst = DIRECT && ROPE;   // as in run(): the table reads go first
     if (more && !kDqFirst) issue_v(ng);
+    if constexpr (RTAB) {
+      // dK's table rows of d tiles (1, 3) into the epilogue slot (free since the
+      // closing barrier: the next tile's first query block goes to the other buffer),
+      // then wait for everything before them, the last block's rows included
+      issue_rope_k_tables(lds_addr(slot), 1);
+      wait_vmcnt<8>();
+    }
     if (npend > 0) dq_group(gfirst, npend);   // the closing barrier published their dS^T
+    if constexpr (RTAB) issue_rope_k_tables(lds0 + (uint32_t)(OFF_RTAB + wave * RTAB_WAVE), 0);   // d tiles (0, 2)
     if (more && kDqFirst) issue_v(ng);
+    if constexpr (RTAB) {   // both copies (only the next tile's V fragment may stay in flight)
+      if (more) {
+        wait_vmcnt<KS>();
+      } else {
+        wait_lds_loads();
+      }
+      rope_conjugate_dk_lds(smem + OFF_RTAB + wave * RTAB_WAVE, slot);
+    }
     __syncthreads();   // every wave is past its last read of the K tile, dQ partials and query blocks
     if (more) {
       issue_k(ng);
@@ -835,9 +949,8 @@ struct BwdKernel {
     // dK = c dS^T Q and dV -> bf16 rows, staged through this wave's epilogue slot
     {
       const int nrows = min(max(n - (j0 + 32 * wave), 0), 32);
-      char* slot = epilogue_slot(more ? first_qbuf(ng) ^ 1 : 0);
       const int64_t off = (kv0 + j0 + 32 * wave) * rs + (int64_t)h * D;
-      if constexpr (ROPE) rope_conjugate_dk();
+      if constexpr (ROPE && !RTAB) rope_conjugate_dk();
       store_acc_rows<D, EPI_PASSES>(dkt, a.scale, slot, a.dk + off, rs, nrows, lane);
       store_acc_rows<D, EPI_PASSES>(dvt, 1.f, slot, a.dv + off, rs, nrows, lane);
     }
