@@ -98,23 +98,43 @@ def measured_traffic(kernel: str, workload: str):
     return (rec["fetch_kib"] * 1024 * rec["fetch_factor"] + rec["write_kib"] * 1024 * rec["write_factor"])
 
 
-def cpu_baseline(case, w, budget_s: float):
-    """The fp64 oracle on a bounded sample of sequences of the same workload."""
-    import oracle
+def host_info():
+    """The host the oracle runs on: logical CPUs, CPU model, BLAS library and threads."""
+    info = {"os_cpu_count": os.cpu_count(), "cpu_model": None, "blas": None, "blas_threads": None}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
-        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if pools:
+            info["blas"] = f"{pools[0].get('internal_api')} {pools[0].get('version')}"
+            info["blas_threads"] = max(int(p.get("num_threads", 1)) for p in pools)
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        pass
+    return info
+
+
+def cpu_baseline(case, w, budget_s: float):
+    """The fp64 oracle on a bounded sample of sequences of the same workload, forward
+    and backward timed apart (the useful-FLOP formula of the GPU figures; the oracle
+    does the full n x n work even when causal)."""
+    import oracle
+    host = host_info()
     off = case["offsets"].cpu().numpy().astype(np.int64)
     lengths = np.diff(off)
     rng = np.random.default_rng(1)
     order = rng.permutation(len(lengths))
     f64 = lambda t: t.to(torch.float64).numpy()  # noqa: E731
     q_host = f64(case["q"].cpu()) if w.broadcast_q else None
-    flops = 0.0
+    fwd_flops = bwd_flops = 0.0
+    t_fwd = t_bwd = 0.0
     used = 0
-    t0 = time.perf_counter()
     for b in order:
         a, e = int(off[b]), int(off[b + 1])
         r0, r1 = (b * w.q_len, (b + 1) * w.q_len) if w.broadcast_q else (a, e)
@@ -122,21 +142,33 @@ def cpu_baseline(case, w, budget_s: float):
             qb = q_host[:, h] if w.broadcast_q else f64(case["q"][a:e, h].cpu())
             kb, vb = f64(case["k"][a:e, h].cpu()), f64(case["v"][a:e, h].cpu())
             gb = f64(case["g"][r0:r1, h].cpu())
+            t0 = time.perf_counter()
             oracle.sequence_forward(qb, kb, vb, case["scale"], w.causal)
+            t1 = time.perf_counter()
             oracle.sequence_backward(qb, kb, vb, gb, case["scale"], w.causal)
+            t2 = time.perf_counter()
+            t_fwd += t1 - t0
+            t_bwd += t2 - t1
         f, bwd = useful_flops(w, [e - a])
-        flops += f + bwd
+        fwd_flops += f
+        bwd_flops += bwd
         used += 1
-        if time.perf_counter() - t0 >= budget_s:
+        if t_fwd + t_bwd >= budget_s:
             break
-    dt = time.perf_counter() - t0
+    dt = t_fwd + t_bwd
+    cores = host["blas_threads"] or host["os_cpu_count"] or 1
     return {
-        "value": flops / dt / 1e12,
+        "value": float((fwd_flops + bwd_flops) / dt / 1e12),
         "unit": "TFLOP/s",
         "cores": int(cores),
         "kind": "oracle",
         "sample": f"{used} of {len(lengths)} sequences (random, seed 1) x {w.heads} heads of "
                   f"{w.name}, fp64 numpy forward+backward, {dt:.1f} s",
+        "fwd_tflops": float(fwd_flops / max(t_fwd, 1e-12) / 1e12),
+        "bwd_tflops": float(bwd_flops / max(t_bwd, 1e-12) / 1e12),
+        "fwd_s": round(t_fwd, 3),
+        "bwd_s": round(t_bwd, 3),
+        "host": host,
     }
 
 

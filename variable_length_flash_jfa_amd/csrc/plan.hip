@@ -132,9 +132,14 @@ __device__ __forceinline__ int fwd_cost(const PlanFwdArgs& a, int64_t n, int m) 
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_fwd_kernel(PlanFwdArgs a) {
-  __shared__ int wave_sums[kPlanThreads / 64 + 1];
+  static_assert(kKeys == kPlanThreads, "one sort bucket per thread");
+  constexpr int kWaves = kPlanThreads / 64;
+  __shared__ int wave_sums[kWaves + 1];
   __shared__ int hist[kKeys];
   __shared__ int offs[kSeg + 1];
+  __shared__ int first_item[kPlanThreads];     // a segment's first item of each thread's run
+  __shared__ int wave_hist[kWaves][kKeys];     // per-wave counts of a chunk's items by cost
+  __shared__ int one_cost;
   const int tid = threadIdx.x;
   const int nseg = (a.batch + kSeg - 1) / kSeg;
   auto seq_len = [&](int b) { return (int64_t)(offs[b + 1] - offs[b]); };
@@ -180,34 +185,104 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fwd_kernel(PlanFwdArgs a) {
       }
     }
     __syncthreads();
-    // descending exclusive scan of the histogram: cursor[k] = #items with cost > k
-    {
-      const int k = kKeys - 1 - tid;
-      int tot = 0;
-      const int start = block_exclusive_scan(hist[k], wave_sums, &tot);
-      __syncthreads();
-      hist[k] = start;
-    }
+    // when every item has the same cost the natural order is the sorted order
+    if (tid == 0) one_cost = 0;
     __syncthreads();
-    // pass 2: scatter in cost order
-    for (int sg = 0; sg < nseg; ++sg) {
-      const Segment g = stage_segment(a.offsets, a.off64, a.batch, sg, offs);
-      int count = 0;
-      for (int b = g.bb; b < g.be; ++b) count += fwd_items_of(a, seq_len(b));
-      const int rounds = wave_max(count);
-      int b = g.bb, m = 0, mi = 0;
-      int64_t n = 0;
-      for (int r = 0; r < rounds; ++r) {
-        if (r < count) {
-          while (m >= mi) {
-            n = seq_len(b);
-            mi = fwd_items_of(a, n);
-            m = 0;
-            if (mi == 0) ++b;
+    if (hist[tid] == total) one_cost = 1;
+    __syncthreads();
+    if (one_cost) {
+      int base = 0;
+      for (int sg = 0; sg < nseg; ++sg) {
+        const Segment g = stage_segment(a.offsets, a.off64, a.batch, sg, offs);
+        int count = 0;
+        for (int b = g.bb; b < g.be; ++b) count += fwd_items_of(a, seq_len(b));
+        int tot = 0;
+        int pos = base + block_exclusive_scan(count, wave_sums, &tot);
+        for (int b = g.bb; b < g.be; ++b) {
+          const int mi = fwd_items_of(a, seq_len(b));
+          for (int m = 0; m < mi; ++m) a.items[pos++] = make_int4(g.b0 + b, m, offs[b], (int)seq_len(b));
+        }
+        base += tot;
+      }
+    } else {
+      // descending exclusive scan of the histogram: cursor[k] = #items with cost > k
+      {
+        const int k = kKeys - 1 - tid;
+        int tot = 0;
+        const int start = block_exclusive_scan(hist[k], wave_sums, &tot);
+        __syncthreads();
+        hist[k] = start;
+      }
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) wave_hist[w][tid] = 0;
+      __syncthreads();
+      // pass 2: a stable counting sort.  Each segment's items are taken 1024 at a time
+      // in (sequence, query block) order, one per thread; an item's place in its cost
+      // bucket is the bucket's running cursor, plus the chunk's items of that cost in
+      // lower waves, plus those in lower lanes of its own wave.  Equal costs thus keep
+      // (sequence, query block) order, and the tile order does not depend on timing.
+      const int lane = tid & 63, wv = tid >> 6;
+      for (int sg = 0; sg < nseg; ++sg) {
+        const Segment g = stage_segment(a.offsets, a.off64, a.batch, sg, offs);
+        const int per = (g.len + kPlanThreads - 1) / kPlanThreads;   // as in stage_segment
+        int count = 0;
+        for (int b = g.bb; b < g.be; ++b) count += fwd_items_of(a, seq_len(b));
+        int tot = 0;
+        first_item[tid] = block_exclusive_scan(count, wave_sums, &tot);
+        __syncthreads();
+        for (int c0 = 0; c0 < tot; c0 += kPlanThreads) {
+          const int i = c0 + tid;
+          int key = -1;
+          int4 item = make_int4(0, 0, 0, 0);
+          if (i < tot) {
+            // the thread whose run holds item i: the last one whose run starts at or before i
+            int lo = 0, hi = kPlanThreads - 1;
+            while (lo < hi) {
+              const int mid = (lo + hi + 1) >> 1;
+              if (first_item[mid] <= i) lo = mid; else hi = mid - 1;
+            }
+            int local = i - first_item[lo];
+            const int bb = min(g.len, lo * per), be = min(g.len, bb + per);
+            for (int b = bb; b < be; ++b) {
+              const int64_t n = seq_len(b);
+              const int mi = fwd_items_of(a, n);
+              if (local < mi) {
+                key = fwd_cost(a, n, local);
+                item = make_int4(g.b0 + b, local, offs[b], (int)n);
+                break;
+              }
+              local -= mi;
+            }
           }
-          const int pos = aggregated_increment(hist, fwd_cost(a, n, m));
-          a.items[pos] = make_int4(g.b0 + b, m, offs[b], (int)n);
-          if (++m >= mi) ++b;
+          // rank among the wave's items of the same cost, in lane order
+          unsigned long long pending = __ballot(key >= 0);
+          int rank = 0;
+          while (pending) {
+            const int leader = __ffsll((long long)pending) - 1;
+            const int lk = __shfl(key, leader);
+            const unsigned long long same = __ballot(key == lk) & pending;
+            if (key == lk) rank = __popcll(same & ((1ull << lane) - 1ull));
+            if (lane == leader) wave_hist[wv][lk] = __popcll(same);
+            pending &= ~same;
+          }
+          __syncthreads();
+          if (key >= 0) {
+            int before = 0;
+            for (int w = 0; w < wv; ++w) before += wave_hist[w][key];
+            a.items[hist[key] + before + rank] = item;
+          }
+          __syncthreads();
+          // advance the cursors past this chunk and clear its counts
+          {
+            int add = 0;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+              add += wave_hist[w][tid];
+              wave_hist[w][tid] = 0;
+            }
+            hist[tid] += add;
+          }
+          __syncthreads();
         }
       }
     }
