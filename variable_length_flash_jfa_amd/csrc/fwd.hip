@@ -198,14 +198,16 @@ struct FwdKernel {
   template <bool MASKED>
   __device__ __forceinline__ void mask_half(f32x16& s, int blk, int c) const {
     if constexpr (MASKED) {
-      const int64_t i = i0 + c32;
+      // Element r of the lane holds key x = 8 (r / 4) + 4 (lane / 32) + r % 4 of the
+      // half, visible when x < lim: keys before the sequence end and, causal, not
+      // after the lane's row.  Compared as r's constant part against lim - 4 (lane / 32),
+      // so that no per-element key index is kept in registers.
+      const int jb = blk * BN + 32 * c;
+      int lim = min(g.n - jb, 64);
+      if constexpr (CAUSAL) lim = min(lim, i0 + c32 - jb + 1);
+      const int L = max(lim, 0) - 4 * hf;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t j = (int64_t)blk * BN + 32 * c + 8 * (r >> 2) + 4 * hf + (r & 3);
-        bool vis = j < g.n;
-        if constexpr (CAUSAL) vis = vis && (j <= i);
-        s[r] = vis ? s[r] : -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r) s[r] = 8 * (r >> 2) + (r & 3) < L ? s[r] : -INFINITY;
     }
   }
   // As a tree of depth three (a serial chain would hold the wave for its whole
@@ -239,6 +241,9 @@ struct FwdKernel {
   }
   // P of elements [lo, hi) of a half: keys 16 kc + 8 (e / 4) + 4 (lane / 32) + e % 4
   // of the half for element 8 kc + e.
+  // The empty asm keeps the results where the unit stands: otherwise the compiler
+  // sinks half 1's exponentials past the rescale branch that precedes O += P1 V1,
+  // out of the phase they were given.
   __device__ __forceinline__ void half_exp(const f32x16& s, bf16x8 (&p)[2], int lo, int hi) {
 #pragma unroll
     for (int r = lo; r < hi; ++r) {
@@ -246,6 +251,7 @@ struct FwdKernel {
       (r & 1 ? lsum2 : lsum) += pv;
       p[r >> 3][r & 7] = (bf16)pv;
     }
+    asm volatile("" : "+v"(p[lo >> 3]), "+v"(lsum), "+v"(lsum2));
   }
 
   // Softmax units, coded 32 half + 8 kind + pair: kind 0 mask and maximum, 1 rescale
