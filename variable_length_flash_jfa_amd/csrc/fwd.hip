@@ -114,8 +114,6 @@ struct FwdKernel {
     lds0 = lds_addr(smem);
   }
 
-  __device__ __forceinline__ char* kbuf(int buf) { return smem + (buf * 2 + 0) * TILE_BYTES; }
-  __device__ __forceinline__ char* vbuf(int buf) { return smem + (buf * 2 + 1) * TILE_BYTES; }
 
   // Tile idx of the list: item `it` = (sequence, query block, first row, length).
   __device__ __forceinline__ Geo geometry(int idx, int4 it, int per_item) const {
@@ -181,7 +179,7 @@ struct FwdKernel {
   // instructions), so the softmax is spread over the block's four MFMA phases:
   //   S0 = K0 Q^T                  (MFMA only)
   //   S1 = K1 Q^T                  half 0: mask, maximum, rescale test, exp2 of
-  //                                its first 12 keys (S1 as two independent chains)
+  //                                its first 12 keys
   //   O^T += V0^T P0^T             half 0: last 4 keys (their P is needed from the
   //                                second half of this phase on); half 1: mask,
   //                                maximum, rescale test, first 16 keys
@@ -211,12 +209,21 @@ struct FwdKernel {
     }
   }
   // As a tree of depth three (a serial chain would hold the wave for its whole
-  // latency while the MFMAs of the other half wait behind it).
+  // latency while the MFMAs of the other half wait behind it), in eight
+  // three-input maxima.  Written as v_max3_f32 directly: through fmaxf the compiler
+  // first quiets every MFMA result (a v_max of the value with itself) in case it
+  // is a signalling NaN, which doubles the count; scores from finite inputs are
+  // never NaN, and a NaN input would reach O through the products anyway.
+  __device__ __forceinline__ static float max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+  }
   __device__ __forceinline__ static float half_max(const f32x16& s) {
     float m[5];
 #pragma unroll
-    for (int k = 0; k < 5; ++k) m[k] = fmaxf(fmaxf(s[3 * k], s[3 * k + 1]), s[3 * k + 2]);
-    return fmaxf(fmaxf(fmaxf(m[0], m[1]), m[2]), fmaxf(fmaxf(m[3], m[4]), s[15]));
+    for (int k = 0; k < 5; ++k) m[k] = max3(s[3 * k], s[3 * k + 1], s[3 * k + 2]);
+    return max3(max3(m[0], m[1], m[2]), max3(m[3], m[4], s[15]), s[15]);
   }
   // Rescale test of a half whose lane maximum is mx; returns the factor O must be
   // multiplied by when `moved` (row sums are rescaled here).
@@ -264,19 +271,19 @@ struct FwdKernel {
 
   template <bool MASKED>
   __device__ __forceinline__ void compute_block(int buf, int blk) {
-    const char* kb = kbuf(buf);
-    const char* vb = vbuf(buf);
-    const uint32_t krb = launder(k_row_base);
-    const uint32_t vtb = launder(v_tr_base);
+    // The buffer's offset (a multiple of 16 KB) is added to the lane bases once: the
+    // swizzle's XORs touch only bits below 9, so (base + offset) ^ x equals
+    // (base ^ x) + offset, and each operand read costs one XOR.
+    const uint32_t krb = launder(k_row_base + (uint32_t)(buf * 2 * TILE_BYTES));
+    const uint32_t vtb = launder(v_tr_base + (uint32_t)((buf * 2 + 1) * TILE_BYTES));
     // K operand of half c, k step ks; V^T operand of O step i (keys 16 (i / DT), d
     // tile i % DT).  Operands are read PF_S (PF_V) MFMA steps ahead; the scheduling
     // fences keep that pipeline, and the interleaving, as written.
-    auto kop = [&](int i) { return lds_read8(kb, row_read_addr(krb, i % KS) + 32 * (i / KS) * 2 * D); };
-    auto vop = [&](int i) { return lds_operand_tr<D>(vb, vtb, 16 * (i / DT), 16 * (i / DT) + 8, i % DT); };
-    // S1 runs as two chains (even and odd k steps) so that its MFMAs do not wait on
-    // each other while half 0's softmax is issued between them; they are added
-    // before half 1's maximum.
-    f32x16 s0 = zero16(), s1 = zero16(), s1b = zero16();
+    auto kop = [&](int i) { return lds_read8(smem, row_read_addr(krb, i % KS) + 32 * (i / KS) * 2 * D); };
+    auto vop = [&](int i) { return lds_operand_tr<D>(smem, vtb, 16 * (i / DT), 16 * (i / DT) + 8, i % DT); };
+    // S1 is one chain: the other wave of the SIMD fills the MFMA pipe while a step
+    // waits for the one before it.
+    f32x16 s0 = zero16(), s1 = zero16();
     bf16x8 p[2][2];
     bf16x8 vr[PF_V + 1];
     float mx0 = 0.f, mx1 = 0.f, alpha1 = 1.f;
@@ -285,10 +292,6 @@ struct FwdKernel {
       const int c = code >> 5, kind = (code >> 3) & 3, pair = code & 7;
       f32x16& s = c == 0 ? s0 : s1;
       if (kind == 0) {
-        if (c == 1) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s1[r] += s1b[r];
-        }
         mask_half<MASKED>(s, blk, c);
         (c == 0 ? mx0 : mx1) = half_max(s);
       } else if (kind == 1) {
@@ -316,11 +319,7 @@ struct FwdKernel {
           s0 = mfma32(kr[i % (PF_S + 1)], qf[i], s0);
         } else {
           const int k = i - KS;
-          if (k & 1) {
-            s1b = mfma32(kr[i % (PF_S + 1)], qf[k], s1b);
-          } else {
-            s1 = mfma32(kr[i % (PF_S + 1)], qf[k], s1);
-          }
+          s1 = mfma32(kr[i % (PF_S + 1)], qf[k], s1);
 #pragma unroll
           for (int u = k * 8 / KS; u < (k + 1) * 8 / KS; ++u) unit(unit_b(u));
         }
