@@ -128,7 +128,7 @@ struct BwdArgs {
 
 // LDS offsets below are byte offsets from the start of the kernel's LDS block.  A
 // lane's part of every access pattern lives in one VGPR; runtime tile offsets
-// (buffer parity, wave, key part) are multiples of 256 (128 for D = 64) and are
+// (buffer parity, wave, dS^T slot) are multiples of 256 (128 for D = 64) and are
 // added to that VGPR once, which commutes with the per-read XOR of the swizzle
 // (the XOR only touches the low 8 (7) bits).  Each read then costs at most one
 // XOR and its constant part rides in the instruction's offset field.
@@ -486,7 +486,9 @@ struct BwdKernel {
                  lds_read_tr(smem + ((dsb ^ x ^ 8u) + (jj + 4) * (BQ * 2))));
     };
     if constexpr (DTW == 1) {
-      f32x16 acc0 = zero16(), acc1 = zero16();
+      // one chain: the other wave of the SIMD fills the MFMA pipe while a step waits
+      // for the one before it (two chains cost 16 adds to merge)
+      f32x16 acc = zero16();
       bf16x8 sa = ds_op(0);
       bf16x8 kb = lds_operand_tr<D>(smem, kb8, 0, 4, 0);
 #pragma unroll
@@ -496,19 +498,12 @@ struct BwdKernel {
           sa_n = ds_op(jj + 16);
           kb_n = lds_operand_tr<D>(smem, kb8, jj + 16, jj + 20, 0);
         }
-        // two independent accumulators halve the dependent-MFMA chain
-        if ((jj / 16) & 1) {
-          acc1 = mfma32(sa, kb, acc1);
-        } else {
-          acc0 = mfma32(sa, kb, acc0);
-        }
+        acc = mfma32(sa, kb, acc);
         sa = sa_n;
         kb = kb_n;
         __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc0[r] += acc1[r];
-      out[0] = acc0;
+      out[0] = acc;
     } else {
       // two d tiles, dq_dt and dq_dt + DT / 2 = dq_dt + 2 (an XOR of the chunk index
       // with 8, since dq_dt < 2), so that a lane holds columns d and d + D / 2 of its
