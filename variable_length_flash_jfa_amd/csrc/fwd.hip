@@ -182,10 +182,14 @@ struct FwdKernel {
   //                                its first 12 keys
   //   O^T += V0^T P0^T             half 0: last 4 keys (their P is needed from the
   //                                second half of this phase on); half 1: mask,
-  //                                maximum, rescale test, first 16 keys
-  //   O^T += V1^T P1^T             half 1: last 16 keys (needed from the second
+  //                                maximum, rescale test, first 10 keys
+  //   O^T += V1^T P1^T             half 1: last 6 keys (needed from the second
   //                                half of this phase on), after half 1's rescale
   //                                of O, if it made one
+  // Each pair of keys takes two MFMA slots: its exponentials in one, their row sums
+  // and bf16 P in the next, so that no instruction waits on the exponential just
+  // issued (a wave issues in order, and a stalled vector instruction also holds
+  // back the wave's next MFMA).
   // Lazy rescaling: the running max of a row moves only when some row of the wave
   // sees a score above its running max by more than 2^kLazyLog2 (a wave-uniform
   // test), so O and the row sums are rescaled rarely; otherwise P is taken against
@@ -246,28 +250,51 @@ struct FwdKernel {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
   }
-  // P of elements [lo, hi) of a half: keys 16 kc + 8 (e / 4) + 4 (lane / 32) + e % 4
-  // of the half for element 8 kc + e.
-  // The empty asm keeps the results where the unit stands: otherwise the compiler
-  // sinks half 1's exponentials past the rescale branch that precedes O += P1 V1,
-  // out of the phase they were given.
-  __device__ __forceinline__ void half_exp(const f32x16& s, bf16x8 (&p)[2], int lo, int hi) {
-#pragma unroll
-    for (int r = lo; r < hi; ++r) {
-      const float pv = fast_exp2(fmaf(s[r], a.scale_log2, -mrun));
-      (r & 1 ? lsum2 : lsum) += pv;
-      p[r >> 3][r & 7] = (bf16)pv;
-    }
-    asm volatile("" : "+v"(p[lo >> 3]), "+v"(lsum), "+v"(lsum2));
+  // Elements 2q and 2q + 1 of a half (keys 16 kc + 8 (e / 4) + 4 (lane / 32) + e % 4
+  // of the half for element 8 kc + e): first exp2 of the scaled, shifted score in
+  // place, later the row sums and the bf16 P.  The empty asm keeps each stage in the
+  // slot the schedule gives it: otherwise the compiler sinks the exponentials past
+  // the rescale branches, behind the MFMAs they were meant to run beside.
+  __device__ __forceinline__ void pair_exp(f32x16& s, int q) {
+    float e0 = fast_exp2(fmaf(s[2 * q], a.scale_log2, -mrun));
+    float e1 = fast_exp2(fmaf(s[2 * q + 1], a.scale_log2, -mrun));
+    asm volatile("" : "+v"(e0), "+v"(e1));
+    s[2 * q] = e0;
+    s[2 * q + 1] = e1;
+  }
+  __device__ __forceinline__ void pair_sum(const f32x16& s, bf16x8 (&p)[2], int q) {
+    lsum += s[2 * q];
+    lsum2 += s[2 * q + 1];
+    p[q >> 2][(2 * q) & 7] = (bf16)s[2 * q];
+    p[q >> 2][(2 * q + 1) & 7] = (bf16)s[2 * q + 1];
+    asm volatile("" : "+v"(p[q >> 2]), "+v"(lsum), "+v"(lsum2));
   }
 
-  // Softmax units, coded 32 half + 8 kind + pair: kind 0 mask and maximum, 1 rescale
-  // test, 2 exp2 of elements 2 pair and 2 pair + 1.  Phase B runs units 0..7 over
-  // the KS MFMA steps of S1, phase C units 0..7 over the 2 DT steps of O += P0 V0,
-  // phase D units 0..3 over the first DT steps of O += P1 V1.
-  static constexpr int unit_b(int u) { return u < 2 ? 8 * u : 16 + (u - 2); }
-  static constexpr int unit_c(int u) { return u < 2 ? 16 + 6 + u : (u < 4 ? 32 + 8 * (u - 2) : 48 + (u - 4)); }
-  static constexpr int unit_d(int u) { return 48 + 4 + u; }
+  // Softmax work of MFMA slot s8 (0..7, eight per phase; with D = 64 a slot takes
+  // two) of phase ph (0: S1, 1: O += P0 V0, 2: O += P1 V1), as bits: 0..7 exps of
+  // half 0's pairs, 8..15 of half 1's, 16..23 sums of half 0's pairs, 24..31 of
+  // half 1's, 32 / 33 mask and maximum / rescale test of half 0, 34 / 35 of half 1.
+  // A pair's sums come one slot after its exps; a half's P is complete before the
+  // first O product that reads it, and every sum of half 0 is in before half 1's
+  // rescale test multiplies the row sums.
+  static constexpr uint64_t slot_acts(int ph, int s8) {
+    auto fe = [](int h, int q) { return uint64_t(1) << (8 * h + q); };
+    auto cs = [](int h, int q) { return uint64_t(1) << (16 + 8 * h + q); };
+    if (ph == 0) {
+      if (s8 == 0) return uint64_t(1) << 32;
+      if (s8 == 1) return uint64_t(1) << 33;
+      return fe(0, s8 - 2) | (s8 >= 3 ? cs(0, s8 - 3) : 0);
+    }
+    if (ph == 1) {
+      if (s8 == 0) return cs(0, 5) | fe(0, 6) | fe(0, 7);
+      if (s8 == 1) return cs(0, 6) | cs(0, 7) | (uint64_t(1) << 34);
+      if (s8 == 2) return uint64_t(1) << 35;
+      return fe(1, s8 - 3) | (s8 >= 4 ? cs(1, s8 - 4) : 0);
+    }
+    if (s8 < 3) return cs(1, s8 + 4) | fe(1, s8 + 5);
+    if (s8 == 3) return cs(1, 7);
+    return 0;
+  }
 
   template <bool MASKED>
   __device__ __forceinline__ void compute_block(int buf, int blk) {
@@ -288,23 +315,37 @@ struct FwdKernel {
     bf16x8 vr[PF_V + 1];
     float mx0 = 0.f, mx1 = 0.f, alpha1 = 1.f;
     bool moved1 = false;
-    auto unit = [&](int code) {
-      const int c = code >> 5, kind = (code >> 3) & 3, pair = code & 7;
-      f32x16& s = c == 0 ? s0 : s1;
-      if (kind == 0) {
-        mask_half<MASKED>(s, blk, c);
-        (c == 0 ? mx0 : mx1) = half_max(s);
-      } else if (kind == 1) {
-        if (c == 0) {
-          bool moved;
-          const float alpha = rescale_test(mx0, moved);
-          if (moved) scale_acc(alpha);
-        } else {   // applied once the O += P0 V0 products are issued
-          alpha1 = rescale_test(mx1, moved1);
-        }
-      } else {
-        half_exp(s, p[c], 2 * pair, 2 * pair + 2);
+    auto slot = [&](int ph, int s8) {
+      const uint64_t A = slot_acts(ph, s8);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if ((A >> (16 + q)) & 1) pair_sum(s0, p[0], q);
+        if ((A >> (24 + q)) & 1) pair_sum(s1, p[1], q);
       }
+      if ((A >> 32) & 1) {
+        mask_half<MASKED>(s0, blk, 0);
+        mx0 = half_max(s0);
+      }
+      if ((A >> 33) & 1) {
+        bool moved;
+        const float alpha = rescale_test(mx0, moved);
+        if (moved) scale_acc(alpha);
+      }
+      if ((A >> 34) & 1) {
+        mask_half<MASKED>(s1, blk, 1);
+        mx1 = half_max(s1);
+      }
+      if ((A >> 35) & 1) alpha1 = rescale_test(mx1, moved1);   // applied once O += P0 V0 is issued
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if ((A >> q) & 1) pair_exp(s0, q);
+        if ((A >> (8 + q)) & 1) pair_exp(s1, q);
+      }
+    };
+    // MFMA step k of a phase with n steps covers slots [8 k / n, 8 (k + 1) / n)
+    auto slots = [&](int ph, int k, int n) {
+#pragma unroll
+      for (int s8 = 8 * k / n; s8 < 8 * (k + 1) / n; ++s8) slot(ph, s8);
     };
     {
       bf16x8 kr[PF_S + 1];
@@ -320,8 +361,7 @@ struct FwdKernel {
         } else {
           const int k = i - KS;
           s1 = mfma32(kr[i % (PF_S + 1)], qf[k], s1);
-#pragma unroll
-          for (int u = k * 8 / KS; u < (k + 1) * 8 / KS; ++u) unit(unit_b(u));
+          slots(0, k, KS);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -334,12 +374,9 @@ struct FwdKernel {
       const int ckc = i / DT;
       acc[i % DT] = mfma32(vr[i % (PF_V + 1)], p[ckc / 2][ckc % 2], acc[i % DT]);
       if (i < 2 * DT) {
-#pragma unroll
-        for (int u = i * 8 / (2 * DT); u < (i + 1) * 8 / (2 * DT); ++u) unit(unit_c(u));
-      } else if (i < 3 * DT) {
-        const int k = i - 2 * DT;
-#pragma unroll
-        for (int u = k * 4 / DT; u < (k + 1) * 4 / DT; ++u) unit(unit_d(u));
+        slots(1, i, 2 * DT);
+      } else {
+        slots(2, i - 2 * DT, 2 * DT);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
