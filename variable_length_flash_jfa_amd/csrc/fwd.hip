@@ -213,21 +213,17 @@ struct FwdKernel {
     }
   }
   // As a tree of depth three (a serial chain would hold the wave for its whole
-  // latency while the MFMAs of the other half wait behind it), in eight
-  // three-input maxima.  Written as v_max3_f32 directly: through fmaxf the compiler
-  // first quiets every MFMA result (a v_max of the value with itself) in case it
-  // is a signalling NaN, which doubles the count; scores from finite inputs are
-  // never NaN, and a NaN input would reach O through the products anyway.
-  __device__ __forceinline__ static float max3(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-  }
+  // latency while the MFMAs of the other half wait behind it), which the compiler
+  // emits as eight three-input maxima.  This file is compiled with
+  // -fno-honor-nans: otherwise every MFMA result is first quieted (a v_max of the
+  // value with itself) in case it is a signalling NaN, which doubles the count.
+  // Scores from finite inputs are never NaN, and a NaN input reaches O through the
+  // products anyway.
   __device__ __forceinline__ static float half_max(const f32x16& s) {
     float m[5];
 #pragma unroll
-    for (int k = 0; k < 5; ++k) m[k] = max3(s[3 * k], s[3 * k + 1], s[3 * k + 2]);
-    return max3(max3(m[0], m[1], m[2]), max3(m[3], m[4], s[15]), s[15]);
+    for (int k = 0; k < 5; ++k) m[k] = fmaxf(fmaxf(s[3 * k], s[3 * k + 1]), s[3 * k + 2]);
+    return fmaxf(fmaxf(fmaxf(m[0], m[1]), m[2]), fmaxf(fmaxf(m[3], m[4]), s[15]));
   }
   // Rescale test of a half whose lane maximum is mx; returns the factor O must be
   // multiplied by when `moved` (row sums are rescaled here).

@@ -55,13 +55,9 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
 // Value of x held by lane (l ^ 32), combined with x by max / sum, via the gfx950
 // cross-half swap (lanes < 32 see the upper half in element 1, lanes >= 32 see
 // the lower half in element 0; the other element keeps the lane's own value).
-// (The maximum is a plain v_max_f32: through fmaxf the compiler would first quiet
-// both operands, in case they are signalling NaNs, with two more instructions.)
 __device__ __forceinline__ float max_across_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  float m;
-  asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(__uint_as_float(r[0])), "v"(__uint_as_float(r[1])));
-  return m;
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_across_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

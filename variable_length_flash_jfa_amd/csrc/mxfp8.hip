@@ -348,12 +348,16 @@ __global__ __launch_bounds__(64 * NW) void fwd_mx_kernel(MxArgs a) {
         }
         // raw-score maxima of the two 32-key halves of column li (c2 > 0 and rounding
         // are monotone, so the base-2 maximum is this maximum times c2)
+        // (a tree, emitted as three-input maxima: a serial chain of 15 would stall the
+        // wave on each step; with -fno-honor-nans the MFMA results are not first
+        // quieted)
         float smax[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-          float mx = st[rb][0];
+          float m[5];
 #pragma unroll
-          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[rb][r]);
+          for (int k = 0; k < 5; ++k) m[k] = fmaxf(fmaxf(st[rb][3 * k], st[rb][3 * k + 1]), st[rb][3 * k + 2]);
+          const float mx = fmaxf(fmaxf(fmaxf(m[0], m[1]), m[2]), fmaxf(fmaxf(m[3], m[4]), st[rb][15]));
           smax[rb] = fmaxf(mx, __shfl_xor(mx, 32));
         }
         const float mnew = fmaxf(mrun, ceilf(fmaxf(smax[0], smax[1]) * a.c2));
@@ -376,13 +380,13 @@ __global__ __launch_bounds__(64 * NW) void fwd_mx_kernel(MxArgs a) {
           pcode[rb] = mx_scale_code(fast_exp2(fmaf(smax[rb], a.c2, -msub)));
           const float off = msub + (float)(pcode[rb] - 127);
           float y[16];
-          float ys = 0.f;
+          float ysum[4] = {0.f, 0.f, 0.f, 0.f};   // four short chains instead of one of 16 adds
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             y[r] = fast_exp2(fmaf(st[rb][r], a.c2, -off));
-            ys += y[r];
+            ysum[r & 3] += y[r];
           }
-          lrun += ldexpf(ys, pcode[rb] - 127);
+          lrun += ldexpf((ysum[0] + ysum[1]) + (ysum[2] + ysum[3]), pcode[rb] - 127);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             pf[4 * rb + e] = pack4_e4m3(y[4 * e], y[4 * e + 1], y[4 * e + 2], y[4 * e + 3]);
