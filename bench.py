@@ -185,31 +185,38 @@ def sparse_comparison(args, jfa, w, case, o, lse, ws_f):
     qblocks = ((w.q_len + 255) // 256) * np.ones_like(lengths) if bq else (lengths + 127) // 128
     stream = torch.cuda.current_stream()
 
-    def timed(fn):
+    kernels = {}
+
+    def timed(fn, name):
         for _ in range(args.warmup):
             fn()
         torch.cuda.synchronize()
+        jfa.profile_enable(True)
+        jfa.profile_read()
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record(stream)
         for _ in range(args.steps):
             fn()
         stop.record(stream)
         torch.cuda.synchronize()
+        kernels[name] = {k_: round(v_[0] / v_[1], 4) for k_, v_ in jfa.profile_read().items()}
+        jfa.profile_enable(False)
         return round(start.elapsed_time(stop) / args.steps, 4)
 
     res = {"dense": timed(lambda: jfa.fwd(q, k, v, off, broadcast_q=bq, scale=scale, out=o, lse=lse,
-                                          workspace=ws_f))}
+                                          workspace=ws_f), "dense")}
     kept = {}
     for kk in [int(x) for x in args.sparse.split(",")]:
         sizes = (len(lengths), w.heads, w.head_dim, w.q_len if bq else 0, int(lengths.sum()), bq, kk)
         ws = torch.empty(jfa._binding.library().jfa_fwd_sparse_workspace_size(*sizes), dtype=torch.uint8,
                          device=q.device)
         res[f"sparse_k{kk}"] = timed(lambda: jfa.fwd_sparse(q, k, v, off, broadcast_q=bq, topk=kk,
-                                                            scale=scale, out=o, lse=lse, workspace=ws))
+                                                            scale=scale, out=o, lse=lse, workspace=ws),
+                                     f"sparse_k{kk}")
         kept[f"k{kk}"] = round(float((np.minimum(nkv, kk) * qblocks).sum() / (nkv * qblocks).sum()), 4)
         log(f"k={kk}: {res[f'sparse_k{kk}']:.4f} ms, blocks kept {kept[f'k{kk}']:.3f}")
     print(json.dumps({"mode": "sparse", "workload": w.name, "steps": args.steps, "ms": res,
-                      "blocks_kept": kept,
+                      "kernel_ms": kernels, "blocks_kept": kept,
                       "speedup_over_dense": {k_: round(res["dense"] / v_, 4) for k_, v_ in res.items()
                                              if k_ != "dense"}}), flush=True)
 

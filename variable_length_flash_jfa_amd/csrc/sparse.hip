@@ -142,6 +142,11 @@ __device__ __forceinline__ bool ranks_before(float sa, int ja, float sb, int jb)
 template <int D>
 __global__ __launch_bounds__(256) void select_blocks_kernel(SelectArgs a) {
   __shared__ float pq_lds[4][D];
+  // each candidate's score, computed once (the first kScoreCache candidates; the
+  // rest, sequences past 65536 keys, are recomputed in every round): lane l writes
+  // and later reads only the entries l + 64 u, so the wave needs no barrier
+  constexpr int kScoreCache = 1024;
+  __shared__ float sc_lds[4][kScoreCache];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ntiles = a.meta[2];
@@ -180,6 +185,7 @@ __global__ __launch_bounds__(256) void select_blocks_kernel(SelectArgs a) {
       }
       return s * a.scale;
     };
+    for (int j = lane; j < min(nkv, kScoreCache); j += 64) sc_lds[w][j] = score(j);
     // k rounds; the blocks a lane owns are j = lane + 64 u, with their selection bits
     uint64_t mine = 0;   // bit u: block lane + 64 u selected (u < 64)
     float prev_s = INFINITY;
@@ -188,7 +194,7 @@ __global__ __launch_bounds__(256) void select_blocks_kernel(SelectArgs a) {
       float best_s = -INFINITY;
       int best_j = 0x7fffffff;
       for (int j = lane; j < nkv; j += 64) {
-        const float s = score(j);
+        const float s = j < kScoreCache ? sc_lds[w][j] : score(j);
         if (ranks_before(prev_s, prev_j, s, j) && ranks_before(s, j, best_s, best_j)) {
           best_s = s;
           best_j = j;
