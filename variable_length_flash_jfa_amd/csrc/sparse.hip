@@ -95,7 +95,18 @@ __global__ __launch_bounds__(256) void pool_blocks_kernel(const bf16* __restrict
   const int c = t % C, r = t / C;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (r < R) {
-    for (int64_t row = r; row < nr; row += R) {
+    // four rows' loads in flight at a time (the adds keep the row order)
+    int64_t row = r;
+    for (; row + 3 * R < nr; row += 4 * R) {
+      bf16x8 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const bf16x8*>(x + (r0 + row + u * R) * rs + 8 * c);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += (float)v[u][e];
+    }
+    for (; row < nr; row += R) {
       const bf16x8 v = *reinterpret_cast<const bf16x8*>(x + (r0 + row) * rs + 8 * c);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += (float)v[e];
