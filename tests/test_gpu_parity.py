@@ -127,6 +127,9 @@ SMALL_CASES = {
     "self_b1_d64": ([300], 3, 64, False, False, 0),
     "self_d128_causal_long_empty": ([900, 0, 1200, 1], 2, 128, False, True, 0),
     "self_d64_causal_long_empty": ([700, 0, 900], 3, 64, False, True, 0),
+    # a sequence longer than 65,536 keys: the forward plan's cost buckets saturate at
+    # 1023 blocks, one forward tile walks 1,094 key blocks, the backward 274 key tiles
+    "bcast_long_70k": ([70000, 5, 1000], 1, 128, True, False, 64),
 }
 
 
