@@ -50,6 +50,9 @@ struct FwdArgs {
   const int4* items;
   int* meta;
   int sched;
+  // broadcast mode, dynamic schedule: tile classes (query block, head), each with a
+  // counter of its own (0: one counter for all tiles)
+  int classes;
   // block-sparse forward: [tiles][topk] selected key blocks (ascending) per tile
   const int* tile_blocks;
   int topk;
@@ -443,7 +446,9 @@ struct FwdKernel {
       __syncthreads();
       if (has_next) load_block(nxt, first_next(), pb);
     }
-    if (has_next) load_q(nxt);   // this tile is done with its Q fragment
+    // this tile is done with its Q fragment; in broadcast mode the next tile keeps it
+    // when it has the same query block and head
+    if (has_next && !(BCAST && nxt.m == g.m && nxt.h == g.h)) load_q(nxt);
     between();
 
     // epilogue
@@ -462,6 +467,11 @@ struct FwdKernel {
 // index of tile r + 2 is claimed (or computed, for the static schedules) and, after
 // tile r's last block, its plan item is copied into LDS by a direct load, so that
 // tile r + 1's first K/V block and Q fragment can be issued during tile r.
+// Broadcast mode, dynamic schedule: the tiles of one (query block, head) class all
+// read the same Q fragment, and every class has the same work (each sequence's
+// tiles see all its keys).  With few classes, each workgroup serves one class,
+// claiming that class's tiles in plan order from a counter of its own, so its Q
+// fragment is loaded once and the tile boundaries load only K/V.
 template <int D, int NW, bool BCAST, bool CAUSAL, bool SPARSE = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_kernel(FwdArgs a) {
@@ -479,6 +489,11 @@ void fwd_kernel(FwdArgs a) {
   const int ntiles = a.meta[2];
   const int per_item = BCAST ? ((a.q_len + K::BM - 1) / K::BM) * a.heads : a.heads;
   const bool dyn = a.sched == kDynamic;
+  const int cls = a.classes > 0 ? lwg % a.classes : 0;
+  auto claim = [&]() {   // next tile of the dynamic schedule (one lane)
+    if (a.classes > 0) return atomicAdd(a.meta + 4 + cls, 1) * a.classes + cls;
+    return atomicAdd(a.meta + 1, 1);
+  };
   auto sched_idx = [&](int r) {
     if (a.sched == kIdentity) return r * num_wg + lwg;
     return r * num_wg + ((r & 1) ? (num_wg - 1 - lwg) : lwg);
@@ -498,8 +513,8 @@ void fwd_kernel(FwdArgs a) {
   int idx0, idx1;
   if (dyn) {
     if (threadIdx.x == 0) {
-      first_idx[0] = atomicAdd(a.meta + 1, 1);
-      first_idx[1] = atomicAdd(a.meta + 1, 1);
+      first_idx[0] = claim();
+      first_idx[1] = claim();
     }
     __syncthreads();
     idx0 = __builtin_amdgcn_readfirstlane(first_idx[0]);
@@ -541,7 +556,7 @@ void fwd_kernel(FwdArgs a) {
     if (has_next) nxt = kern.geometry(nidx, *reinterpret_cast<const int4*>(next_item), per_item);
     int pend = ntiles;   // index of tile r + 2 (lane 0 of wave 0 under the dynamic schedule)
     if (dyn) {
-      if (threadIdx.x == 0) pend = atomicAdd(a.meta + 1, 1);
+      if (threadIdx.x == 0) pend = claim();
     } else {
       pend = sched_idx(r + 2);
     }
@@ -562,9 +577,16 @@ void fwd_kernel(FwdArgs a) {
 }
 
 template <int D, int NW, bool BCAST, bool CAUSAL, bool SPARSE = false>
-hipError_t launch_inst(const FwdArgs& a, hipStream_t s, int64_t max_tiles) {
+hipError_t launch_inst(const FwdArgs& args, hipStream_t s, int64_t max_tiles) {
   const void* fn = reinterpret_cast<const void*>(&fwd_kernel<D, NW, BCAST, CAUSAL, SPARSE>);
   const int grid = persistent_grid(fn, 64 * NW, max_tiles);
+  FwdArgs a = args;
+  a.classes = 0;
+  if (BCAST && !CAUSAL && !SPARSE && a.sched == kDynamic) {
+    // one class per workgroup when there are at least four workgroups per class
+    const int per_item = ((a.q_len + 32 * NW - 1) / (32 * NW)) * a.heads;
+    if (per_item <= kFwdClassMax && grid >= 4 * per_item) a.classes = per_item;
+  }
   hipLaunchKernelGGL((fwd_kernel<D, NW, BCAST, CAUSAL, SPARSE>), dim3(grid), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }

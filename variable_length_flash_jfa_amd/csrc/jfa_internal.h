@@ -75,8 +75,10 @@ struct Rope {
 
 // Plan written on the device: meta[0] = number of items, meta[1] = dynamic-schedule
 // counter, meta[2] = number of tiles, meta[3] (backward) = 1 when every tile holds a
-// whole self-mode sequence and writes its dQ directly.  items[i] = (sequence b,
-// block, offsets[b], offsets[b + 1] - offsets[b]).
+// whole self-mode sequence and writes its dQ directly, meta[4 .. 4 + kFwdClassMax)
+// (forward) = per-class counters of the broadcast-mode dynamic schedule.
+// items[i] = (sequence b, block, offsets[b], offsets[b + 1] - offsets[b]).
+constexpr int kFwdClassMax = 12;
 struct Plan {
   int* meta;
   int4* items;

@@ -293,6 +293,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fwd_kernel(PlanFwdArgs a) {
     a.meta[1] = 0;
     a.meta[2] = total * per_item;
   }
+  if (tid < kFwdClassMax) a.meta[4 + tid] = 0;
 }
 
 struct PlanBwdArgs {
