@@ -211,112 +211,168 @@ __global__ __launch_bounds__(64 * NW) void fwd_mx_kernel(MxArgs a) {
   const int li = lane & 31, hh = lane >> 5;
   const int ntiles = a.meta[2];
   const int per_item = BCAST ? ((a.q_len + BM - 1) / BM) * a.heads : a.heads;
-  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+  const int64_t vstride = (int64_t)a.heads * D;   // between consecutive V blocks (x 32 bytes)
+  // tile geometry: sequence b (K/V rows kv0 .. kv0 + n), query block m, head h, and
+  // the key blocks the workgroup visits (all of the sequence, or, causal, up to its
+  // last query row)
+  struct Geo {
+    int64_t kv0, gbase;
+    int b, n, m, h, nblk;
+  };
+  auto geo = [&](int t) {
+    Geo g;
     const int4 it = a.items[t / per_item];
     const int rem = t % per_item;
-    const int b = it.x;
-    const int64_t kv0 = it.z;
-    const int n = it.w;
-    const int m = BCAST ? rem / a.heads : it.y;
-    const int h = BCAST ? rem % a.heads : rem;
-    const int q_rows = BCAST ? a.q_len : n;
-    const int i0 = m * BM + 32 * wave;
-    const bool active = i0 < q_rows;
-    // key blocks of the workgroup (all of the sequence, or, causal, up to its last
-    // query row) and of this wave
-    const int nblk = ((CAUSAL ? min(n, m * BM + BM) : n) + 63) / 64;
-    const int wave_end = CAUSAL ? min(n, i0 + 32) : n;
-    const int64_t gbase = (int64_t)b + kv0 / 32;
-    const int64_t vstride = (int64_t)a.heads * D;   // between consecutive V blocks (x 32 bytes)
-    // staging registers of the next block
-    i32x4 kst[KR], vst_[VR];
-    uint32_t kss = 0;
-    i32x4 vss = i32x4{0, 0, 0, 0};
-    auto fetch = [&](int kb) {
-      const int j0 = 64 * kb;
+    g.b = it.x;
+    g.kv0 = it.z;
+    g.n = it.w;
+    g.m = BCAST ? rem / a.heads : it.y;
+    g.h = BCAST ? rem % a.heads : rem;
+    g.nblk = ((CAUSAL ? min(g.n, g.m * BM + BM) : g.n) + 63) / 64;
+    g.gbase = (int64_t)g.b + g.kv0 / 32;
+    return g;
+  };
+  // staging registers of the next block
+  i32x4 kst[KR], vst_[VR];
+  uint32_t kss = 0;
+  i32x4 vss = i32x4{0, 0, 0, 0};
+  auto fetch = [&](const Geo& g, int kb) {
+    const int j0 = 64 * kb;
 #pragma unroll
-      for (int r = 0; r < KR; ++r) {
-        const int c = tid + NT * r;
-        if (KCH % NT == 0 || c < KCH) {
-          const int row = c / (D / 16), col = c % (D / 16);
-          const int key = min(j0 + row, n - 1);
-          kst[r] = *reinterpret_cast<const i32x4*>(a.k8 + ((kv0 + key) * a.heads + h) * D + col * 16);
-        }
+    for (int r = 0; r < KR; ++r) {
+      const int c = tid + NT * r;
+      if (KCH % NT == 0 || c < KCH) {
+        const int row = c / (D / 16), col = c % (D / 16);
+        const int key = min(j0 + row, g.n - 1);
+        kst[r] = *reinterpret_cast<const i32x4*>(a.k8 + ((g.kv0 + key) * a.heads + g.h) * D + col * 16);
       }
+    }
 #pragma unroll
-      for (int r = 0; r < VR; ++r) {
-        const int c = tid + NT * r;
-        if (VCH % NT == 0 || c < VCH) {
-          const int blk = c / (2 * D), within = c % (2 * D);
-          vst_[r] = i32x4{0, 0, 0, 0};
-          if (j0 + 32 * blk < n)
-            vst_[r] = *reinterpret_cast<const i32x4*>(a.v8 + ((gbase + j0 / 32 + blk) * vstride + h * D) * 32 +
-                                                      within * 16);
-        }
+    for (int r = 0; r < VR; ++r) {
+      const int c = tid + NT * r;
+      if (VCH % NT == 0 || c < VCH) {
+        const int blk = c / (2 * D), within = c % (2 * D);
+        vst_[r] = i32x4{0, 0, 0, 0};
+        if (j0 + 32 * blk < g.n)
+          vst_[r] = *reinterpret_cast<const i32x4*>(a.v8 + ((g.gbase + j0 / 32 + blk) * vstride + g.h * D) * 32 +
+                                                    within * 16);
       }
-      if (tid < 64) {
-        const int key = min(j0 + tid, n - 1);
-        const uint8_t* sp = a.ks + ((kv0 + key) * a.heads + h) * NSB;
-        kss = NSB == 4 ? *reinterpret_cast<const uint32_t*>(sp) : *reinterpret_cast<const uint16_t*>(sp);
-      } else if (tid < 64 + VSCH) {
-        const int c = tid - 64;
-        const int blk = c / (D / 16), within = c % (D / 16);
-        vss = i32x4{0x7f7f7f7f, 0x7f7f7f7f, 0x7f7f7f7f, 0x7f7f7f7f};   // code 127 (1.0) for a missing block
-        if (j0 + 32 * blk < n)
-          vss = *reinterpret_cast<const i32x4*>(a.vs + (gbase + j0 / 32 + blk) * vstride + h * D + within * 16);
-      }
-    };
-    auto stash = [&](int buf) {
-      uint8_t* base = smem + buf * BUF;
+    }
+    if (tid < 64) {
+      const int key = min(j0 + tid, g.n - 1);
+      const uint8_t* sp = a.ks + ((g.kv0 + key) * a.heads + g.h) * NSB;
+      kss = NSB == 4 ? *reinterpret_cast<const uint32_t*>(sp) : *reinterpret_cast<const uint16_t*>(sp);
+    } else if (tid < 64 + VSCH) {
+      const int c = tid - 64;
+      const int blk = c / (D / 16), within = c % (D / 16);
+      vss = i32x4{0x7f7f7f7f, 0x7f7f7f7f, 0x7f7f7f7f, 0x7f7f7f7f};   // code 127 (1.0) for a missing block
+      if (j0 + 32 * blk < g.n)
+        vss = *reinterpret_cast<const i32x4*>(a.vs + (g.gbase + j0 / 32 + blk) * vstride + g.h * D + within * 16);
+    }
+  };
+  auto stash = [&](int buf) {
+    uint8_t* base = smem + buf * BUF;
 #pragma unroll
-      for (int r = 0; r < KR; ++r) {
-        const int c = tid + NT * r;
-        if (KCH % NT == 0 || c < KCH)
-          *reinterpret_cast<i32x4*>(base + (c / (D / 16)) * KROW + (c % (D / 16)) * 16) = kst[r];
-      }
+    for (int r = 0; r < KR; ++r) {
+      const int c = tid + NT * r;
+      if (KCH % NT == 0 || c < KCH)
+        *reinterpret_cast<i32x4*>(base + (c / (D / 16)) * KROW + (c % (D / 16)) * 16) = kst[r];
+    }
 #pragma unroll
-      for (int r = 0; r < VR; ++r) {
-        const int c = tid + NT * r;
-        if (VCH % NT == 0 || c < VCH) *reinterpret_cast<i32x4*>(base + KT + c * 16) = vst_[r];
-      }
-      if (tid < 64) {
-        if (NSB == 4)
-          *reinterpret_cast<uint32_t*>(base + KT + VT + tid * 4) = kss;
-        else
-          *reinterpret_cast<uint16_t*>(base + KT + VT + tid * 2) = (uint16_t)kss;
-      } else if (tid < 64 + VSCH) {
-        *reinterpret_cast<i32x4*>(base + KT + VT + KST + (tid - 64) * 16) = vss;
-      }
-    };
-    // Q^T fragment: lane (query li, half hh) holds columns 64 s + 16 hh .. + 15 and
-    // 64 s + 32 + 16 hh .. + 15, and the code of column block 2 s + hh
-    i32x8 qf[KS];
-    int qsc[KS];
-    if (active) {
-      const int64_t qrow = BCAST ? (int64_t)min(i0 + li, q_rows - 1) : kv0 + min(i0 + li, q_rows - 1);
-      const uint8_t* qp = a.q8 + (qrow * a.heads + h) * D;
-      const uint8_t* qsp = a.qs + (qrow * a.heads + h) * NSB;
+    for (int r = 0; r < VR; ++r) {
+      const int c = tid + NT * r;
+      if (VCH % NT == 0 || c < VCH) *reinterpret_cast<i32x4*>(base + KT + c * 16) = vst_[r];
+    }
+    if (tid < 64) {
+      if (NSB == 4)
+        *reinterpret_cast<uint32_t*>(base + KT + VT + tid * 4) = kss;
+      else
+        *reinterpret_cast<uint16_t*>(base + KT + VT + tid * 2) = (uint16_t)kss;
+    } else if (tid < 64 + VSCH) {
+      *reinterpret_cast<i32x4*>(base + KT + VT + KST + (tid - 64) * 16) = vss;
+    }
+  };
+  // Q^T fragment: lane (query li, half hh) holds columns 64 s + 16 hh .. + 15 and
+  // 64 s + 32 + 16 hh .. + 15, and the code of column block 2 s + hh
+  i32x8 qf[KS];
+  int qsc[KS];
+  auto load_q = [&](const Geo& g) {
+    const int q_rows = BCAST ? a.q_len : g.n;
+    const int i0 = g.m * BM + 32 * wave;
+    if (i0 < q_rows) {
+      const int64_t qrow = BCAST ? (int64_t)min(i0 + li, q_rows - 1) : g.kv0 + min(i0 + li, q_rows - 1);
+      const uint8_t* qp = a.q8 + (qrow * a.heads + g.h) * D;
+      const uint8_t* qsp = a.qs + (qrow * a.heads + g.h) * NSB;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         qf[s] = load32(qp + 64 * s + 16 * hh, qp + 64 * s + 32 + 16 * hh);
         qsc[s] = qsp[2 * s + hh];
       }
     }
+  };
+
+  // XT: tile t + gridDim.x's first block is loaded during tile t's last block (into
+  // the other LDS buffer) and its Q fragment after it; in broadcast mode a tile of
+  // the same query block and head keeps the Q fragment (with a grid that is a
+  // multiple of the tiles per sequence, every tile of a workgroup does).  Without
+  // XT (self mode at two waves, chosen for short sequences: tiles of one or two
+  // blocks) a tile loads its Q fragment and first block together at its start, so
+  // that they land in one memory latency.  Block kb of a tile sits in buffer
+  // (pb + kb) & 1.
+  constexpr bool XT = BCAST || NW > 2;
+  int t = blockIdx.x;
+  if (t >= ntiles) return;
+  Geo cur{};
+  if constexpr (XT) {
+    cur = geo(t);
+    load_q(cur);
+    if (cur.nblk > 0) {
+      fetch(cur, 0);
+      stash(0);
+    }
+    __syncthreads();
+  }
+  int pb = 0;
+  for (;;) {
+    if constexpr (!XT) {   // the previous tile's last barrier retired its readers
+      cur = geo(t);
+      load_q(cur);
+      if (cur.nblk > 0) {
+        fetch(cur, 0);
+        stash(pb);
+      }
+      __syncthreads();
+    }
+    const int tn = t + (int)gridDim.x;
+    const bool has_next = tn < ntiles;
+    const Geo nxt = XT && has_next ? geo(tn) : cur;
+    const int b = cur.b, n = cur.n, m = cur.m, h = cur.h, nblk = cur.nblk;
+    const int64_t kv0 = cur.kv0;
+    const int q_rows = BCAST ? a.q_len : n;
+    const int i0 = m * BM + 32 * wave;
+    const bool active = i0 < q_rows;
+    const int wave_end = CAUSAL ? min(n, i0 + 32) : n;
+    // The Q fragment may have been loaded at the end of the previous tile: consume it
+    // here, so that the compiler's wait for it lands before the block loop and not at
+    // every block's first product (where it would also wait for the next block's loads).
+#pragma unroll
+    for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(qf[s]), "+v"(qsc[s]));
     f32x16 acc[DB];
 #pragma unroll
     for (int d = 0; d < DB; ++d) acc[d] = f32x16{};
     float mrun = -INFINITY, lrun = 0.f;
-    __syncthreads();   // the previous tile's readers of both buffers are done
-    if (nblk > 0) {
-      fetch(0);
-      stash(0);
-    }
-    __syncthreads();
     for (int kb = 0; kb < nblk; ++kb) {
       const int j0 = 64 * kb;
-      if (kb + 1 < nblk) fetch(kb + 1);
+      const int buf = (pb + kb) & 1;
+      // the next block of this tile, or else the next tile's first, goes into the
+      // other buffer at the end of this one (one load site: with a load site per
+      // case the compiler merges the staging registers with copies that wait for
+      // the loads at once)
+      const bool in_tile = kb + 1 < nblk;
+      const bool pf = in_tile || (XT && has_next && nxt.nblk > 0);
+      if (pf) fetch(in_tile ? cur : nxt, in_tile ? kb + 1 : 0);
       if (active && j0 < wave_end) {
-        const uint8_t* base = smem + (kb & 1) * BUF;
+        const uint8_t* base = smem + buf * BUF;
         // S^T for keys j0 + 32 rb + li (rows) x the wave's 32 queries (columns)
         f32x16 st[2];
 #pragma unroll
@@ -404,9 +460,16 @@ __global__ __launch_bounds__(64 * NW) void fwd_mx_kernel(MxArgs a) {
               i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, pf, acc[d], 0, 0, 0, vsc, 0, psc);
         }
       }
-      if (kb + 1 < nblk) stash((kb + 1) & 1);
+      if (pf) stash(buf ^ 1);
       __syncthreads();
     }
+    if (XT && nblk == 0 && has_next && nxt.nblk > 0) {   // an empty sequence (broadcast mode)
+      fetch(nxt, 0);
+      stash(pb);
+      __syncthreads();
+    }
+    // the tile is done with its Q fragment
+    if (XT && has_next && !(BCAST && nxt.m == m && nxt.h == h)) load_q(nxt);
     // epilogue: O = acc / l (bf16), LSE = ln 2 (m + log2 l)
     if (active) {
       const float lt = lrun + __shfl_xor(lrun, 32);
@@ -426,6 +489,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_mx_kernel(MxArgs a) {
         if (hh == 0) a.lse[(int64_t)h * a.rows + orow] = lt > 0.f ? (mrun + __log2f(lt)) * kLn2 : -INFINITY;
       }
     }
+    if (!has_next) break;
+    pb = (pb + nblk) & 1;
+    cur = nxt;
+    t = tn;
   }
 }
 
