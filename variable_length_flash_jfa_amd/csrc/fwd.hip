@@ -582,8 +582,9 @@ hipError_t launch_inst(const FwdArgs& args, hipStream_t s, int64_t max_tiles) {
   const int grid = persistent_grid(fn, 64 * NW, max_tiles);
   FwdArgs a = args;
   a.classes = 0;
-  if (BCAST && !CAUSAL && !SPARSE && a.sched == kDynamic) {
-    // one class per workgroup when there are at least four workgroups per class
+  if (BCAST && !CAUSAL && a.sched == kDynamic) {
+    // one class per workgroup when there are at least four workgroups per class (the
+    // block-sparse tiles of a sequence all visit min(k, its key blocks) blocks)
     const int per_item = ((a.q_len + 32 * NW - 1) / (32 * NW)) * a.heads;
     if (per_item <= kFwdClassMax && grid >= 4 * per_item) a.classes = per_item;
   }
