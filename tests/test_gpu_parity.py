@@ -202,6 +202,23 @@ def test_schedules_agree(bq, causal):
     _compare_full(case, outs[0])
 
 
+def test_broadcast_tile_classes():
+    # broadcast mode with two query blocks per head (Lq = 300: a ragged second block)
+    # and empty sequences: under the dynamic schedule the forward serves each
+    # (query block, head) class from a counter of its own; every schedule must give
+    # the same bits
+    jfa = _jfa()
+    rng = np.random.default_rng(23)
+    lengths = [int(x) for x in rng.integers(0, 700, size=40)]
+    lengths[3] = 0
+    lengths[17] = 0
+    case = workloads.make_case(lengths, heads=2, head_dim=128, broadcast_q=True, q_len=300, seed=29)
+    outs = [_run(case, sched=s) for s in (jfa.SCHED_DYNAMIC, jfa.SCHED_IDENTITY)]
+    for name in ("o", "lse", "dk", "dv"):
+        assert torch.equal(outs[0][name], outs[1][name]), name
+    _compare_full(case, outs[0])
+
+
 def test_autograd_wrapper():
     jfa = _jfa()
     case = workloads.make_case([40, 90], heads=2, head_dim=64, broadcast_q=True, q_len=48, seed=3)
