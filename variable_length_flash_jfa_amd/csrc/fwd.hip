@@ -8,7 +8,9 @@
 // Structure (MI355X design; the pages' Blackwell kernel is prior art only):
 //  * persistent workgroups walk a device-built tile list (sorted by K/V work and
 //    dealt boustrophedon, or round-robin, or claimed through an atomic counter;
-//    section "Five changes unlocked the gains", items 1 and 2);
+//    section "Five changes unlocked the gains", items 1 and 2); in broadcast mode
+//    the counter is split by (query block, head) class, one class per workgroup,
+//    so that a workgroup's Q fragment stays in registers from tile to tile;
 //  * a tile is (sequence, block of 32*NW query rows, head); each 64-lane wave owns
 //    32 query rows, keeps its Q fragment in registers and computes
 //    S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16, so that the
