@@ -223,7 +223,8 @@ def sparse_comparison(args, jfa, w, case, o, lse, ws_f):
 
 def rope_comparison(args, jfa, w, case, o, lse, dq, dk, dv, ws_f, ws_b):
     """Fused rotary backward vs plain backward vs plain backward + separate rotary
-    backward, as in the Block Attention page's rotary-fusion table.  The separate
+    backward, as in the rotary-fusion table of "Meta's TLX Block Attention Beats
+    Flash Attention v2 by 2.3x on Blackwell GPUs" (section "The Rotary Fusion Bonus").  The separate
     rotary backward reads the bf16 gradients, rotates them in fp32 and writes bf16."""
     q, k, v, g, off = case["q"], case["k"], case["v"], case["g"], case["offsets"]
     bq, causal, scale = w.broadcast_q, w.causal, case["scale"]

@@ -29,8 +29,9 @@
  *   - lse    fp32 [H, rows]: natural-log log-sum-exp of the scaled scores
  *            c * q_i . k_j over the visible keys; -inf for a row with no key.
  *   - dq like q, dk and dv like k; all bf16.  Accumulation is fp32 throughout.
- *   - head_dim must be 64 or 128 (the page on Block Attention, section "Who Should
- *     Use This", names these two head sizes); heads >= 1.
+ *   - head_dim must be 64 or 128 ("Meta's TLX Block Attention Beats Flash Attention
+ *     v2 by 2.3x on Blackwell GPUs", section "Who Should Use This", names these two
+ *     head sizes); heads >= 1.
  *   - Work is enqueued on `stream` without any host synchronisation; the caller
  *     keeps every buffer alive until that work completes.  Outputs are
  *     overwritten, never accumulated into.
@@ -64,8 +65,9 @@ typedef enum {
 /* Tile schedule used by the forward and backward kernels (process-wide).
  *   JFA_SCHED_SORTED_ZIGZAG  forward tiles sorted by KV work (descending) and dealt
  *                            boustrophedon across persistent workgroups; backward
- *                            valid (b, h, KV-block) tiles dealt round-robin (JFA news
- *                            page, "Five changes unlocked the gains", item 1).
+ *                            valid (b, h, KV-block) tiles dealt round-robin ("Meta's
+ *                            TLX attention kernel outpaces FlashAttention-4 on B200",
+ *                            section "Five changes unlocked the gains", item 1).
  *   JFA_SCHED_IDENTITY       tiles in natural (b, block, h) order, dealt round-robin.
  *   JFA_SCHED_DYNAMIC        sorted tiles claimed through a device atomic counter by
  *                            whichever workgroup is free (the same section, item 2).
@@ -130,11 +132,12 @@ jfa_status_t jfa_fwd_noalloc(const void* q, const void* k, const void* v,
 
 /* Backward pass: gradients of sum(O * dO) with respect to q, k and v, given the
  * o and lse that jfa_fwd returned for the same inputs.  In broadcast mode dq is
- * the sum over all sequences (JFA news page, "GEM's sequences do not fit a fixed
- * grid").  In self mode, when every sequence fits one backward tile (block-diagonal
+ * the sum over all sequences ("Meta's TLX attention kernel outpaces FlashAttention-4
+ * on B200", section "GEM's sequences do not fit a fixed grid").  In self mode, when every sequence fits one backward tile (block-diagonal
  * attention in 64-token blocks, for instance), the row sums dO . O are formed from
- * the tile's own probabilities and o is not read (Block Attention page, "One
- * Constraint, Five Eliminations"); it must still be a valid pointer.  Same size
+ * the tile's own probabilities and o is not read ("Meta's TLX Block Attention Beats
+ * Flash Attention v2 by 2.3x on Blackwell GPUs", section "One Constraint, Five
+ * Eliminations"); it must still be a valid pointer.  Same size
  * rules as jfa_fwd. */
 jfa_status_t jfa_bwd(const void* q, const void* k, const void* v,
                      const void* offsets, int offsets_is_int64,
@@ -186,7 +189,8 @@ jfa_status_t jfa_bwd_rope(const void* q, const void* k, const void* v,
 #define JFA_SPARSE_QUERY_BLOCK_BROADCAST 256
 #define JFA_SPARSE_QUERY_BLOCK_SELF 128
 
-/* Block-sparse top-k forward (the JFA news page and the reading note name a
+/* Block-sparse top-k forward ("Meta's TLX attention kernel outpaces FlashAttention-4
+ * on B200" and "Optimizing Jagged Flash Attention with TLX" name a
  * block-sparse fork of the kernel: a scoring step picks the top k key/value blocks
  * for each query block, and attention runs only over those blocks).  Non-causal
  * modes only (causal gives JFA_ERR_UNSUPPORTED).

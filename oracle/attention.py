@@ -51,7 +51,8 @@ def sequence_forward(qb, kb, vb, scale: float, causal: bool = False):
     qb: [Lq, D] queries, kb/vb: [n, D] keys/values.  Returns
     (O [Lq, D], lse [Lq]) in fp64.  Follows the plain definition
     O = softmax(c Q K^T) V, with the row log-sum-exp kept for the backward
-    ("One Constraint, Five Eliminations", Block Attention page).
+    ("Meta's TLX Block Attention Beats Flash Attention v2 by 2.3x on Blackwell
+    GPUs", section "One Constraint, Five Eliminations").
     """
     qb, kb, vb = _f64(qb), _f64(kb), _f64(vb)
     lq, n = qb.shape[0], kb.shape[0]
@@ -73,8 +74,9 @@ def sequence_backward(qb, kb, vb, gb, scale: float, causal: bool = False):
 
     Returns (dQ [Lq, D], dK [n, D], dV [n, D]).  Standard softmax-attention
     calculus: dV = P^T G; dP = G V^T; delta_i = sum_j P_ij dP_ij (the row-wise
-    sum that the Block Attention page's "One Constraint, Five Eliminations"
-    section calls the Di preprocessing); dS = P * (dP - delta);
+    sum that "Meta's TLX Block Attention Beats Flash Attention v2 by 2.3x on
+    Blackwell GPUs", section "One Constraint, Five Eliminations", calls the Di
+    preprocessing); dS = P * (dP - delta);
     dK = c dS^T Q; dQ = c dS K.
     """
     qb, kb, vb, gb = _f64(qb), _f64(kb), _f64(vb), _f64(gb)
@@ -146,8 +148,8 @@ def forward(q, k, v, offsets, *, broadcast_q: bool, causal: bool = False, scale:
     q: [Lq, H, D] (broadcast-Q) or [T, H, D] (self); k, v: [T, H, D];
     offsets: [B + 1].  Returns O [rows, H, D] and LSE [H, rows] in fp64 where
     rows = B * Lq (broadcast, row b * Lq + i belongs to sequence b) or T.
-    Plain per-sequence, per-head loop ("GEM's sequences do not fit a fixed
-    grid", JFA news page).
+    Plain per-sequence, per-head loop ("Meta's TLX attention kernel outpaces
+    FlashAttention-4 on B200", section "GEM's sequences do not fit a fixed grid").
     """
     offsets = _check(q, k, offsets, broadcast_q, causal)
     b_count = len(offsets) - 1
@@ -171,8 +173,9 @@ def backward(q, k, v, offsets, g, *, broadcast_q: bool, causal: bool = False, sc
     """Gradients of L = sum(O * G) for the packed batch.
 
     Returns dQ (shape of q), dK, dV (shape of k).  In broadcast-Q mode every
-    sequence adds its query gradient into the one shared dQ (JFA news page,
-    "GEM's sequences do not fit a fixed grid").
+    sequence adds its query gradient into the one shared dQ ("Meta's TLX attention
+    kernel outpaces FlashAttention-4 on B200", section "GEM's sequences do not fit a
+    fixed grid").
     """
     offsets = _check(q, k, offsets, broadcast_q, causal)
     b_count = len(offsets) - 1

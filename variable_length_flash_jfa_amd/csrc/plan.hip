@@ -10,9 +10,10 @@
 // offsets and no synchronisation.
 //
 // Backward: the list of valid (sequence, K/V block) pairs is precomputed from a
-// prefix sum of per-sequence block counts (reading note, same section; "TLX JFA"
-// note, section "Structural changes and layered opts", item 1), and the kernel
-// deals them round-robin.
+// prefix sum of per-sequence block counts ("Optimizing Jagged Flash Attention with
+// TLX", same section; "TLX JFA: Meta's Blackwell Attention Kernel", section
+// "Structural changes and layered opts", item 1), and the kernel deals them
+// round-robin.
 #include "jfa_device.h"
 #include "jfa_internal.h"
 
