@@ -71,7 +71,7 @@ def algorithmic_bytes(w, lengths):
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the kernel sources; ties stored counter readings to this build."""
+    """sha256 over the kernel sources; ties stored counter readings to the sources they were taken on."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "variable_length_flash_jfa_amd", "csrc")
@@ -349,8 +349,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
-              "multi-GPU path in this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library runs on "
+              "one GPU and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
