@@ -143,6 +143,34 @@ def test_mxfp8_forward_matches_oracle(name):
     _check_lse(lse, lse_ref)
 
 
+@pytest.mark.parametrize("bq", [True, False])
+def test_mxfp8_forward_many_tiles_per_workgroup(bq):
+    # Many more tiles than workgroups (about 12 to 20 each, 4-wave workgroups): each
+    # workgroup loads its next tile's first block (and, in self mode, its Q fragment)
+    # during the current tile, and broadcast tiles keep their Q fragment; the
+    # broadcast batch has an empty sequence every 37, so empty tiles sit between
+    # others.  Every row against the oracle.
+    rng = np.random.default_rng(41 if bq else 47)
+    if bq:
+        lengths = [int(x) for x in rng.integers(0, 150, size=2500)]
+        for i in range(0, len(lengths), 37):
+            lengths[i] = 0
+        case = workloads.make_case(lengths, heads=2, head_dim=64, broadcast_q=True, causal=False, q_len=100,
+                                   seed=43)
+    else:
+        lengths = [int(x) for x in rng.integers(100, 300, size=800)]
+        case = workloads.make_case(lengths, heads=2, head_dim=64, broadcast_q=False, causal=True, q_len=0,
+                                   seed=49)
+    jfa = _jfa()
+    q, k, v = (case[x].cuda() for x in ("q", "k", "v"))
+    o, lse = _mx_run(jfa, q, k, v, case["offsets"].cuda(), bq, not bq, case["scale"])
+    torch.cuda.synchronize()
+    o_ref, lse_ref, slack = mx.forward_mx(*(_f64(case[x]) for x in ("q", "k", "v")), case["offsets"].numpy(),
+                                          broadcast_q=bq, causal=not bq, scale=case["scale"])
+    _check_o(o, o_ref, slack)
+    _check_lse(lse, lse_ref)
+
+
 def test_mxfp8_forward_close_to_bf16_forward():
     """The 8-bit forward stays near the bf16 forward on the same inputs: a coarse
     check of the whole path (quantization of Q, K, V and P shifts O by a few
