@@ -131,6 +131,10 @@ MANY = {
     "self_causal_short_one_long": (_lengths(4, 17000, 1, 64, long_at=16990, long_len=150), 2, 64,
                                    False, True, 0),
     "bcast_9k": (_lengths(5, 9000, 0, 120), 2, 128, True, False, 48),
+    # 256-row broadcast tiles (eight waves): about 23 tiles per workgroup, under the
+    # dynamic schedule one (query block, head) class per workgroup, with empty
+    # sequences between the others
+    "bcast_lq256_3k": (_lengths(7, 3000, 1, 200, zero_every=29), 2, 64, True, False, 256),
 }
 
 
