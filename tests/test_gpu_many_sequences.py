@@ -130,6 +130,9 @@ MANY = {
     # as above except one sequence in the last segment: the multi-tile backward
     "self_causal_short_one_long": (_lengths(4, 17000, 1, 64, long_at=16990, long_len=150), 2, 64,
                                    False, True, 0),
+    # the two-wave D = 128 single-tile backward, three workgroups per CU: about 44
+    # tiles per workgroup, so the static schedules read many next-tile items
+    "self_short_d128_17k": (_lengths(8, 17000, 0, 64, zero_every=53), 2, 128, False, False, 0),
     "bcast_9k": (_lengths(5, 9000, 0, 120), 2, 128, True, False, 48),
     # 256-row broadcast tiles (eight waves): about 23 tiles per workgroup, under the
     # dynamic schedule one (query block, head) class per workgroup, with empty
@@ -141,8 +144,8 @@ MANY = {
 @pytest.mark.parametrize("sched", [0, 1, 2])
 @pytest.mark.parametrize("name", list(MANY))
 def test_many_sequences_every_row(name, sched):
-    if sched != 2 and name not in ("self_17k", "bcast_9k"):
-        pytest.skip("schedules other than the default are covered on two of the cases")
+    if sched != 2 and name not in ("self_17k", "bcast_9k", "self_short_d128_17k"):
+        pytest.skip("schedules other than the default are covered on three of the cases")
     lengths, h, d, bq, causal, lq = MANY[name]
     jfa = _jfa()
     off_dtype = torch.int32 if sched == 1 else torch.int64

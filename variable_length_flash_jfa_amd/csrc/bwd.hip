@@ -152,7 +152,8 @@ struct BwdKernel {
   static constexpr int KT_BYTES = BN * D * 2;
   static constexpr int QT_BYTES = BQ * D * 2;
   static constexpr int DS_BYTES = BN * BQ * 2;
-  static constexpr int ROW_BYTES = BQ * 8;   // (LSE log2 e, delta) per query row
+  // per query row: (LSE log2 e, delta), or in DIRECT the forward's LSE alone
+  static constexpr int ROW_BYTES = DIRECT ? BQ * 4 : BQ * 8;
   // LDS map
   static constexpr int OFF_K = 0;
   static constexpr int OFF_Q = OFF_K + KT_BYTES;              // 2 buffers
@@ -170,7 +171,14 @@ struct BwdKernel {
   static constexpr int RPOS_BYTES = RTAB ? 2 * 256 : 0;
   static constexpr int RTAB_WAVE = 2 * BQ * 32 * 4;            // cos, then sin: [32 rows][32 columns] fp32
   static constexpr int OFF_RTAB = OFF_RPOS + RPOS_BYTES;
-  static constexpr int SMEM = OFF_RTAB + (RTAB ? NW * RTAB_WAVE : 0);
+  // The schedule's words: the claimed tile index and the static schedules' next plan
+  // item (a 64-lane copy target).  DIRECT keeps neither here: its claimed index
+  // borrows the partial-delta area, which is idle between a tile's last query block
+  // and the next tile's first barrier, and its static schedules read the item from
+  // memory.  That keeps the 2-wave D = 128 workgroup at 53,760 bytes, 42 of the
+  // 1,280-byte LDS allocation units, so that three fit in a CU's 160 KB.
+  static constexpr int OFF_ITEM = OFF_RTAB + (RTAB ? NW * RTAB_WAVE : 0);
+  static constexpr int SMEM = OFF_ITEM + (DIRECT ? 0 : 256 + 4);
   static constexpr uint32_t GQ = OFF_DO - OFF_Q;              // dO tile minus Q tile, same buffer
   static constexpr int XB = D == 128 ? 256 : 128;             // the XOR-free granule
   static_assert(BN == 32 * NW && G * DT == NW * DTW && DTW <= 2, "tile shape");
@@ -265,7 +273,8 @@ struct BwdKernel {
     const bf16* qsrc = a.q + ((BCAST ? 0 : kv0_) + qi0) * rs + (int64_t)h_ * D;
     const bf16* gsrc = a.d_o + (grow0_ + qi0) * rs + (int64_t)h_ * D;
     if constexpr (QLD) {
-      const uint32_t dst = lds0 + (uint32_t)(buf * QT_BYTES + wave * 1024);
+      // (wave-uniform; stated, since the DIRECT row copy below is lane-masked)
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(buf * QT_BYTES + wave * 1024));
       lds_load16_at(make_rsrc_sgpr(qsrc, bytes), q_voff, dst + (uint32_t)OFF_Q);
       lds_load16_at(make_rsrc_sgpr(gsrc, bytes), q_voff, dst + (uint32_t)OFF_DO);
     } else {
@@ -281,9 +290,9 @@ struct BwdKernel {
       }
     }
     if (wave == NW - 1) {
-      if constexpr (DIRECT) {   // the forward's LSE, one float per row
+      if constexpr (DIRECT) {   // the forward's LSE, one float per row, from BQ lanes
         const float* src = a.lse + (int64_t)h_ * a.rows + grow0_ + qi0;
-        lds_load4(make_rsrc_sgpr(src, (uint32_t)rows * 4u), (uint32_t)lane * 4u, rowbuf(buf));
+        if (lane < BQ) lds_load4(make_rsrc_sgpr(src, (uint32_t)rows * 4u), (uint32_t)lane * 4u, rowbuf(buf));
       } else {                  // (LSE log2 e, delta) pairs
         const float2* src = a.rowstat + (int64_t)h_ * a.rows + grow0_ + qi0;
         lds_load4(make_rsrc_sgpr(src, (uint32_t)rows * 8u), (uint32_t)lane * 4u, rowbuf(buf));
@@ -961,17 +970,17 @@ void bwd_kernel(BwdArgs a) {
   using K = BwdKernel<D, NW, BCAST, CAUSAL, DIRECT, ROPE>;
   using Geo = typename K::Geo;
   __shared__ __attribute__((aligned(16))) char smem[K::SMEM];
-  __shared__ __attribute__((aligned(16))) int next_item[64];   // DMA target, 16 bytes used
-  __shared__ int claimed;
+  int* const next_item = reinterpret_cast<int*>(smem + K::OFF_ITEM);   // DMA target, 16 bytes used
+  int* const claimed = reinterpret_cast<int*>(smem + (DIRECT ? K::OFF_DEL : K::OFF_ITEM + 256));
   K kern(a, smem);
   const int num_wg = gridDim.x;
   const int lwg = xcd_logical_wg(blockIdx.x, num_wg);
   const int ntiles = a.meta[2];
   const bool dyn = a.sched == kDynamic;
   auto claim = [&]() {
-    if (threadIdx.x == 0) claimed = atomicAdd(a.meta + 1, 1);
+    if (threadIdx.x == 0) *claimed = atomicAdd(a.meta + 1, 1);
     __syncthreads();
-    const int v = claimed;
+    const int v = *claimed;
     __syncthreads();
     return v;
   };
@@ -981,18 +990,18 @@ void bwd_kernel(BwdArgs a) {
   kern.issue_kv(g);
   kern.issue_q0(g);
   for (bool first = true;; first = false) {
-    // static schedules know the next tile now: its item is copied into LDS while
-    // this tile runs (the copy completes at this tile's first load wait)
+    // static schedules know the next tile now: outside DIRECT its item is copied
+    // into LDS while this tile runs (the copy completes at this tile's first load wait)
     int nidx = dyn ? -1 : idx + num_wg;
     auto pre = [&]() {
-      if (!dyn && nidx < ntiles && kern.wave == 0)
+      if (!DIRECT && !dyn && nidx < ntiles && kern.wave == 0)
         lds_load4(make_rsrc_sgpr(a.items + nidx / a.heads, 16u), (uint32_t)kern.lane * 4u,
                   reinterpret_cast<char*>(next_item));
     };
     auto next = [&](Geo& out) -> bool {
       if (dyn) nidx = claim();
       if (nidx >= ntiles) return false;
-      const int4 it = dyn ? a.items[nidx / a.heads] : *reinterpret_cast<const int4*>(next_item);
+      const int4 it = (dyn || DIRECT) ? a.items[nidx / a.heads] : *reinterpret_cast<const int4*>(next_item);
       out = kern.geometry(it, nidx % a.heads);
       return true;
     };
