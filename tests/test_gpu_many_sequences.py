@@ -133,6 +133,10 @@ MANY = {
     # the two-wave D = 128 single-tile backward, three workgroups per CU: about 44
     # tiles per workgroup, so the static schedules read many next-tile items
     "self_short_d128_17k": (_lengths(8, 17000, 0, 64, zero_every=53), 2, 128, False, False, 0),
+    # as above, causal, with one sequence of 300 keys: the whole call takes the
+    # multi-tile two-wave D = 128 backward (delta pass, reduce-adds, finalize)
+    "self_causal_short_one_long_d128": (_lengths(9, 17000, 1, 64, long_at=9000, long_len=300), 2, 128,
+                                        False, True, 0),
     "bcast_9k": (_lengths(5, 9000, 0, 120), 2, 128, True, False, 48),
     # 256-row broadcast tiles (eight waves): about 23 tiles per workgroup, under the
     # dynamic schedule one (query block, head) class per workgroup, with empty
@@ -144,8 +148,9 @@ MANY = {
 @pytest.mark.parametrize("sched", [0, 1, 2])
 @pytest.mark.parametrize("name", list(MANY))
 def test_many_sequences_every_row(name, sched):
-    if sched != 2 and name not in ("self_17k", "bcast_9k", "self_short_d128_17k"):
-        pytest.skip("schedules other than the default are covered on three of the cases")
+    if sched != 2 and name not in ("self_17k", "bcast_9k", "self_short_d128_17k",
+                                   "self_causal_short_one_long_d128"):
+        pytest.skip("schedules other than the default are covered on four of the cases")
     lengths, h, d, bq, causal, lq = MANY[name]
     jfa = _jfa()
     off_dtype = torch.int32 if sched == 1 else torch.int64
