@@ -127,14 +127,16 @@ MANY = {
     "self_causal_17k": (_lengths(2, 17000, 1, 200, zero_every=89), 2, 128, False, True, 0),
     # every sequence within one 64-key backward tile: the single-tile backward
     "self_causal_short_17k": (_lengths(3, 17000, 1, 64), 2, 64, False, True, 0),
-    # as above except one sequence in the last segment: the multi-tile backward
+    # as above except one sequence in the last segment: the plan splits the tiles
+    # between the single-tile kernel and the multi-tile one (delta and the dQ
+    # finalize over the long sequence's rows)
     "self_causal_short_one_long": (_lengths(4, 17000, 1, 64, long_at=16990, long_len=150), 2, 64,
                                    False, True, 0),
     # the two-wave D = 128 single-tile backward, three workgroups per CU: about 44
     # tiles per workgroup, so the static schedules read many next-tile items
     "self_short_d128_17k": (_lengths(8, 17000, 0, 64, zero_every=53), 2, 128, False, False, 0),
-    # as above, causal, with one sequence of 300 keys: the whole call takes the
-    # multi-tile two-wave D = 128 backward (delta pass, reduce-adds, finalize)
+    # as above, causal, with one sequence of 300 keys: split between the two-wave
+    # D = 128 single-tile and multi-tile kernels
     "self_causal_short_one_long_d128": (_lengths(9, 17000, 1, 64, long_at=9000, long_len=300), 2, 128,
                                         False, True, 0),
     "bcast_9k": (_lengths(5, 9000, 0, 120), 2, 128, True, False, 48),

@@ -116,6 +116,11 @@ SMALL_CASES = {
     "single_tile_d128_nw4": ([128, 100, 110, 128, 90, 97], 2, 128, False, False, 0),
     "single_tile_d64_nw4_causal": ([128, 120, 99, 128, 70], 2, 64, False, True, 0),
     "single_tile_d64_nw2": ([64, 3, 64, 50, 17], 2, 64, False, False, 0),
+    # most sequences within one backward tile, one or two longer: the plan splits the
+    # tiles, the single-tile kernel takes the short sequences and the reduce-adding
+    # kernel (with delta and the dQ finalize over its rows only) the long ones
+    "split_d128_nw2": ([64, 17, 150, 10, 5, 64, 30, 20], 2, 128, False, False, 0),
+    "split_d128_nw4_causal": ([128, 100, 300, 20, 90], 2, 128, False, True, 0),
     # self mode with a mean length of at least 512: 256-row forward tiles of eight waves
     "self_d128_causal_long": ([900, 1200, 64, 700, 1], 2, 128, False, True, 0),
     "self_d64_long": ([600, 1000, 3, 700], 2, 64, False, False, 0),
@@ -155,6 +160,33 @@ def test_single_tile_backward_does_not_read_o():
     ref = jfa.bwd(q, k, v, off, o, lse, g, **kw)
     nan_o = torch.full_like(o, float("nan"))
     got = jfa.bwd(q, k, v, off, nan_o, lse, g, **kw)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), ref, got):
+        assert torch.equal(a.cpu(), b.cpu()), name
+    out = {"o": o.cpu(), "lse": lse.cpu(), "dq": got[0].cpu(), "dk": got[1].cpu(), "dv": got[2].cpu()}
+    _compare_full(case, out)
+
+
+def test_split_backward_reads_o_of_long_sequences_only():
+    """In a call whose sequences are split between the single-tile kernel and the
+    reduce-adding one, delta is formed from O only for the rows of the longer
+    sequences: NaNs in the O rows of the short sequences change no gradient."""
+    jfa = _jfa()
+    lengths = [64, 17, 150, 10, 5, 64, 30, 20]
+    case = workloads.make_case(lengths, heads=2, head_dim=128, broadcast_q=False, causal=True,
+                               q_len=0, seed=12)
+    q, k, v, g = (case[x].cuda() for x in ("q", "k", "v", "g"))
+    off = case["offsets"].cuda()
+    kw = dict(broadcast_q=False, causal=True, scale=case["scale"])
+    o, lse = jfa.fwd(q, k, v, off, **kw)
+    ref = jfa.bwd(q, k, v, off, o, lse, g, **kw)
+    o_short_nan = o.clone()
+    start = 0
+    for n in lengths:
+        if n <= 64:
+            o_short_nan[start:start + n] = float("nan")
+        start += n
+    got = jfa.bwd(q, k, v, off, o_short_nan, lse, g, **kw)
     torch.cuda.synchronize()
     for name, a, b in zip(("dq", "dk", "dv"), ref, got):
         assert torch.equal(a.cpu(), b.cpu()), name

@@ -1,10 +1,12 @@
-"""The forward tile plan the device builds (white-box: read from the workspace).
+"""The tile plans the device builds (white-box: read from the workspace).
 
 The plan is a stable descending counting sort of the work items by their cost, the
 number of 64-key blocks a tile visits ("Meta's TLX attention kernel outpaces
 FlashAttention-4 on B200", section "Five changes unlocked the gains", item 1): costs
 must not increase along the list, items of equal cost keep (sequence, query block)
-order, every item appears exactly once, and two calls give the same list.
+order, every item appears exactly once, and two calls give the same list.  The
+backward plan lists the tiles of each sequence in order, split in self mode between
+the sequences of one tile and the longer ones.
 
 Workspace layout (api.cpp): the buffer is aligned up to 256 bytes, then the meta words
 (item count first) take 256 bytes and the items follow, 16 bytes each:
@@ -97,3 +99,56 @@ def test_forward_plan_of_many_segments_is_stable():
     for c in np.unique(costs):
         assert np.all(np.diff(items[costs == c][:, 0]) > 0)
     assert sorted(items[:, 0].tolist()) == list(range(9000))
+
+
+def _bwd_plan(case):
+    """meta words and items of the backward plan (same workspace layout as above)."""
+    jfa = _jfa()
+    q, k, v, g = (case[x].cuda() for x in ("q", "k", "v", "g"))
+    off = case["offsets"].cuda()
+    lengths = case["lengths"]
+    kw = dict(broadcast_q=False, causal=case["causal"], scale=case["scale"])
+    o, lse = jfa.fwd(q, k, v, off, **kw)
+    need = jfa.bwd_workspace_size(len(lengths), k.shape[1], k.shape[2], 0, k.shape[0], False, case["causal"])
+    ws = torch.zeros(need + 256, dtype=torch.uint8, device="cuda")
+    jfa.bwd(q, k, v, off, o, lse, g, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    base = (-ws.data_ptr()) % 256
+    raw = ws.cpu().numpy()[base:].view(np.int32)
+    meta = raw[:8].astype(np.int64)
+    items = raw[64:64 + 4 * int(meta[0])].reshape(-1, 4).astype(np.int64)
+    return meta, items
+
+
+BWD_PLAN_CASES = {
+    # name: (lengths, causal, keys per backward tile, split)
+    # mean 49: 64-key tiles, and every sequence may fit one: the plan splits
+    "split": ([64, 17, 150, 0, 10, 5, 64, 130, 30, 20], True, 64, True),
+    # mean 224: 128-key tiles, too long on average for the single-tile kernel
+    "no_split": ([700, 3, 64, 129, 0, 448], False, 128, False),
+}
+
+
+@pytest.mark.parametrize("name", list(BWD_PLAN_CASES))
+def test_backward_plan_lists(name):
+    """Self mode: the tiles of sequences longer than one tile come first, in (sequence,
+    key block) order; with split the sequences of 1..bn keys follow, one item each, in
+    sequence order, and the meta words give both lists' tile counts and the second's
+    first item."""
+    lengths, causal, bn, split = BWD_PLAN_CASES[name]
+    heads = 2
+    case = workloads.make_case(lengths, heads=heads, head_dim=128, broadcast_q=False, causal=causal,
+                               q_len=0, seed=5)
+    meta, items = _bwd_plan(case)
+    off = np.concatenate([[0], np.cumsum(lengths)])
+    first = [(b, j) for b, n in enumerate(lengths) if not (split and n <= bn)
+             for j in range((n + bn - 1) // bn)]
+    second = [(b, 0) for b, n in enumerate(lengths) if split and 1 <= n <= bn]
+    assert int(meta[0]) == len(first) + len(second)
+    assert int(meta[2]) == len(first) * heads
+    assert int(meta[3]) == len(second) * heads
+    if split:
+        assert int(meta[5]) == len(first)
+    assert [tuple(x) for x in items[:, :2].tolist()] == first + second
+    assert np.array_equal(items[:, 2], off[items[:, 0]])
+    assert np.array_equal(items[:, 3], np.asarray(lengths)[items[:, 0]])

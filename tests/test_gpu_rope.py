@@ -25,10 +25,15 @@ CASES = {
     "bcast_d64_lq100": ([17, 64, 129], 2, 64, True, False, 100),
     "self_d128_causal": ([1, 5, 64, 127, 300], 2, 128, False, True, 0),
     "self_d64": ([2, 33, 190, 257], 3, 64, False, False, 0),
-    # every sequence within one 64-key tile: without the rotary conjugate this call
-    # would store dQ from the tiles; with it dQ goes through the finalize
+    # every sequence within one 64-key tile: the single-tile kernel rotates and stores dQ
     "self_d128_single_tile_lengths": ([64, 17, 64, 40], 2, 128, False, False, 0),
+    # split between the single-tile kernel and the reduce-adding one, whose rows the
+    # finalize rotates
     "self_d128_causal_short": ([3, 64, 100, 128, 1], 2, 128, False, True, 0),
+    "self_d128_split": ([64, 17, 150, 10, 5, 64, 30, 20], 2, 128, False, False, 0),
+    # mean length above one 128-key tile: with and without the conjugate every tile
+    # reduce-adds its dQ, so the two calls run the same kernels
+    "self_d128_causal_long_mean": ([1, 5, 64, 700, 300], 2, 128, False, True, 0),
 }
 
 
@@ -79,8 +84,11 @@ def test_rope_backward_matches_oracle(name):
 
 
 def test_rope_at_zero_angle_equals_plain_backward():
-    """cos = 1, sin = 0: the conjugate is the identity (self mode: bitwise)."""
-    case = _case("self_d128_causal")
+    """cos = 1, sin = 0: the conjugate is the identity (self mode: bitwise, on a batch
+    whose calls with and without the conjugate take the same kernels).  In a batch
+    of short sequences the plain call gives most of them to the single-tile kernel,
+    which forms delta as sum_j P dP instead of dO . O: equal up to rounding only."""
+    case = _case("self_d128_causal_long_mean")
     rope = workloads.rope_inputs(case)
     rope["cos"] = torch.ones_like(rope["cos"])
     rope["sin"] = torch.zeros_like(rope["sin"])

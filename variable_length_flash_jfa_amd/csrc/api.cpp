@@ -389,7 +389,7 @@ jfa_status_t bwd_impl(const char* fn, const void* q, const void* k, const void* 
   hipError_t e = timed_launch("plan_bwd", s, [&] { return jfa::launch_plan_bwd(p, plan, sched, s); });
   if (e != hipSuccess) return hip_fail(e, fn, "plan launch");
   e = timed_launch("bwd_pre", s, [&] {
-    return jfa::launch_bwd_pre(p, o, d_o, lse, rowstat, dq_acc, acc_elems, plan.meta, s);
+    return jfa::launch_bwd_pre(p, o, d_o, lse, rowstat, dq_acc, acc_elems, plan, s);
   });
   if (e != hipSuccess) return hip_fail(e, fn, "delta launch");
   if (p.total_kv > 0) {
@@ -399,7 +399,7 @@ jfa_status_t bwd_impl(const char* fn, const void* q, const void* k, const void* 
     if (e != hipSuccess) return hip_fail(e, fn, "kernel launch");
   }
   e = timed_launch("dq_finalize", s,
-                   [&] { return jfa::launch_dq_finalize(p, dq_acc, dq, plan.meta, rope, s); });
+                   [&] { return jfa::launch_dq_finalize(p, dq_acc, dq, plan, rope, s); });
   if (e != hipSuccess) return hip_fail(e, fn, "dq finalize launch");
   return JFA_OK;
 }

@@ -1,12 +1,15 @@
 // Jagged Flash Attention backward for gfx950.
 //
 // Launch sequence of one backward call:
-//   1. bwd_pre_kernel: delta_i = sum_d dO_i . O_i per (row, head) -- the row-wise
+//   1. the backward tile planner (plan.hip).  In self mode, when the sequences may
+//      fit one tile each, it splits the tiles in two lists: sequences within one
+//      tile, whose tiles form delta themselves and store their final dQ (the
+//      single-tile, DIRECT kernel), and the longer ones, which take the steps below;
+//   2. bwd_pre_kernel: delta_i = sum_d dO_i . O_i per (row, head) -- the row-wise
 //      sum the backward needs ("Meta's TLX Block Attention Beats Flash Attention
 //      v2 by 2.3x on Blackwell GPUs", section "One Constraint, Five
 //      Eliminations", the Di preprocessing) -- and zeroing of the fp32 dQ
-//      accumulator;
-//   2. the backward tile planner (plan.hip);
+//      accumulator (bwd_pre_split_kernel: the rows of the first list only);
 //   3. bwd_kernel: persistent workgroups over valid (sequence, 256-key block, head)
 //      tiles.  Eight waves own 32 keys each, hold dK^T / dV^T accumulators and
 //      their V fragment in registers, and stream the tile's query rows in blocks
@@ -27,7 +30,8 @@
 //      stay in flight while it computes (the pages pipeline this reduction through
 //      a double-buffered on-chip stage: section "Five changes unlocked the gains",
 //      item 3);
-//   5. dq_finalize_kernel: sum of the stripes, times the softmax scale -> bf16.
+//   5. dq_finalize_kernel: sum of the stripes, times the softmax scale -> bf16 (in a
+//      split call, dq_finalize_split_kernel over the first list's rows).
 #include "jfa_device.h"
 #include "jfa_internal.h"
 
@@ -41,44 +45,25 @@ namespace {
 // rowstat[(h rows + row) 2 + 0] = LSE[h][row] log2(e) (so that P = exp2(S c log2 e -
 // that) needs no multiply per score), rowstat[... + 1] = delta[h][row]; one 8-byte
 // pair per row lets a single direct load bring both values of 32 rows into LDS.
-// CHECK: the call may have every sequence within one tile (known on the device only,
-// meta[3]); the kernel then returns at once, and takes four pairs per group of
-// threads so that there are fewer blocks to retire.  Otherwise there is no check (its
-// load would stand in front of every block's work) and one pair per group.
-template <int D, bool CHECK>
+// Every (row, head) pair of the call: one group of D / 8 threads per pair, and a
+// grid-stride zero fill of the whole accumulator.
+template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o,
                                                        const bf16* __restrict__ d_o,
                                                        const float* __restrict__ lse,
                                                        float2* __restrict__ rowstat, int64_t rows,
                                                        int heads, float* __restrict__ dq_acc,
-                                                       int64_t acc_vec4, const int* __restrict__ meta) {
-  // every sequence within one tile: the tiles read LSE themselves, form delta
-  // inline and write dQ directly, so there is nothing to do
-  if (CHECK && meta[3] != 0) return;
+                                                       int64_t acc_vec4) {
   constexpr int TPR = D / 8;                 // threads per (row, head)
-  constexpr int PPG = CHECK ? 4 : 1;         // pairs per group of TPR threads
   const int part = threadIdx.x % TPR;
   const int64_t npairs = rows * heads;
-  const int64_t groups = (int64_t)gridDim.x * (256 / TPR);
-  const int64_t g0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) / TPR;
-  // group g takes pairs g, g + groups, ... (consecutive groups, consecutive pairs);
-  // all loads are issued before the sums.  A pair's TPR lanes share every branch.
-  bf16x8 x[PPG], y[PPG];
-#pragma unroll
-  for (int u = 0; u < PPG; ++u) {
-    const int64_t pair = g0 + u * groups;
-    if (pair < npairs) {
-      x[u] = *reinterpret_cast<const bf16x8*>(o + pair * D + part * 8);
-      y[u] = *reinterpret_cast<const bf16x8*>(d_o + pair * D + part * 8);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < PPG; ++u) {
-    const int64_t pair = g0 + u * groups;
-    if (pair >= npairs) break;
+  const int64_t pair = ((int64_t)blockIdx.x * 256 + threadIdx.x) / TPR;
+  if (pair < npairs) {   // a pair's TPR lanes share the branch
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(o + pair * D + part * 8);
+    const bf16x8 y = *reinterpret_cast<const bf16x8*>(d_o + pair * D + part * 8);
     float s = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s += (float)x[u][e] * (float)y[u][e];
+    for (int e = 0; e < 8; ++e) s += (float)x[e] * (float)y[e];
 #pragma unroll
     for (int m = TPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
     if (part == 0) {
@@ -92,6 +77,59 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o
   float4* acc = reinterpret_cast<float4*>(dq_acc);
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < acc_vec4; i += nthreads)
     acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// Rows of a split call's first list (self mode; see the backward plan): an item
+// (b, j, kv0, n) of a sequence longer than one tile covers the rows [kv0 + j bn,
+// kv0 + min(n, (j + 1) bn)), and together the items cover every row whose delta and
+// dQ finalize the call needs; the single-tile kernel forms the others' itself.
+// Workgroups take (item, head) units in turn, a group of threads per row.
+struct SplitRows {
+  int64_t r0, r1;
+  int h;
+};
+__device__ __forceinline__ SplitRows split_rows(const int4* __restrict__ items, int u, int heads, int bn) {
+  const int4 it = items[u / heads];
+  SplitRows r;
+  r.r0 = (int64_t)it.z + (int64_t)it.y * bn;
+  r.r1 = (int64_t)it.z + min(it.w, (it.y + 1) * bn);
+  r.h = u % heads;
+  return r;
+}
+
+// The same statistics and zeroing for the rows of a split call's first list only
+// (meta[2] = its items x heads units; none when every sequence fits one tile).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_split_kernel(const bf16* __restrict__ o,
+                                                             const bf16* __restrict__ d_o,
+                                                             const float* __restrict__ lse,
+                                                             float2* __restrict__ rowstat, int64_t rows,
+                                                             int heads, float* __restrict__ dq_acc,
+                                                             const int4* __restrict__ items,
+                                                             const int* __restrict__ meta, int bn) {
+  constexpr int TPR = D / 8, RPP = 256 / TPR;   // threads per row, rows per pass
+  const int part = threadIdx.x % TPR, sub = threadIdx.x / TPR;
+  const int units = meta[2];
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const SplitRows sr = split_rows(items, u, heads, bn);
+    for (int64_t row = sr.r0 + sub; row < sr.r1; row += RPP) {   // a row's TPR lanes share it
+      const int64_t pair = row * heads + sr.h;
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(o + pair * D + part * 8);
+      const bf16x8 y = *reinterpret_cast<const bf16x8*>(d_o + pair * D + part * 8);
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += (float)x[e] * (float)y[e];
+#pragma unroll
+      for (int m = TPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+      if (part == 0) {
+        const int64_t i = (int64_t)sr.h * rows + row;
+        rowstat[i] = make_float2(lse[i] * kLog2e, s);
+      }
+      float4* acc = reinterpret_cast<float4*>(dq_acc + pair * D + part * 8);
+      acc[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+      acc[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -132,8 +170,8 @@ struct BwdArgs {
 // added to that VGPR once, which commutes with the per-read XOR of the swizzle
 // (the XOR only touches the low 8 (7) bits).  Each read then costs at most one
 // XOR and its constant part rides in the instruction's offset field.
-// DIRECT: self mode with every sequence in one tile (the plan flags such a call in
-// meta[3]); delta is formed inline and dQ is stored, not reduce-added.
+// DIRECT: self-mode tiles that hold a whole sequence (the plan's second list);
+// delta is formed inline and dQ is stored, not reduce-added.
 // ROPE: the rotary conjugate is applied to dK in the epilogue (and to dQ where the
 // tiles store it); without it none of that code is compiled in.
 template <int D, int NW, bool BCAST, bool CAUSAL, bool DIRECT, bool ROPE>
@@ -965,8 +1003,8 @@ struct BwdKernel {
 template <int D, int NW, bool BCAST, bool CAUSAL, bool DIRECT, bool ROPE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_kernel(BwdArgs a) {
-  // self mode launches both variants; the plan's meta[3] picks the one that runs
-  if ((__builtin_amdgcn_readfirstlane(a.meta[3]) != 0) != DIRECT) return;
+  // The plan's lists: a DIRECT kernel takes the tiles of sequences within one tile
+  // (the second list), the other the rest (the first); either may be empty.
   using K = BwdKernel<D, NW, BCAST, CAUSAL, DIRECT, ROPE>;
   using Geo = typename K::Geo;
   __shared__ __attribute__((aligned(16))) char smem[K::SMEM];
@@ -975,10 +1013,12 @@ void bwd_kernel(BwdArgs a) {
   K kern(a, smem);
   const int num_wg = gridDim.x;
   const int lwg = xcd_logical_wg(blockIdx.x, num_wg);
-  const int ntiles = a.meta[2];
+  const int ntiles = __builtin_amdgcn_readfirstlane(DIRECT ? a.meta[3] : a.meta[2]);
+  const int4* const items = a.items + (DIRECT ? __builtin_amdgcn_readfirstlane(a.meta[5]) : 0);
+  int* const counter = a.meta + (DIRECT ? 4 : 1);
   const bool dyn = a.sched == kDynamic;
   auto claim = [&]() {
-    if (threadIdx.x == 0) *claimed = atomicAdd(a.meta + 1, 1);
+    if (threadIdx.x == 0) *claimed = atomicAdd(counter, 1);
     __syncthreads();
     const int v = *claimed;
     __syncthreads();
@@ -986,7 +1026,7 @@ void bwd_kernel(BwdArgs a) {
   };
   int idx = dyn ? claim() : lwg;
   if (idx >= ntiles) return;
-  Geo g = kern.geometry(a.items[idx / a.heads], idx % a.heads);
+  Geo g = kern.geometry(items[idx / a.heads], idx % a.heads);
   kern.issue_kv(g);
   kern.issue_q0(g);
   for (bool first = true;; first = false) {
@@ -995,13 +1035,13 @@ void bwd_kernel(BwdArgs a) {
     int nidx = dyn ? -1 : idx + num_wg;
     auto pre = [&]() {
       if (!DIRECT && !dyn && nidx < ntiles && kern.wave == 0)
-        lds_load4(make_rsrc_sgpr(a.items + nidx / a.heads, 16u), (uint32_t)kern.lane * 4u,
+        lds_load4(make_rsrc_sgpr(items + nidx / a.heads, 16u), (uint32_t)kern.lane * 4u,
                   reinterpret_cast<char*>(next_item));
     };
     auto next = [&](Geo& out) -> bool {
       if (dyn) nidx = claim();
       if (nidx >= ntiles) return false;
-      const int4 it = (dyn || DIRECT) ? a.items[nidx / a.heads] : *reinterpret_cast<const int4*>(next_item);
+      const int4 it = (dyn || DIRECT) ? items[nidx / a.heads] : *reinterpret_cast<const int4*>(next_item);
       out = kern.geometry(it, nidx % a.heads);
       return true;
     };
@@ -1015,77 +1055,117 @@ void bwd_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // 5. dQ finalize
 // ---------------------------------------------------------------------------
-// CHECK: the call may have every sequence within one tile, whose tiles then wrote dQ
-// (meta[3]); the kernel then returns at once, from a bounded grid that strides over
-// the elements.  Without CHECK the flag is not read and every thread takes one
-// element group.
-template <bool CHECK>
+// One thread per four accumulator elements of the call.
 __global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restrict__ acc,
                                                           bf16* __restrict__ dq, int64_t n_vec4,
-                                                          int64_t stripe_vec4, int stripes,
-                                                          float scale, const int* __restrict__ meta) {
-  if (CHECK && meta[3] != 0) return;   // the tiles wrote dQ
+                                                          int64_t stripe_vec4, int stripes, float scale) {
   const float4* a4 = reinterpret_cast<const float4*>(acc);
-  const int64_t step = CHECK ? (int64_t)gridDim.x * 256 : n_vec4;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_vec4; i += step) {
-    float4 s = a4[i];
-    for (int k = 1; k < stripes; ++k) {
-      const float4 t = a4[i + k * stripe_vec4];
-      s.x += t.x;
-      s.y += t.y;
-      s.z += t.z;
-      s.w += t.w;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_vec4) return;
+  float4 s = a4[i];
+  for (int k = 1; k < stripes; ++k) {
+    const float4 t = a4[i + k * stripe_vec4];
+    s.x += t.x;
+    s.y += t.y;
+    s.z += t.z;
+    s.w += t.w;
+  }
+  bf16x4 o;
+  o[0] = (bf16)(s.x * scale);
+  o[1] = (bf16)(s.y * scale);
+  o[2] = (bf16)(s.z * scale);
+  o[3] = (bf16)(s.w * scale);
+  reinterpret_cast<bf16x4*>(dq)[i] = o;
+}
+
+// The rows of a split call's first list only (self mode: one accumulator stripe);
+// the single-tile kernel stored the others' dQ itself.
+template <int D>
+__global__ __launch_bounds__(256) void dq_finalize_split_kernel(const float* __restrict__ acc,
+                                                                bf16* __restrict__ dq, int heads, float scale,
+                                                                const int4* __restrict__ items,
+                                                                const int* __restrict__ meta, int bn) {
+  constexpr int TPR = D / 4, RPP = 256 / TPR;   // threads per row (four columns each), rows per pass
+  const int part = threadIdx.x % TPR, sub = threadIdx.x / TPR;
+  const int units = meta[2];
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const SplitRows sr = split_rows(items, u, heads, bn);
+    for (int64_t row = sr.r0 + sub; row < sr.r1; row += RPP) {
+      const int64_t e0 = (row * heads + sr.h) * D + part * 4;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(acc + e0);
+      bf16x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (bf16)(v[e] * scale);
+      *reinterpret_cast<bf16x4*>(dq + e0) = o;
     }
-    bf16x4 o;
-    o[0] = (bf16)(s.x * scale);
-    o[1] = (bf16)(s.y * scale);
-    o[2] = (bf16)(s.z * scale);
-    o[3] = (bf16)(s.w * scale);
-    reinterpret_cast<bf16x4*>(dq)[i] = o;
   }
 }
 
 // dQ finalize with the rotary conjugate: sum of the stripes, times the softmax
 // scale, rotated by the opposite angle of the query row's position, -> bf16.  One
-// thread takes four columns d .. d + 3 (d < D/2) of a (row, head) and their partners
-// d + D/2 .. d + D/2 + 3.  CHECK as for dq_finalize_kernel (the tiles may have
-// stored dQ, rotated, themselves).
-template <int D, bool CHECK>
+// thread takes four columns d .. d + 3 (d = 4 g < D/2) of a (row, head) pair rh and
+// their partners d + D/2 .. d + D/2 + 3.
+template <int D>
+__device__ __forceinline__ void finalize_rope_group(const float* __restrict__ acc, bf16* __restrict__ dq,
+                                                    int64_t rh, int64_t row, int g, int64_t stripe_elems,
+                                                    int stripes, float scale, const float* __restrict__ rcos,
+                                                    const float* __restrict__ rsin,
+                                                    const int* __restrict__ pos_q, int max_pos) {
+  const int64_t e0 = rh * D + 4 * g;
+  f32x4 lo = *reinterpret_cast<const f32x4*>(acc + e0);
+  f32x4 hi = *reinterpret_cast<const f32x4*>(acc + e0 + D / 2);
+  for (int k = 1; k < stripes; ++k) {
+    lo += *reinterpret_cast<const f32x4*>(acc + e0 + k * stripe_elems);
+    hi += *reinterpret_cast<const f32x4*>(acc + e0 + D / 2 + k * stripe_elems);
+  }
+  const int pos = min(max(pos_q[row], 0), max_pos - 1);
+  const f32x4 c = *reinterpret_cast<const f32x4*>(rcos + (int64_t)pos * (D / 2) + 4 * g);
+  const f32x4 sn = *reinterpret_cast<const f32x4*>(rsin + (int64_t)pos * (D / 2) + 4 * g);
+  bf16x4 olo, ohi;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a0 = lo[e] * scale, b0 = hi[e] * scale;
+    olo[e] = (bf16)(a0 * c[e] + b0 * sn[e]);
+    ohi[e] = (bf16)(b0 * c[e] - a0 * sn[e]);
+  }
+  *reinterpret_cast<bf16x4*>(dq + e0) = olo;
+  *reinterpret_cast<bf16x4*>(dq + e0 + D / 2) = ohi;
+}
+
+// Every (row, head) pair of the call, one thread per four-column group.
+template <int D>
 __global__ __launch_bounds__(256) void dq_finalize_rope_kernel(const float* __restrict__ acc,
                                                                bf16* __restrict__ dq, int64_t rows,
                                                                int heads, int64_t stripe_elems,
                                                                int stripes, float scale,
                                                                const float* __restrict__ rcos,
                                                                const float* __restrict__ rsin,
-                                                               const int* __restrict__ pos_q,
-                                                               int max_pos, const int* __restrict__ meta) {
-  if (CHECK && meta[3] != 0) return;   // the tiles wrote dQ
+                                                               const int* __restrict__ pos_q, int max_pos) {
   constexpr int G = D / 8;   // four-column groups in each half
-  const int64_t total = rows * heads * G;
-  const int64_t step = CHECK ? (int64_t)gridDim.x * 256 : total;
-  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += step) {
-    const int64_t rh = t / G;   // row * heads + head
-    const int g = (int)(t - rh * G);
-    const int64_t row = rh / heads;
-    const int64_t e0 = rh * D + 4 * g;
-    f32x4 lo = *reinterpret_cast<const f32x4*>(acc + e0);
-    f32x4 hi = *reinterpret_cast<const f32x4*>(acc + e0 + D / 2);
-    for (int k = 1; k < stripes; ++k) {
-      lo += *reinterpret_cast<const f32x4*>(acc + e0 + k * stripe_elems);
-      hi += *reinterpret_cast<const f32x4*>(acc + e0 + D / 2 + k * stripe_elems);
-    }
-    const int pos = min(max(pos_q[row], 0), max_pos - 1);
-    const f32x4 c = *reinterpret_cast<const f32x4*>(rcos + (int64_t)pos * (D / 2) + 4 * g);
-    const f32x4 sn = *reinterpret_cast<const f32x4*>(rsin + (int64_t)pos * (D / 2) + 4 * g);
-    bf16x4 olo, ohi;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a0 = lo[e] * scale, b0 = hi[e] * scale;
-      olo[e] = (bf16)(a0 * c[e] + b0 * sn[e]);
-      ohi[e] = (bf16)(b0 * c[e] - a0 * sn[e]);
-    }
-    *reinterpret_cast<bf16x4*>(dq + e0) = olo;
-    *reinterpret_cast<bf16x4*>(dq + e0 + D / 2) = ohi;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= rows * heads * G) return;
+  const int64_t rh = t / G;   // row * heads + head
+  finalize_rope_group<D>(acc, dq, rh, rh / heads, (int)(t - rh * G), stripe_elems, stripes, scale, rcos,
+                         rsin, pos_q, max_pos);
+}
+
+// The rows of a split call's first list only, with the rotary conjugate.
+template <int D>
+__global__ __launch_bounds__(256) void dq_finalize_rope_split_kernel(const float* __restrict__ acc,
+                                                                     bf16* __restrict__ dq, int heads,
+                                                                     float scale,
+                                                                     const float* __restrict__ rcos,
+                                                                     const float* __restrict__ rsin,
+                                                                     const int* __restrict__ pos_q,
+                                                                     int max_pos, const int4* __restrict__ items,
+                                                                     const int* __restrict__ meta, int bn) {
+  constexpr int G = D / 8, RPP = 256 / G;   // threads per row, rows per pass
+  const int g = threadIdx.x % G, sub = threadIdx.x / G;
+  const int units = meta[2];
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const SplitRows sr = split_rows(items, u, heads, bn);
+    for (int64_t row = sr.r0 + sub; row < sr.r1; row += RPP)
+      finalize_rope_group<D>(acc, dq, row * heads + sr.h, row, g, 0, 1, scale, rcos, rsin, pos_q, max_pos);
   }
 }
 
@@ -1096,9 +1176,9 @@ hipError_t launch_bwd_one(const BwdArgs& a, hipStream_t s, int64_t max_tiles) {
   hipLaunchKernelGGL((bwd_kernel<D, NW, BCAST, CAUSAL, DIRECT, ROPE>), dim3(grid), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
-// Broadcast mode has one variant.  In self mode whether every sequence fits one
-// tile is known on the device only (meta[3], from the plan), so both variants are
-// launched and the one that does not match returns at once.  With the rotary
+// Broadcast mode has one variant.  In a split self-mode call (maybe_single_tile)
+// both are launched, each over its list of the plan (an empty list returns at once):
+// which sequences fit one tile is known on the device only.  With the rotary
 // conjugate the single-tile variant exists only for two d tiles per wave (D = 128,
 // two waves), see single_tile_allowed.
 template <int D, int NW, bool BCAST, bool CAUSAL, bool ROPE>
@@ -1156,16 +1236,22 @@ int bwd_waves(const Problem& p) {
   return mean_len >= 512 ? 8 : 4;
 }
 
-// Whether every sequence may lie within one backward tile (self mode, and the mean
-// length at most the tile's keys); the plan decides on the device (meta[3]).
+// Whether the single-tile kernel may take the sequences that lie within one backward
+// tile: self mode, and with the rotary conjugate only where its tiles can rotate dQ.
 bool single_tile_allowed(const Problem& p) {
   // with the rotary conjugate the tiles can rotate dQ only when a lane holds both
   // halves of its columns: two d tiles per wave (D = 128, two waves)
   return !p.broadcast && (!p.rope || (p.head_dim == 128 && bwd_waves(p) == 2));
 }
 
+// Whether the plan splits the tiles between the single-tile kernel and the
+// reduce-adding one: where the single-tile kernel may run, with 64-key tiles (the mean
+// length is at most 96, so most sequences are short) or when every sequence may fit
+// one tile.
 bool maybe_single_tile(const Problem& p) {
-  return single_tile_allowed(p) && p.total_kv <= (int64_t)p.batch * 32 * bwd_waves(p);
+  if (!single_tile_allowed(p)) return false;
+  const int nw = bwd_waves(p);
+  return nw == 2 || p.total_kv <= (int64_t)p.batch * 32 * nw;
 }
 
 int64_t bwd_max_items(const Problem& p) {
@@ -1173,26 +1259,36 @@ int64_t bwd_max_items(const Problem& p) {
   return (p.total_kv + bn - 1) / bn + p.batch;
 }
 
+// Grid of the split-mode row kernels: workgroups that take (item, head) units in turn.
+static unsigned split_grid(const Problem& p) {
+  const int64_t units = bwd_max_items(p) * p.heads;
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(units, (int64_t)device_cu_count() * 16));
+}
+
 hipError_t launch_bwd_pre(const Problem& p, const void* o, const void* d_o, const float* lse,
-                          float* rowstat, float* dq_acc, int64_t dq_acc_elems, const int* meta,
+                          float* rowstat, float* dq_acc, int64_t dq_acc_elems, const Plan& plan,
                           hipStream_t s) {
+  float2* rs2 = reinterpret_cast<float2*>(rowstat);
+  const bf16* o16 = static_cast<const bf16*>(o);
+  const bf16* g16 = static_cast<const bf16*>(d_o);
+  if (maybe_single_tile(p)) {   // the plan split the tiles: rows of the first list only
+    auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3(split_grid(p)), dim3(256), 0, s, o16, g16, lse, rs2, p.rows, p.heads,
+                         dq_acc, plan.items, plan.meta, 32 * bwd_waves(p));
+    };
+    p.head_dim == 128 ? go(bwd_pre_split_kernel<128>) : go(bwd_pre_split_kernel<64>);
+    return hipGetLastError();
+  }
   const int64_t pairs = p.rows * p.heads;
   const int tpr = p.head_dim / 8;
-  const bool check = maybe_single_tile(p);
-  const int ppg = check ? 4 : 1;
-  int64_t blocks = (pairs * tpr + ppg * 256 - 1) / (ppg * 256);
+  int64_t blocks = (pairs * tpr + 255) / 256;
   if (blocks < 1) blocks = 1;
   const int64_t vec4 = dq_acc_elems / 4;
-  float2* rs2 = reinterpret_cast<float2*>(rowstat);
   auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const bf16*>(o),
-                       static_cast<const bf16*>(d_o), lse, rs2, p.rows, p.heads, dq_acc, vec4, meta);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, s, o16, g16, lse, rs2, p.rows, p.heads,
+                       dq_acc, vec4);
   };
-  if (p.head_dim == 128) {
-    check ? go(bwd_pre_kernel<128, true>) : go(bwd_pre_kernel<128, false>);
-  } else {
-    check ? go(bwd_pre_kernel<64, true>) : go(bwd_pre_kernel<64, false>);
-  }
+  p.head_dim == 128 ? go(bwd_pre_kernel<128>) : go(bwd_pre_kernel<64>);
   return hipGetLastError();
 }
 
@@ -1228,38 +1324,44 @@ hipError_t launch_bwd(const Problem& p, const Plan& plan, int sched, const float
   return p.head_dim == 128 ? launch_bwd_d<128>(p, a, s) : launch_bwd_d<64>(p, a, s);
 }
 
-hipError_t launch_dq_finalize(const Problem& p, const float* dq_acc, void* dq, const int* meta,
+hipError_t launch_dq_finalize(const Problem& p, const float* dq_acc, void* dq, const Plan& plan,
                               const Rope& rope, hipStream_t s) {
-  const int64_t q_rows = p.broadcast ? p.q_len : p.total_kv;
-  const int64_t n = q_rows * p.heads * p.head_dim;
-  if (rope.cos != nullptr) {
-    const int64_t threads = q_rows * p.heads * (p.head_dim / 8);
-    int64_t rblocks = (threads + 255) / 256;
-    if (rblocks == 0) return hipSuccess;
-    const bool check = maybe_single_tile(p);
-    if (check) rblocks = std::min<int64_t>(rblocks, (int64_t)device_cu_count() * 32);
-    auto go = [&](auto kernel) {
-      hipLaunchKernelGGL(kernel, dim3((unsigned)rblocks), dim3(256), 0, s, dq_acc, static_cast<bf16*>(dq),
-                         q_rows, p.heads, n, p.broadcast ? kDqStripes : 1, p.scale, rope.cos, rope.sin,
-                         rope.pos_q, rope.max_pos, meta);
-    };
-    if (p.head_dim == 128) {
-      check ? go(dq_finalize_rope_kernel<128, true>) : go(dq_finalize_rope_kernel<128, false>);
+  bf16* dq16 = static_cast<bf16*>(dq);
+  if (maybe_single_tile(p)) {   // the plan split the tiles: rows of the first list only
+    const int bn = 32 * bwd_waves(p);
+    if (rope.cos != nullptr) {
+      auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(split_grid(p)), dim3(256), 0, s, dq_acc, dq16, p.heads, p.scale,
+                           rope.cos, rope.sin, rope.pos_q, rope.max_pos, plan.items, plan.meta, bn);
+      };
+      p.head_dim == 128 ? go(dq_finalize_rope_split_kernel<128>) : go(dq_finalize_rope_split_kernel<64>);
     } else {
-      check ? go(dq_finalize_rope_kernel<64, true>) : go(dq_finalize_rope_kernel<64, false>);
+      auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(split_grid(p)), dim3(256), 0, s, dq_acc, dq16, p.heads, p.scale,
+                           plan.items, plan.meta, bn);
+      };
+      p.head_dim == 128 ? go(dq_finalize_split_kernel<128>) : go(dq_finalize_split_kernel<64>);
     }
     return hipGetLastError();
   }
+  const int64_t q_rows = p.broadcast ? p.q_len : p.total_kv;
+  const int64_t n = q_rows * p.heads * p.head_dim;
+  const int stripes = p.broadcast ? kDqStripes : 1;
+  if (rope.cos != nullptr) {
+    const int64_t blocks = (q_rows * p.heads * (p.head_dim / 8) + 255) / 256;
+    if (blocks == 0) return hipSuccess;
+    auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, s, dq_acc, dq16, q_rows, p.heads, n,
+                         stripes, p.scale, rope.cos, rope.sin, rope.pos_q, rope.max_pos);
+    };
+    p.head_dim == 128 ? go(dq_finalize_rope_kernel<128>) : go(dq_finalize_rope_kernel<64>);
+    return hipGetLastError();
+  }
   const int64_t vec4 = n / 4;
-  int64_t blocks = (vec4 + 255) / 256;
+  const int64_t blocks = (vec4 + 255) / 256;
   if (blocks == 0) return hipSuccess;
-  const bool check = maybe_single_tile(p);
-  if (check) blocks = std::min<int64_t>(blocks, (int64_t)device_cu_count() * 32);
-  auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, s, dq_acc, static_cast<bf16*>(dq),
-                       vec4, vec4, p.broadcast ? kDqStripes : 1, p.scale, meta);
-  };
-  check ? go(dq_finalize_kernel<true>) : go(dq_finalize_kernel<false>);
+  hipLaunchKernelGGL(dq_finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, s, dq_acc, dq16, vec4, vec4,
+                     stripes, p.scale);
   return hipGetLastError();
 }
 

@@ -74,9 +74,12 @@ struct Rope {
 };
 
 // Plan written on the device: meta[0] = number of items, meta[1] = dynamic-schedule
-// counter, meta[2] = number of tiles, meta[3] (backward) = 1 when every tile holds a
-// whole self-mode sequence and writes its dQ directly, meta[4 .. 4 + kFwdClassMax)
-// (forward) = per-class counters of the broadcast-mode dynamic schedule.
+// counter, meta[2] = number of tiles.  Forward: meta[4 .. 4 + kFwdClassMax) =
+// per-class counters of the broadcast-mode dynamic schedule.  Backward of a split
+// call (maybe_single_tile): meta[2] counts the tiles of the first list (sequences
+// longer than one tile), meta[3] those of the second (sequences within one tile,
+// which write their dQ directly), meta[4] is the second list's counter and meta[5]
+// its first item; otherwise meta[3] = 0.
 // items[i] = (sequence b, block, offsets[b], offsets[b + 1] - offsets[b]).
 constexpr int kFwdClassMax = 12;
 struct Plan {
@@ -90,7 +93,7 @@ int64_t fwd_max_items(const Problem& p);         // capacity of the forward item
 int64_t bwd_max_items(const Problem& p);         // capacity of the backward item list
 int bwd_waves(const Problem& p);                 // waves per backward workgroup (2, 4 or 8)
 bool single_tile_allowed(const Problem& p);      // the single-tile backward path may be used
-bool maybe_single_tile(const Problem& p);        // ... and every sequence may fit one tile
+bool maybe_single_tile(const Problem& p);        // ... and the plan splits the tiles for it
 
 hipError_t launch_plan_fwd(const Problem& p, const Plan& plan, int sched, hipStream_t s);
 hipError_t launch_plan_sparse(const Problem& p, int* kv_first, int* q_first, hipStream_t s);
@@ -119,19 +122,20 @@ hipError_t launch_fwd_mx(const Problem& p, const Plan& plan, const MxOperands& x
                          hipStream_t s);
 
 // rowstat: [heads][rows] pairs (LSE log2 e, delta = rowsum(dO * O)), 2 floats each,
-// and the zeroed dQ accumulator.  Runs after the backward plan and does nothing when
-// meta[3] is set (the tiles then form delta themselves and write dQ directly).
+// and the zeroed dQ accumulator.  Runs after the backward plan; in a split call only
+// for the rows of the plan's first list (the single-tile tiles form delta themselves
+// and write dQ directly).
 hipError_t launch_bwd_pre(const Problem& p, const void* o, const void* d_o, const float* lse,
-                          float* rowstat, float* dq_acc, int64_t dq_acc_elems, const int* meta,
+                          float* rowstat, float* dq_acc, int64_t dq_acc_elems, const Plan& plan,
                           hipStream_t s);
 hipError_t launch_plan_bwd(const Problem& p, const Plan& plan, int sched, hipStream_t s);
-// lse: the forward's [heads][rows] LSE, read instead of rowstat when every tile
-// holds a whole self-mode sequence (meta[3]).
+// lse: the forward's [heads][rows] LSE, read instead of rowstat by the tiles of a
+// split call's second list (each holds a whole self-mode sequence).
 hipError_t launch_bwd(const Problem& p, const Plan& plan, int sched, const float* rowstat,
                       const float* lse, const void* d_o, float* dq_acc, void* dq, void* dk, void* dv,
                       const Rope& rope, hipStream_t s);
-// Does nothing when meta[3] is set (the tiles wrote dQ).
-hipError_t launch_dq_finalize(const Problem& p, const float* dq_acc, void* dq, const int* meta,
+// In a split call only the rows of the plan's first list (the others' tiles wrote dQ).
+hipError_t launch_dq_finalize(const Problem& p, const float* dq_acc, void* dq, const Plan& plan,
                               const Rope& rope, hipStream_t s);
 
 // Number of compute units of the current device (cached per device).

@@ -303,47 +303,73 @@ struct PlanBwdArgs {
   int batch;
   int heads;
   int bn;          // keys per backward tile
-  int allow_direct;   // single-tile calls may store dQ directly (single_tile_allowed)
+  int split;       // sequences of one tile get a list of their own (maybe_single_tile)
   int4* items;
   int* meta;
 };
 
-// Valid (sequence, K/V block) pairs in natural order; tile t = (items[t / H], t % H).
-// meta[3] = 1 when, in self mode, every sequence fits one tile: each tile then sees
-// all keys of its queries, so its dQ is final and is written directly (with the
-// rotary conjugate only where the tiles can rotate dQ, see single_tile_allowed).
-// Each item also carries the sequence's first row and length (int32: the library
-// rejects T >= 2^30), so a tile's geometry is one 16-byte load.
+// Valid (sequence, K/V block) pairs in natural order, in up to two lists; tile t of
+// a list = (list[t / H], t % H).  Each item also carries the sequence's first row and
+// length (int32: the library rejects T >= 2^30), so a tile's geometry is one 16-byte
+// load.
+// Without split every tile reduce-adds its dQ partial: one list, meta[2] = its tiles,
+// meta[3] = 0.
+// With split (self mode, where the single-tile backward may run) a sequence of 1..bn
+// keys goes to a second list, after the first.  Such a tile sees all keys of its
+// queries, so its dQ is final and is written directly (with the rotary conjugate only
+// where the tiles can rotate dQ, see single_tile_allowed); the tiles of longer
+// sequences reduce-add.  meta[2] = tiles of the first list (M H), meta[3] = tiles of
+// the second, meta[5] = M, the second list's first item; meta[1] and meta[4] are the
+// lists' dynamic-schedule counters.  In self mode an item of the first list also names
+// the rows whose delta and dQ finalize the call needs: [kv0 + j bn, kv0 + min(n,
+// (j + 1) bn)).
 __global__ __launch_bounds__(kPlanThreads) void plan_bwd_kernel(PlanBwdArgs a) {
   __shared__ int wave_sums[kPlanThreads / 64 + 1];
   __shared__ int offs[kSeg + 1];
-  __shared__ int all_single;
   const int tid = threadIdx.x;
-  if (tid == 0) all_single = 1;
   const int nseg = (a.batch + kSeg - 1) / kSeg;
-  int total = 0;
+  auto first_items = [&](int n) { return a.split && n <= a.bn ? 0 : (n + a.bn - 1) / a.bn; };
+  auto second_items = [&](int n) { return a.split && n >= 1 && n <= a.bn ? 1 : 0; };
+  // with split, a first pass sizes the first list
+  int first_total = 0;
+  if (a.split) {
+    for (int sg = 0; sg < nseg; ++sg) {
+      const Segment g = stage_segment(a.offsets, a.off64, a.batch, sg, offs);
+      int count = 0;
+      for (int b = g.bb; b < g.be; ++b) count += first_items(offs[b + 1] - offs[b]);
+      int tot = 0;
+      block_exclusive_scan(count, wave_sums, &tot);
+      first_total += tot;
+    }
+  }
+  int total = 0, total2 = 0;
   for (int sg = 0; sg < nseg; ++sg) {
     const Segment g = stage_segment(a.offsets, a.off64, a.batch, sg, offs);
-    int count = 0;
+    int count = 0, count2 = 0;
     for (int b = g.bb; b < g.be; ++b) {
       const int n = offs[b + 1] - offs[b];
-      count += (n + a.bn - 1) / a.bn;
-      if (n > a.bn) all_single = 0;   // every writer stores the same value
+      count += first_items(n);
+      count2 += second_items(n);
     }
-    int tot = 0;
+    int tot = 0, tot2 = 0;
     int pos = total + block_exclusive_scan(count, wave_sums, &tot);
+    int pos2 = first_total + total2 + block_exclusive_scan(count2, wave_sums, &tot2);
     for (int b = g.bb; b < g.be; ++b) {
       const int kv0 = offs[b], n = offs[b + 1] - kv0;
-      const int nb = (n + a.bn - 1) / a.bn;
+      if (second_items(n)) a.items[pos2++] = make_int4(g.b0 + b, 0, kv0, n);
+      const int nb = first_items(n);
       for (int j = 0; j < nb; ++j) a.items[pos++] = make_int4(g.b0 + b, j, kv0, n);
     }
     total += tot;
+    total2 += tot2;
   }
   if (tid == 0) {
-    a.meta[0] = total;
+    a.meta[0] = total + total2;
     a.meta[1] = 0;
     a.meta[2] = total * a.heads;
-    a.meta[3] = a.allow_direct && all_single;   // read after the scan's barriers
+    a.meta[3] = total2 * a.heads;
+    a.meta[4] = 0;
+    a.meta[5] = total;
   }
 }
 
@@ -429,7 +455,7 @@ hipError_t launch_plan_bwd(const Problem& p, const Plan& plan, int /*sched*/, hi
   a.batch = p.batch;
   a.heads = p.heads;
   a.bn = 32 * bwd_waves(p);
-  a.allow_direct = single_tile_allowed(p) ? 1 : 0;
+  a.split = maybe_single_tile(p) ? 1 : 0;
   a.items = plan.items;
   a.meta = plan.meta;
   hipLaunchKernelGGL(plan_bwd_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
