@@ -133,12 +133,13 @@ jfa_status_t jfa_fwd_noalloc(const void* q, const void* k, const void* v,
 /* Backward pass: gradients of sum(O * dO) with respect to q, k and v, given the
  * o and lse that jfa_fwd returned for the same inputs.  In broadcast mode dq is
  * the sum over all sequences ("Meta's TLX attention kernel outpaces FlashAttention-4
- * on B200", section "GEM's sequences do not fit a fixed grid").  In self mode, when every sequence fits one backward tile (block-diagonal
- * attention in 64-token blocks, for instance), the row sums dO . O are formed from
- * the tile's own probabilities and o is not read ("Meta's TLX Block Attention Beats
- * Flash Attention v2 by 2.3x on Blackwell GPUs", section "One Constraint, Five
- * Eliminations"); it must still be a valid pointer.  Same size
- * rules as jfa_fwd. */
+ * on B200", section "GEM's sequences do not fit a fixed grid").  In self mode with
+ * short sequences (block-diagonal attention in 64-token blocks, for instance), the
+ * row sums dO . O of a sequence that fits one backward tile are formed from the
+ * tile's own probabilities and its rows of o are not read ("Meta's TLX Block
+ * Attention Beats Flash Attention v2 by 2.3x on Blackwell GPUs", section "One
+ * Constraint, Five Eliminations"); o must still be a valid pointer to the whole
+ * tensor.  Same size rules as jfa_fwd. */
 jfa_status_t jfa_bwd(const void* q, const void* k, const void* v,
                      const void* offsets, int offsets_is_int64,
                      int64_t batch, int64_t num_heads, int64_t head_dim,
@@ -162,9 +163,9 @@ jfa_status_t jfa_bwd(const void* q, const void* k, const void* v,
  *   pos_q: int32 device array, one position per query row ([Lq] in broadcast mode,
  *          [T] in self mode); pos_k: int32 device array [T], one per key row;
  *   positions outside [0, max_pos) are clamped into it.
- * dq is rotated either in the fp32 dQ finalize or, on the single-tile path of
- * jfa_bwd (every self-mode sequence within one 64-key tile, D = 128), by the tiles
- * before they store it; other single-tile calls take the finalize route.  Same workspace
+ * dq is rotated either in the fp32 dQ finalize or, for the sequences that take the
+ * single-tile path of jfa_bwd (self mode, D = 128, 64-key tiles, sequences within
+ * one tile), by the tiles before they store it.  Same workspace
  * (jfa_bwd_workspace_size), ownership and error rules as jfa_bwd; null tables or
  * positions, max_pos outside [1, 2^24] or misaligned tables give
  * JFA_ERR_INVALID_ARGUMENT. */
