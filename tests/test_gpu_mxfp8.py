@@ -18,6 +18,7 @@ import torch
 
 import workloads
 from oracle import mxfp8 as mx
+import test_gpu_parity as tp   # the growing-score key ramp
 
 pytestmark = pytest.mark.gpu
 
@@ -135,6 +136,35 @@ def test_mxfp8_forward_matches_oracle(name):
     off = case["offsets"].cuda()
     if name == "self_d64":
         off = off.to(torch.int32)
+    o, lse = _mx_run(jfa, q, k, v, off, bq, causal, case["scale"])
+    torch.cuda.synchronize()
+    o_ref, lse_ref, slack = mx.forward_mx(*(_f64(case[x]) for x in ("q", "k", "v")), case["offsets"].numpy(),
+                                          broadcast_q=bq, causal=causal, scale=case["scale"])
+    _check_o(o, o_ref, slack)
+    _check_lse(lse, lse_ref)
+
+
+RAMP_CASES = {
+    # name: (lengths, heads, head_dim, broadcast_q, causal, q_len, growth of the largest
+    # score along a sequence, base 2)
+    "bcast_ramp_within_lazy_bound": ([300, 700, 1000], 2, 128, True, False, 256, 4.0),
+    "bcast_ramp_rescales": ([300, 700, 1000], 2, 128, True, False, 256, 24.0),
+    "self_causal_ramp_rescales": ([400, 700, 513, 64], 2, 128, False, True, 0, 24.0),
+}
+
+
+@pytest.mark.parametrize("name", list(RAMP_CASES))
+def test_mxfp8_forward_growing_scores(name):
+    """Scores that climb along each sequence (keys ramped along the mean query
+    direction): the running maximum either stays stale, within 2^8 of the scores, or
+    is rescaled several times per row; O and LSE match the oracle either way."""
+    lengths, h, d, bq, causal, lq, growth = RAMP_CASES[name]
+    case = workloads.make_case(lengths, heads=h, head_dim=d, broadcast_q=bq, causal=causal, q_len=lq,
+                               seed=zlib.crc32(name.encode()) % 1000)
+    case = tp._ramp_keys(case, growth)
+    jfa = _jfa()
+    q, k, v = (case[x].cuda() for x in ("q", "k", "v"))
+    off = case["offsets"].cuda()
     o, lse = _mx_run(jfa, q, k, v, off, bq, causal, case["scale"])
     torch.cuda.synchronize()
     o_ref, lse_ref, slack = mx.forward_mx(*(_f64(case[x]) for x in ("q", "k", "v")), case["offsets"].numpy(),

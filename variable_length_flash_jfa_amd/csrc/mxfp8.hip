@@ -416,8 +416,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_mx_kernel(MxArgs a) {
           const float mx = fmaxf(fmaxf(fmaxf(m[0], m[1]), m[2]), fmaxf(fmaxf(m[3], m[4]), st[rb][15]));
           smax[rb] = fmaxf(mx, __shfl_xor(mx, 32));
         }
-        const float mnew = fmaxf(mrun, ceilf(fmaxf(smax[0], smax[1]) * a.c2));
-        if (__ballot(mnew != mrun)) {
+        // Lazy rescaling: the integer running max moves only when some row of the
+        // wave would grow by more than 2^8 (a wave-uniform test); otherwise P is taken
+        // against the stale max and may reach 2^8, which the block scale codes absorb
+        // (with an integer max the scaled elements y, and so the quantized P, do not
+        // depend on it) and O / l and the log-sum-exp divide out.
+        const float mc = ceilf(fmaxf(smax[0], smax[1]) * a.c2);
+        if (__ballot(mc > mrun + 8.f)) {
+          const float mnew = fmaxf(mrun, mc);
           const float alpha = mrun == -INFINITY ? 0.f : ldexpf(1.f, (int)(mrun - mnew));
           lrun *= alpha;
 #pragma unroll
