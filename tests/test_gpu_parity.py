@@ -234,6 +234,26 @@ def test_schedules_agree(bq, causal):
     _compare_full(case, outs[0])
 
 
+@pytest.mark.parametrize("lengths,causal", [
+    # 64-key tiles: short sequences to the single-tile kernel, two longer ones to the other
+    ([64, 17, 150, 10, 5, 64, 30, 20, 128, 33, 0, 64], False),
+    # 128-key tiles (mean 128), causal: one sequence longer than a tile
+    ([128, 100, 300, 20, 90], True),
+])
+def test_split_schedules_agree(lengths, causal):
+    """A call split between the single-tile and reduce-adding backward kernels gives
+    the same gradients under all three schedules (each list has its own counter)."""
+    jfa = _jfa()
+    case = workloads.make_case(lengths, heads=3, head_dim=128, broadcast_q=False, causal=causal, q_len=0,
+                               seed=23)
+    outs = [_run(case, sched=s) for s in (jfa.SCHED_SORTED_ZIGZAG, jfa.SCHED_IDENTITY, jfa.SCHED_DYNAMIC)]
+    for other in outs[1:]:
+        for name in ("o", "lse", "dk", "dv"):
+            assert torch.equal(outs[0][name], other[name]), name
+        _check_grad(_f64(other["dq"]), _f64(outs[0]["dq"]), "dQ across schedules")
+    _compare_full(case, outs[0])
+
+
 def test_broadcast_tile_classes():
     # broadcast mode with two query blocks per head (Lq = 300: a ragged second block)
     # and empty sequences: under the dynamic schedule the forward serves each
