@@ -83,22 +83,26 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o
 // (b, j, kv0, n) of a sequence longer than one tile covers the rows [kv0 + j bn,
 // kv0 + min(n, (j + 1) bn)), and together the items cover every row whose delta and
 // dQ finalize the call needs; the single-tile kernel forms the others' itself.
-// Workgroups take (item, head) units in turn, a group of threads per row.
-struct SplitRows {
-  int64_t r0, r1;
-  int h;
+// Each wave takes items in turn (units of 16 rows would leave most of a larger group
+// idle) and walks the item's (row, head) pairs in memory order, a group of lanes per
+// pair; the next item is loaded during the current one.
+struct SplitWalk {
+  int lane, nwaves, unit, units;
+  __device__ SplitWalk(const int* __restrict__ meta, int heads) {
+    lane = threadIdx.x & 63;
+    nwaves = (int)gridDim.x * (int)(blockDim.x >> 6);
+    unit = (int)blockIdx.x * (int)(blockDim.x >> 6) + (int)(threadIdx.x >> 6);
+    units = meta[2] / heads;   // meta[2] counts the first list's (item, head) tiles
+  }
 };
-__device__ __forceinline__ SplitRows split_rows(const int4* __restrict__ items, int u, int heads, int bn) {
-  const int4 it = items[u / heads];
-  SplitRows r;
-  r.r0 = (int64_t)it.z + (int64_t)it.y * bn;
-  r.r1 = (int64_t)it.z + min(it.w, (it.y + 1) * bn);
-  r.h = u % heads;
-  return r;
+__device__ __forceinline__ void split_pairs(const int4& it, int heads, int bn, int64_t& p0, int64_t& p1) {
+  p0 = ((int64_t)it.z + (int64_t)it.y * bn) * heads;                 // first (row, head) pair
+  p1 = ((int64_t)it.z + min(it.w, (it.y + 1) * bn)) * heads;          // one past the last
 }
 
 // The same statistics and zeroing for the rows of a split call's first list only
-// (meta[2] = its items x heads units; none when every sequence fits one tile).
+// (none when every sequence fits one tile).  NP passes of pairs have their loads
+// issued before any of them is used.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_split_kernel(const bf16* __restrict__ o,
                                                              const bf16* __restrict__ d_o,
@@ -107,28 +111,47 @@ __global__ __launch_bounds__(256) void bwd_pre_split_kernel(const bf16* __restri
                                                              int heads, float* __restrict__ dq_acc,
                                                              const int4* __restrict__ items,
                                                              const int* __restrict__ meta, int bn) {
-  constexpr int TPR = D / 8, RPP = 256 / TPR;   // threads per row, rows per pass
-  const int part = threadIdx.x % TPR, sub = threadIdx.x / TPR;
-  const int units = meta[2];
-  for (int u = blockIdx.x; u < units; u += gridDim.x) {
-    const SplitRows sr = split_rows(items, u, heads, bn);
-    for (int64_t row = sr.r0 + sub; row < sr.r1; row += RPP) {   // a row's TPR lanes share it
-      const int64_t pair = row * heads + sr.h;
-      const bf16x8 x = *reinterpret_cast<const bf16x8*>(o + pair * D + part * 8);
-      const bf16x8 y = *reinterpret_cast<const bf16x8*>(d_o + pair * D + part * 8);
-      float s = 0.f;
+  constexpr int TPR = D / 8, PPP = 64 / TPR, NP = 4;   // lanes per pair, pairs per wave pass, passes in flight
+  SplitWalk w(meta, heads);
+  const int part = w.lane % TPR, sub = w.lane / TPR;
+  if (w.unit >= w.units) return;
+  int4 it = items[w.unit];
+  for (int u = w.unit; u < w.units; u += w.nwaves) {
+    const int un = u + w.nwaves;
+    const int4 itn = un < w.units ? items[un] : it;
+    int64_t p0, p1;
+    split_pairs(it, heads, bn, p0, p1);
+    for (int64_t q0 = p0 + sub; q0 < p1; q0 += NP * PPP) {   // a pair's TPR lanes share it
+      bf16x8 x[NP], y[NP];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += (float)x[e] * (float)y[e];
-#pragma unroll
-      for (int m = TPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
-      if (part == 0) {
-        const int64_t i = (int64_t)sr.h * rows + row;
-        rowstat[i] = make_float2(lse[i] * kLog2e, s);
+      for (int k = 0; k < NP; ++k) {
+        const int64_t pair = q0 + k * PPP;
+        if (pair < p1) {
+          x[k] = *reinterpret_cast<const bf16x8*>(o + pair * D + part * 8);
+          y[k] = *reinterpret_cast<const bf16x8*>(d_o + pair * D + part * 8);
+        }
       }
-      float4* acc = reinterpret_cast<float4*>(dq_acc + pair * D + part * 8);
-      acc[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-      acc[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int k = 0; k < NP; ++k) {
+        const int64_t pair = q0 + k * PPP;
+        if (pair < p1) {
+          float s = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s += (float)x[k][e] * (float)y[k][e];
+#pragma unroll
+          for (int m = TPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+          if (part == 0) {
+            const int64_t row = pair / heads;
+            const int64_t i = (pair - row * heads) * rows + row;   // [head][row]
+            rowstat[i] = make_float2(lse[i] * kLog2e, s);
+          }
+          float4* acc = reinterpret_cast<float4*>(dq_acc + pair * D + part * 8);
+          acc[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+          acc[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
     }
+    it = itn;
   }
 }
 
@@ -1079,25 +1102,42 @@ __global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restric
 }
 
 // The rows of a split call's first list only (self mode: one accumulator stripe);
-// the single-tile kernel stored the others' dQ itself.
+// the single-tile kernel stored the others' dQ itself.  Walk as in
+// bwd_pre_split_kernel.
 template <int D>
 __global__ __launch_bounds__(256) void dq_finalize_split_kernel(const float* __restrict__ acc,
                                                                 bf16* __restrict__ dq, int heads, float scale,
                                                                 const int4* __restrict__ items,
                                                                 const int* __restrict__ meta, int bn) {
-  constexpr int TPR = D / 4, RPP = 256 / TPR;   // threads per row (four columns each), rows per pass
-  const int part = threadIdx.x % TPR, sub = threadIdx.x / TPR;
-  const int units = meta[2];
-  for (int u = blockIdx.x; u < units; u += gridDim.x) {
-    const SplitRows sr = split_rows(items, u, heads, bn);
-    for (int64_t row = sr.r0 + sub; row < sr.r1; row += RPP) {
-      const int64_t e0 = (row * heads + sr.h) * D + part * 4;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(acc + e0);
-      bf16x4 o;
+  constexpr int TPR = D / 4, PPP = 64 / TPR, NP = 8;   // lanes per pair (four columns each), pairs per pass
+  SplitWalk w(meta, heads);
+  const int part = w.lane % TPR, sub = w.lane / TPR;
+  if (w.unit >= w.units) return;
+  int4 it = items[w.unit];
+  for (int u = w.unit; u < w.units; u += w.nwaves) {
+    const int un = u + w.nwaves;
+    const int4 itn = un < w.units ? items[un] : it;
+    int64_t p0, p1;
+    split_pairs(it, heads, bn, p0, p1);
+    for (int64_t q0 = p0 + sub; q0 < p1; q0 += NP * PPP) {
+      f32x4 v[NP];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = (bf16)(v[e] * scale);
-      *reinterpret_cast<bf16x4*>(dq + e0) = o;
+      for (int k = 0; k < NP; ++k) {
+        const int64_t pair = q0 + k * PPP;
+        if (pair < p1) v[k] = *reinterpret_cast<const f32x4*>(acc + pair * D + part * 4);
+      }
+#pragma unroll
+      for (int k = 0; k < NP; ++k) {
+        const int64_t pair = q0 + k * PPP;
+        if (pair < p1) {
+          bf16x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = (bf16)(v[k][e] * scale);
+          *reinterpret_cast<bf16x4*>(dq + pair * D + part * 4) = x;
+        }
+      }
     }
+    it = itn;
   }
 }
 
@@ -1159,13 +1199,19 @@ __global__ __launch_bounds__(256) void dq_finalize_rope_split_kernel(const float
                                                                      const int* __restrict__ pos_q,
                                                                      int max_pos, const int4* __restrict__ items,
                                                                      const int* __restrict__ meta, int bn) {
-  constexpr int G = D / 8, RPP = 256 / G;   // threads per row, rows per pass
-  const int g = threadIdx.x % G, sub = threadIdx.x / G;
-  const int units = meta[2];
-  for (int u = blockIdx.x; u < units; u += gridDim.x) {
-    const SplitRows sr = split_rows(items, u, heads, bn);
-    for (int64_t row = sr.r0 + sub; row < sr.r1; row += RPP)
-      finalize_rope_group<D>(acc, dq, row * heads + sr.h, row, g, 0, 1, scale, rcos, rsin, pos_q, max_pos);
+  constexpr int G = D / 8, PPP = 64 / G;   // lanes per pair, pairs per wave pass
+  SplitWalk w(meta, heads);
+  const int g = w.lane % G, sub = w.lane / G;
+  if (w.unit >= w.units) return;
+  int4 it = items[w.unit];
+  for (int u = w.unit; u < w.units; u += w.nwaves) {
+    const int un = u + w.nwaves;
+    const int4 itn = un < w.units ? items[un] : it;   // the next item, during this one
+    int64_t p0, p1;
+    split_pairs(it, heads, bn, p0, p1);
+    for (int64_t pair = p0 + sub; pair < p1; pair += PPP)
+      finalize_rope_group<D>(acc, dq, pair, pair / heads, g, 0, 1, scale, rcos, rsin, pos_q, max_pos);
+    it = itn;
   }
 }
 
@@ -1245,13 +1291,14 @@ bool single_tile_allowed(const Problem& p) {
 }
 
 // Whether the plan splits the tiles between the single-tile kernel and the
-// reduce-adding one: where the single-tile kernel may run, with 64-key tiles (the mean
-// length is at most 96, so most sequences are short) or when every sequence may fit
-// one tile.
+// reduce-adding one: where the single-tile kernel may run and the mean length is at
+// most 9/8 of a tile.  The split pays when most rows belong to sequences of one tile
+// (its delta pass and dQ finalize walk the longer sequences' items, which is slower
+// per row than the all-rows kernels); the mean is all the host knows, and up to 9/8
+// of a tile it still admits a batch of one-tile sequences with a few longer ones.
 bool maybe_single_tile(const Problem& p) {
   if (!single_tile_allowed(p)) return false;
-  const int nw = bwd_waves(p);
-  return nw == 2 || p.total_kv <= (int64_t)p.batch * 32 * nw;
+  return p.total_kv * 8 <= (int64_t)p.batch * 32 * bwd_waves(p) * 9;
 }
 
 int64_t bwd_max_items(const Problem& p) {
@@ -1262,7 +1309,7 @@ int64_t bwd_max_items(const Problem& p) {
 // Grid of the split-mode row kernels: workgroups that take (item, head) units in turn.
 static unsigned split_grid(const Problem& p) {
   const int64_t units = bwd_max_items(p) * p.heads;
-  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(units, (int64_t)device_cu_count() * 16));
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(units, (int64_t)device_cu_count() * 32));
 }
 
 hipError_t launch_bwd_pre(const Problem& p, const void* o, const void* d_o, const float* lse,
