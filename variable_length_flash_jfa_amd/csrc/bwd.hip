@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void bwd_pre_split_kernel(const bf16* __restri
                                                              int heads, float* __restrict__ dq_acc,
                                                              const int4* __restrict__ items,
                                                              const int* __restrict__ meta, int bn) {
-  constexpr int TPR = D / 8, PPP = 64 / TPR, NP = 4;   // lanes per pair, pairs per wave pass, passes in flight
+  constexpr int TPR = D / 8, PPP = 64 / TPR, NP = 16;   // lanes per pair, pairs per wave pass, passes in flight
   SplitWalk w(meta, heads);
   const int part = w.lane % TPR, sub = w.lane / TPR;
   if (w.unit >= w.units) return;
@@ -1109,7 +1109,7 @@ __global__ __launch_bounds__(256) void dq_finalize_split_kernel(const float* __r
                                                                 bf16* __restrict__ dq, int heads, float scale,
                                                                 const int4* __restrict__ items,
                                                                 const int* __restrict__ meta, int bn) {
-  constexpr int TPR = D / 4, PPP = 64 / TPR, NP = 8;   // lanes per pair (four columns each), pairs per pass
+  constexpr int TPR = D / 4, PPP = 64 / TPR, NP = 16;   // lanes per pair (four columns each), pairs per pass
   SplitWalk w(meta, heads);
   const int part = w.lane % TPR, sub = w.lane / TPR;
   if (w.unit >= w.units) return;
@@ -1309,7 +1309,7 @@ int64_t bwd_max_items(const Problem& p) {
 // Grid of the split-mode row kernels: workgroups that take (item, head) units in turn.
 static unsigned split_grid(const Problem& p) {
   const int64_t units = bwd_max_items(p) * p.heads;
-  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(units, (int64_t)device_cu_count() * 32));
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(units, (int64_t)device_cu_count() * 64));
 }
 
 hipError_t launch_bwd_pre(const Problem& p, const void* o, const void* d_o, const float* lse,
